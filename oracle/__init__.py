@@ -1,0 +1,185 @@
+"""CPU oracle for the Sparse Delta Memory step -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the package smoke check and the benchmark's CPU-baseline leg may
+import this module.  The GPU product path never imports it and has no CPU
+fallback.  The arithmetic lives in sdm_oracle.c (plain C, gcc, no FMA
+contraction, no fast-math); this file only builds it and marshals numpy
+arrays.  See sdm_oracle.c for the definition it follows and its sources.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(_HERE, "liboracle.so")
+F32, BF16 = 0, 1
+_lib = None
+
+
+def build(verbose: bool = False) -> None:
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall",
+           "-Wextra", "-o", LIB + ".tmp", os.path.join(_HERE, "sdm_oracle.c"), "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    global _lib
+    _lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built; run oracle.build()")
+        lib = ctypes.CDLL(LIB)
+        p = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        lib.oracle_select.argtypes = [p, p, i64, i32, i32, p, p, p]
+        lib.oracle_state_init.argtypes = [p, i32, p, i32, i32, i64, i32]
+        lib.oracle_scan.argtypes = [p, i32, i64, i32, i64, i32, i32, p, p, p, p, p, p, p, p,
+                                    i32, i32]
+        lib.oracle_step_decode.argtypes = [p, i32, i32, i32, i32, i32, i32, i32] + [p] * 10
+        lib.oracle_last_error.restype = ctypes.c_char_p
+        lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        for f in ("oracle_select", "oracle_state_init", "oracle_scan", "oracle_step_decode"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc):
+    if rc != 0:
+        raise OracleError(_L().oracle_last_error().decode())
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data if a is not None else None
+
+
+def workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def select(x1, x2, K: int, threads: int = 1):
+    """Product-key top-K of halves x1, x2 [..., n] -> (idx int32, score f32,
+    weight f64), each [..., K].  `threads` > 1 splits the independent units
+    over several calls of the (single-threaded) oracle."""
+    x1 = _c(x1, np.float32)
+    x2 = _c(x2, np.float32)
+    assert x1.shape == x2.shape
+    n = x1.shape[-1]
+    lead = x1.shape[:-1]
+    units = int(np.prod(lead)) if lead else 1
+    idx = np.empty(lead + (K,), np.int32)
+    score = np.empty(lead + (K,), np.float32)
+    weight = np.empty(lead + (K,), np.float64)
+    f1, f2 = x1.reshape(units, n), x2.reshape(units, n)
+    fi, fs, fw = idx.reshape(units, K), score.reshape(units, K), weight.reshape(units, K)
+    L = _L()
+    if threads <= 1 or units < 64:
+        _check(L.oracle_select(_ptr(f1), _ptr(f2), units, n, K, _ptr(fi), _ptr(fs), _ptr(fw)))
+    else:
+        step = (units + threads - 1) // threads
+        spans = [(s, min(units, s + step)) for s in range(0, units, step)]
+
+        def run(sp):
+            a, b = sp
+            return L.oracle_select(_ptr(f1[a:b]), _ptr(f2[a:b]), b - a, n, K, _ptr(fi[a:b]),
+                                   _ptr(fs[a:b]), _ptr(fw[a:b]))
+
+        with ThreadPoolExecutor(threads) as ex:
+            for rc in ex.map(run, spans):
+                _check(rc)
+    return idx, score, weight
+
+
+def state_init(M0, B: int, dtype: int = F32):
+    """M [B,H,N,d_v] (float32, or uint16 bf16 bits) from M0 [H,N,d_v]."""
+    M0 = _c(M0, np.float32)
+    H, N, d_v = M0.shape
+    M = np.empty((B, H, N, d_v), np.float32 if dtype == F32 else np.uint16)
+    _check(_L().oracle_state_init(_ptr(M), dtype, _ptr(M0), B, H, N, d_v))
+    return M
+
+
+def scan(M, dtype, widx, wk, ridx, rw, v, alpha, beta, cols=None, out=None):
+    """T steps on ONE memory M [N,d_v] in place; returns out [T,d_v] (float32).
+    cols = (c0, c1) restricts the computed columns."""
+    N, d_v = M.shape
+    assert M.flags.c_contiguous
+    assert M.dtype == (np.float32 if dtype == F32 else np.uint16)
+    widx, ridx = _c(widx, np.int32), _c(ridx, np.int32)
+    wk, rw = _c(wk, np.float64), _c(rw, np.float64)
+    v = _c(v, np.float32)
+    alpha, beta = _c(alpha, np.float32), _c(beta, np.float32)
+    T, W = widx.shape
+    R = ridx.shape[1]
+    assert v.shape == (T, d_v) and alpha.shape == (T,) and beta.shape == (T,)
+    if out is None:
+        out = np.zeros((T, d_v), np.float32)
+    c0, c1 = (0, d_v) if cols is None else cols
+    _check(_L().oracle_scan(_ptr(M), dtype, N, d_v, T, W, R, _ptr(widx), _ptr(wk), _ptr(ridx),
+                            _ptr(rw), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(out), c0, c1))
+    return out
+
+
+def step_decode(M, dtype, s1, s2, q1, q2, v, alpha, beta, W: int, R: int):
+    """One token for every (b,h) of M [B,H,N,d_v] in place.
+    Returns (out [B,H,d_v], widx [B,H,W], ridx [B,H,R])."""
+    B, H, N, d_v = M.shape
+    n = s1.shape[-1]
+    s1, s2, q1, q2 = (_c(a, np.float32) for a in (s1, s2, q1, q2))
+    v, alpha, beta = _c(v, np.float32), _c(alpha, np.float32), _c(beta, np.float32)
+    out = np.empty((B, H, d_v), np.float32)
+    wi = np.empty((B, H, W), np.int32)
+    ri = np.empty((B, H, R), np.int32)
+    _check(_L().oracle_step_decode(_ptr(M), dtype, B, H, n, d_v, W, R, _ptr(s1), _ptr(s2),
+                                   _ptr(q1), _ptr(q2), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(out), _ptr(wi), _ptr(ri)))
+    return out, wi, ri
+
+
+def bf16_from_double(x: float) -> int:
+    return int(_L().oracle_bf16_from_double(float(x)))
+
+
+def bf16_to_double(h: int) -> float:
+    return float(_L().oracle_bf16_to_double(int(h)))
+
+
+def bf16_bits_to_f32(a) -> np.ndarray:
+    """View uint16 bf16 bits as float32 values (exact widening)."""
+    a = np.asarray(a, np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def run_memory(M, dtype, s1, s2, q1, q2, v, alpha, beta, W, R, cols=None, threads=1):
+    """Whole sequence on ONE memory: selections for all T steps, then the scan.
+    s1.. [T,n]; v [T,d_v]; alpha, beta [T].  Returns dict of outputs."""
+    widx, wsc, wk = select(s1, s2, W, threads=threads)
+    ridx, rsc, rw = select(q1, q2, R, threads=threads)
+    out = scan(M, dtype, widx, wk, ridx, rw, v, alpha, beta, cols=cols)
+    return {"widx": widx, "wscore": wsc, "wk": wk, "ridx": ridx, "rscore": rsc, "rw": rw,
+            "out": out}

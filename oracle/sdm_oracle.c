@@ -1,0 +1,297 @@
+/* CPU oracle for the Sparse Delta Memory (SDM) recurrent step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check
+ * and the benchmark's CPU-baseline leg may load this library.  The GPU
+ * product path never calls, links or falls back to it, and it shares no code,
+ * header, table or helper with the GPU path.
+ *
+ * What it computes.  Source pages: "Riepilogo Tecnico: Sparse Delta Memory
+ * (SDM)" (gist.science/it/paper/2607.07386), sections "Meccanismo Core",
+ * items 1-4, and "Stato Iniziale Appreso"; the same content appears in
+ * "技術要約：Sparse Delta Memory (SDM)" (gist.science/ja/paper/2607.07386),
+ * sections "コアメカニズム" and "学習された初期状態".
+ *
+ *  - Memory: an explicit table M with N = n*n rows of d_v values (item 1).
+ *  - Selection (item 2): the key (or query) is split in two halves x1, x2 of
+ *    length n; slot f = a*n + b scores x1[a] + x2[b].  The top-K slots are
+ *    found without forming all N scores, through
+ *    topk(x1 (+) x2) = topk(topk(x1) (+) topk(x2)):
+ *      stage 1: the K best indices of each half, in the order
+ *               "larger value first, lower index first on equal values";
+ *      stage 2: the K best of the K*K candidate sums
+ *               sigma = fl32(x1[a] + x2[b]) in the order
+ *               "larger sigma first, lower flat index f first on equal sigma".
+ *    K = W for the write selection (from s1, s2) and K = R for the read
+ *    selection (from q1, q2).
+ *  - Selection weights: softmax over the K selected sigma (the pages name the
+ *    weights k_t^(i) but do not say how they are formed; softmax over the
+ *    selected scores is the reading used throughout).  Computed in double.
+ *  - Gated delta write on the W selected rows (item 3):
+ *      Mt[i] = alpha_t * M[i];  M[i] = Mt[i] + beta_t * k_i * (v_t - Mt[i]);
+ *    every other row is left as it is.  Computed in double from the stored
+ *    value and rounded once to the state type (fp32, or bf16 with
+ *    round-to-nearest-even).
+ *  - Sparse read (item 4): o_t = sum_j r_j * M[g_j] over the R selected read
+ *    rows, taken from the stored memory after this step's write.
+ *    Accumulated in double, rounded once to fp32.
+ *  - Learned initial state: every sequence's memory starts as a copy of M0
+ *    (fp32; rounded to bf16 with round-to-nearest-even for bf16 state).
+ *
+ * All inputs must be finite; the functions return a non-zero status and set
+ * a message otherwise.  Plain, slow and single-threaded on purpose.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+static __thread char g_msg[256];
+
+const char* oracle_last_error(void) { return g_msg; }
+
+static int fail(const char* what) {
+  snprintf(g_msg, sizeof g_msg, "%s", what);
+  return 1;
+}
+
+/* ------------------------------------------------------------------ bf16 */
+
+static double bf16_to_double(uint16_t h) {
+  uint32_t b = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &b, 4);
+  return (double)f;
+}
+
+/* Round a double to the nearest bf16 value (ties to even) and return its bits.
+ * bf16 keeps 8 significant bits and the binary32 exponent range, so the grid
+ * spacing near |x| in [2^(e-1), 2^e) is 2^(e-8), and never finer than the
+ * subnormal spacing 2^-133. */
+static uint16_t bf16_from_double(double x) {
+  if (x == 0.0) return signbit(x) ? 0x8000u : 0x0000u;
+  int e;
+  (void)frexp(x, &e);
+  int q = e - 8;
+  if (q < -133) q = -133;
+  double r = nearbyint(ldexp(x, -q));
+  double y = ldexp(r, q);
+  float f = (float)y;
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  return (uint16_t)(b >> 16);
+}
+
+/* ------------------------------------------------------------- selection */
+
+/* Half order: index i goes before index j. */
+static int half_before(const float* x, int i, int j) {
+  return x[i] > x[j] || (x[i] == x[j] && i < j);
+}
+
+/* The first K indices of x[0..n) in half order, written to best[0..K) in
+ * that order.  Kept as a sorted buffer of the best K seen so far. */
+static void topk_half(const float* x, int n, int K, int* best) {
+  int cnt = 0;
+  for (int i = 0; i < n; ++i) {
+    if (cnt == K && !half_before(x, i, best[K - 1])) continue;
+    int pos = cnt < K ? cnt : K - 1;
+    while (pos > 0 && half_before(x, i, best[pos - 1])) {
+      best[pos] = best[pos - 1];
+      --pos;
+    }
+    best[pos] = i;
+    if (cnt < K) ++cnt;
+  }
+}
+
+/* Candidate order: (sigma, f) goes before (sigma2, f2). */
+static int cand_before(float s, int32_t f, float s2, int32_t f2) {
+  return s > s2 || (s == s2 && f < f2);
+}
+
+static int all_finite(const float* x, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (!isfinite(x[i])) return 0;
+  return 1;
+}
+
+/* One selection: K slots of the product-key table spanned by halves x1, x2. */
+static void select_one(const float* x1, const float* x2, int n, int K, int* A, int* Bv,
+                       float* cs, int32_t* cf, int32_t* idx, float* score, double* weight) {
+  topk_half(x1, n, K, A);
+  topk_half(x2, n, K, Bv);
+  int cnt = 0;
+  for (int ia = 0; ia < K; ++ia) {
+    for (int ib = 0; ib < K; ++ib) {
+      int a = A[ia], b = Bv[ib];
+      float s = x1[a] + x2[b]; /* one binary32 addition, round to nearest even */
+      int32_t f = (int32_t)a * (int32_t)n + (int32_t)b;
+      if (cnt == K && !cand_before(s, f, cs[K - 1], cf[K - 1])) continue;
+      int pos = cnt < K ? cnt : K - 1;
+      while (pos > 0 && cand_before(s, f, cs[pos - 1], cf[pos - 1])) {
+        cs[pos] = cs[pos - 1];
+        cf[pos] = cf[pos - 1];
+        --pos;
+      }
+      cs[pos] = s;
+      cf[pos] = f;
+      if (cnt < K) ++cnt;
+    }
+  }
+  double top = (double)cs[0];
+  double z = 0.0;
+  for (int j = 0; j < K; ++j) z += exp((double)cs[j] - top);
+  for (int j = 0; j < K; ++j) {
+    idx[j] = cf[j];
+    if (score) score[j] = cs[j];
+    weight[j] = exp((double)cs[j] - top) / z;
+  }
+}
+
+/* units independent selections: x1, x2 [units, n]; idx, score, weight
+ * [units, K] in the selection order.  score may be NULL. */
+int oracle_select(const float* x1, const float* x2, int64_t units, int n, int K, int32_t* idx,
+                  float* score, double* weight) {
+  if (!x1 || !x2 || !idx || !weight) return fail("null pointer");
+  if (units < 0 || n < 1 || K < 1 || K > n) return fail("bad sizes");
+  if ((int64_t)n * n >= ((int64_t)1 << 31)) return fail("n*n must fit int32 flat indices");
+  int* A = (int*)malloc(sizeof(int) * (size_t)K);
+  int* Bv = (int*)malloc(sizeof(int) * (size_t)K);
+  float* cs = (float*)malloc(sizeof(float) * (size_t)K);
+  int32_t* cf = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+  if (!A || !Bv || !cs || !cf) {
+    free(A); free(Bv); free(cs); free(cf);
+    return fail("out of memory");
+  }
+  int rc = 0;
+  for (int64_t u = 0; u < units; ++u) {
+    const float* a = x1 + u * n;
+    const float* b = x2 + u * n;
+    if (!all_finite(a, n) || !all_finite(b, n)) {
+      rc = fail("non-finite sub-score");
+      break;
+    }
+    select_one(a, b, n, K, A, Bv, cs, cf, idx + u * K, score ? score + u * K : NULL,
+               weight + u * K);
+  }
+  free(A); free(Bv); free(cs); free(cf);
+  return rc;
+}
+
+/* ----------------------------------------------------------------- state */
+
+/* M[b,h] = M0[h] for all b.  dtype 0: fp32 copy; 1: bf16, nearest even.
+ * M [B,H,N,d_v] (float or uint16), M0 [H,N,d_v] float. */
+int oracle_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N, int d_v) {
+  if (!M || !M0) return fail("null pointer");
+  if (B < 1 || H < 1 || N < 1 || d_v < 1 || (dtype != 0 && dtype != 1)) return fail("bad sizes");
+  int64_t per = N * d_v;
+  if (!all_finite(M0, per * H)) return fail("non-finite M0");
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const float* src = M0 + (int64_t)h * per;
+      int64_t off = ((int64_t)b * H + h) * per;
+      if (dtype == 0) {
+        memcpy((float*)M + off, src, sizeof(float) * (size_t)per);
+      } else {
+        uint16_t* dst = (uint16_t*)M + off;
+        for (int64_t i = 0; i < per; ++i) dst[i] = bf16_from_double((double)src[i]);
+      }
+    }
+  return 0;
+}
+
+static double load_elem(const void* M, int dtype, int64_t pos) {
+  if (dtype == 0) return (double)((const float*)M)[pos];
+  return bf16_to_double(((const uint16_t*)M)[pos]);
+}
+
+static void store_elem(void* M, int dtype, int64_t pos, double val) {
+  if (dtype == 0) ((float*)M)[pos] = (float)val;
+  else ((uint16_t*)M)[pos] = bf16_from_double(val);
+}
+
+/* T sequential steps on ONE memory M [N, d_v].  Per step t: the gated delta
+ * write of rows widx[t, 0..W) with weights wk, then the read of rows
+ * ridx[t, 0..R) with weights rw into out[t, :].  Only columns [c0, c1) are
+ * computed (each column's recurrence involves that column alone); out's other
+ * columns are left untouched.  v, out [T, d_v]; alpha, beta [T]. */
+int oracle_scan(void* M, int dtype, int64_t N, int d_v, int64_t T, int W, int R,
+                const int32_t* widx, const double* wk, const int32_t* ridx, const double* rw,
+                const float* v, const float* alpha, const float* beta, float* out, int c0,
+                int c1) {
+  if (!M || !widx || !wk || !ridx || !rw || !v || !alpha || !beta || !out)
+    return fail("null pointer");
+  if (N < 1 || d_v < 1 || T < 0 || W < 1 || R < 1 || (dtype != 0 && dtype != 1))
+    return fail("bad sizes");
+  if (c0 < 0 || c1 > d_v || c0 > c1) return fail("bad column range");
+  for (int64_t t = 0; t < T; ++t) {
+    const int32_t* wi = widx + t * W;
+    const int32_t* ri = ridx + t * R;
+    for (int j = 0; j < W; ++j) {
+      if (wi[j] < 0 || wi[j] >= N) return fail("write index out of range");
+      for (int l = 0; l < j; ++l)
+        if (wi[l] == wi[j]) return fail("write indices of a step must be distinct");
+    }
+    for (int j = 0; j < R; ++j)
+      if (ri[j] < 0 || ri[j] >= N) return fail("read index out of range");
+    const float* vt = v + t * d_v;
+    if (!all_finite(vt, d_v) || !isfinite(alpha[t]) || !isfinite(beta[t]))
+      return fail("non-finite v/alpha/beta");
+    double a = (double)alpha[t], be = (double)beta[t];
+    /* write: forget gate then delta update, selected rows only */
+    for (int j = 0; j < W; ++j) {
+      int64_t row = (int64_t)wi[j] * d_v;
+      double k = wk[t * W + j];
+      for (int c = c0; c < c1; ++c) {
+        double m = load_elem(M, dtype, row + c);
+        double mt = a * m;
+        double u = mt + be * k * ((double)vt[c] - mt);
+        store_elem(M, dtype, row + c, u);
+      }
+    }
+    /* read: weighted sum of the stored rows after the write */
+    for (int c = c0; c < c1; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < R; ++j)
+        acc += rw[t * R + j] * load_elem(M, dtype, (int64_t)ri[j] * d_v + c);
+      out[t * d_v + c] = (float)acc;
+    }
+  }
+  return 0;
+}
+
+/* One single-token step for every (b,h): write and read selections from the
+ * halves, then the write and the read, on M [B,H,N,d_v].  s1, s2, q1, q2
+ * [B,H,n]; v, out [B,H,d_v]; alpha, beta [B,H]; widx [B,H,W], ridx [B,H,R]
+ * (may be NULL). */
+int oracle_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,
+                       const float* s1, const float* s2, const float* q1, const float* q2,
+                       const float* v, const float* alpha, const float* beta, float* out,
+                       int32_t* widx, int32_t* ridx) {
+  if (B < 1 || H < 1 || n < 1 || W < 1 || R < 1 || W > n || R > n) return fail("bad sizes");
+  int64_t N = (int64_t)n * n;
+  int32_t* wi = (int32_t*)malloc(sizeof(int32_t) * (size_t)W);
+  int32_t* ri = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
+  double* wk = (double*)malloc(sizeof(double) * (size_t)W);
+  double* rw = (double*)malloc(sizeof(double) * (size_t)R);
+  int rc = (wi && ri && wk && rw) ? 0 : fail("out of memory");
+  for (int64_t u = 0; rc == 0 && u < (int64_t)B * H; ++u) {
+    rc = oracle_select(s1 + u * n, s2 + u * n, 1, n, W, wi, NULL, wk);
+    if (rc == 0) rc = oracle_select(q1 + u * n, q2 + u * n, 1, n, R, ri, NULL, rw);
+    if (rc != 0) break;
+    size_t es = dtype == 0 ? sizeof(float) : sizeof(uint16_t);
+    void* Mu = (char*)M + (size_t)u * (size_t)N * (size_t)d_v * es;
+    rc = oracle_scan(Mu, dtype, N, d_v, 1, W, R, wi, wk, ri, rw, v + u * d_v, alpha + u,
+                     beta + u, out + u * d_v, 0, d_v);
+    if (rc == 0 && widx) memcpy(widx + u * W, wi, sizeof(int32_t) * (size_t)W);
+    if (rc == 0 && ridx) memcpy(ridx + u * R, ri, sizeof(int32_t) * (size_t)R);
+  }
+  free(wi); free(ri); free(wk); free(rw);
+  return rc;
+}
+
+/* bf16 helpers exposed for the tests of the oracle itself. */
+uint16_t oracle_bf16_from_double(double x) { return bf16_from_double(x); }
+double oracle_bf16_to_double(uint16_t h) { return bf16_to_double(h); }

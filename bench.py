@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the Sparse Delta Memory step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config mid]
+                    [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: the learned-state copy M[b,h] = M0[h] (sdm_state_init),
+the write and read product-key selections (sdm_select x2) and the T-step
+gated-delta write + sparse read (sdm_scan).  The default workload is the
+N = 2^20, d_v = 128 configuration "mid" (B8 H8 n1024 T4096 W=R=64, fp32
+state); the others are parity-test cases.
+
+Printed: one JSON line with tokens/s of the whole step (B*T tokens per step),
+the roofline of the dominant kernel (the scan, HBM-bound; achieved =
+algorithmic slot bytes (2W+R)*d_v*4 per head-token times B*H*T, divided by the
+scan's mean duration from HIP events on its stream), and the CPU oracle timed
+on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SDM scan tokens/sec + slot-traffic HBM GB/s (% of peak), N=2^20, d_v=128"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_traffic.json")
+SCAN_SOURCES = [os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc", f)
+                for f in ("scan.hip", "device_common.h")]
+
+
+def scan_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(n_launch_bytes: float):
+    """HBM bytes per scan launch from the committed counter summary, or None
+    when there is none or the scan kernel has changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != scan_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(cfg, n_heads: int = 2):
+    """The oracle, as it stands, on memories (b, h) for h < n_heads and all b,
+    all T steps; one memory per thread.  Returns the record."""
+    import numpy as np
+
+    import oracle
+    import sdm_inputs as S
+
+    names = ("s1", "s2", "q1", "q2", "v", "alpha", "beta")
+    host = {k: S.host_block(cfg, k, 0, cfg.B, 0, n_heads) for k in names}
+    M0 = S.host_block(cfg, "M0", h0=0, nh=n_heads)
+    jobs = [(b, h) for h in range(n_heads) for b in range(cfg.B)]
+    P = min(workers(), len(jobs))
+
+    def run(job):
+        b, h = job
+        M = M0[h].copy()
+        oracle.run_memory(M, oracle.F32, *(host[k][b, h] for k in names), cfg.W, cfg.R)
+        return cfg.T
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(P) as ex:
+        head_steps = sum(ex.map(run, jobs))
+    dt = time.perf_counter() - t0
+    tokens = head_steps / cfg.H  # one token = H head-steps
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": P, "kind": "oracle",
+            "sample": f"{len(jobs)} of {cfg.B * cfg.H} memories (heads 0..{n_heads - 1}, all "
+                      f"{cfg.B} sequences), all {cfg.T} steps: selections + scan; "
+                      f"{dt:.1f} s wall on {P} threads",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="mid")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs the SDM step on one GPU only: each (b,h) memory is independent, "
+              "so several GPUs would each run their own share with no exchange; "
+              "use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sdm_inputs as S
+    import sparse_memory_linear_sdm_amd as sdm
+
+    if not os.path.exists(sdm.LIB_PATH) or not os.path.exists(S.DEV_LIB):
+        import __graft_entry__
+
+        __graft_entry__.build()
+
+    cfg = S.CONFIGS[args.config]
+    if cfg.decode:
+        raise SystemExit("the decode configuration is a parity-test case, not a bench line")
+    assert cfg.state == "f32"
+    dev = torch.device("cuda:0")
+    B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
+    print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} T{T} W{W} R{R}; generating "
+          f"inputs on the GPU", file=sys.stderr, flush=True)
+
+    f32 = torch.float32
+    inp = {}
+    for k in ("s1", "s2", "q1", "q2"):
+        inp[k] = torch.empty((B, H, T, n), dtype=f32, device=dev)
+    inp["v"] = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
+    inp["alpha"] = torch.empty((B, H, T), dtype=f32, device=dev)
+    inp["beta"] = torch.empty((B, H, T), dtype=f32, device=dev)
+    for k, t in inp.items():
+        S.device_block(cfg, k, t)
+    M0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
+    S.device_block(cfg, "M0", M0)
+    M = torch.empty((B, H, N, d_v), dtype=f32, device=dev)
+    widx = torch.empty((B, H, T, W), dtype=torch.int32, device=dev)
+    wk = torch.empty((B, H, T, W), dtype=f32, device=dev)
+    ridx = torch.empty((B, H, T, R), dtype=torch.int32, device=dev)
+    rw = torch.empty((B, H, T, R), dtype=f32, device=dev)
+    out = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(record=None):
+        e = [ev() for _ in range(5)] if record is not None else None
+        if e: e[0].record(stream)
+        sdm.state_init(M0, B, out=M)
+        if e: e[1].record(stream)
+        sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk))
+        sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw))
+        if e: e[2].record(stream)
+        sdm.scan(M, widx, wk, ridx, rw, inp["v"], inp["alpha"], inp["beta"], out=out)
+        if e: e[3].record(stream)
+        if record is not None:
+            record.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    g0, g1 = ev(), ev()
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(recs)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = g0.elapsed_time(g1)
+    ms_step = ms_total / args.steps
+    init_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / args.steps
+    sel_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
+    scan_ms = sum(r[2].elapsed_time(r[3]) for r in recs) / args.steps
+
+    tokens_per_step = B * T
+    head_tokens = B * H * T
+    slot_bytes = head_tokens * (2 * W + R) * d_v * 4  # algorithmic, one scan launch
+    scan_gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
+    traffic = measured_traffic(slot_bytes)
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_step / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox4x32-10 inputs generated on the GPU)",
+        "config": {"workload": f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
+                               f"fp32 state", "B": B, "H": H, "n": n, "N": N, "d_v": d_v,
+                   "T": T, "W": W, "R": R, "state": cfg.state},
+        "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "kernel": "scan_kernel<float,32>",
+                     "algorithmic_bytes_per_launch": slot_bytes},
+        "breakdown_ms": {"state_init": init_ms, "select_write_read": sel_ms, "scan": scan_ms},
+        "scan_tokens_per_s": tokens_per_step / (scan_ms * 1e-3),
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/* sdm.h -- C ABI of the Sparse Delta Memory (SDM) step library (libsdm.so),
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The step (pages "Riepilogo Tecnico: Sparse Delta Memory (SDM)",
+ * gist.science/it/paper/2607.07386, and its Japanese twin
+ * gist.science/ja/paper/2607.07386; section "Meccanismo Core" items 1-4 and
+ * section "Stato Iniziale Appreso"):
+ *   - the state is an explicit table M of N = n*n slots, each a row of d_v
+ *     values, one table per (batch b, head h);
+ *   - a key and a query are each split in two halves (x1, x2) of length n;
+ *     slot f = a*n + b scores x1[a] + x2[b]; the top-K slots are found with
+ *     topk(x1 (+) x2) = topk(topk(x1) (+) topk(x2)) without forming all N
+ *     scores (K = W for writes, K = R for reads);
+ *   - the selected write rows get the gated delta update
+ *       Mt[i] = alpha_t * M[i];  M[i] = Mt[i] + beta_t * k_i * (v_t - Mt[i]),
+ *     all other rows stay as they are;
+ *   - the output is the weighted sum of the selected read rows;
+ *   - every sequence starts from a learned initial table M0.
+ * The pages do not say how the weights k_i and the read weights are formed;
+ * this library uses softmax over the selected summed scores, and reads after
+ * the step's write.
+ *
+ * Conventions for every call
+ *   - Every buffer pointer is a DEVICE pointer to caller-owned memory,
+ *     contiguous, row-major, in the layout stated per argument.  The library
+ *     allocates nothing, keeps no pointer after the call returns, and only
+ *     writes the documented outputs (and M, updated in place).
+ *   - `stream` is a hipStream_t (passed as void*; NULL = the null stream).
+ *     Work is enqueued asynchronously in call order; nothing synchronises the
+ *     host unless the environment variable SDM_DEBUG_SYNC=1 is set, which
+ *     makes each call wait for its kernels and report asynchronous errors.
+ *   - All arguments are validated before any launch.  Return values:
+ *       SDM_OK (0)               success (work enqueued);
+ *       SDM_ERR_INVALID (1)      bad argument (null pointer, size out of
+ *                                range, misaligned pointer); nothing enqueued;
+ *       SDM_ERR_UNSUPPORTED (2)  a shape outside the compiled set; nothing
+ *                                enqueued (there is no fallback path);
+ *       SDM_ERR_HIP (3)          the HIP runtime reported an error.
+ *     A human-readable reason for the last non-OK return on the calling
+ *     thread is available from sdm_last_error().  Nothing throws or aborts.
+ *   - Supported shapes: n in 1..64 or n in {128, 256, 512, 1024, 2048};
+ *     1 <= K, W, R <= min(n, 64); d_v in {16, 32, 64, 128, 256};
+ *     state dtype SDM_F32 or SDM_BF16 (bf16 state uses fp32 arithmetic and
+ *     rounds to nearest even on store).  Pointers to M, M0 and v must be
+ *     16-byte aligned; sub-score pointers must be 16-byte aligned when
+ *     n >= 256 and 4-byte aligned otherwise.
+ *   - Calls on different streams are independent as long as they do not
+ *     share an output buffer (including M).
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { SDM_OK = 0, SDM_ERR_INVALID = 1, SDM_ERR_UNSUPPORTED = 2, SDM_ERR_HIP = 3 };
+enum { SDM_F32 = 0, SDM_BF16 = 1 };
+
+/* Product-key top-K selection with softmax weights ("Meccanismo Core",
+ * item 2), for `units` independent (key or query) half pairs.
+ *   x1, x2  [units, n] fp32 half sub-scores (all values finite, and every
+ *           sum x1[a] + x2[b] finite, so the weights are defined).
+ *   idx     [units, K] int32 out: flat slots f = a*n + b, ordered by
+ *           (score descending, f ascending).  Stage 1 keeps, per half, the K
+ *           indices of largest value (lower index first on equal values);
+ *           stage 2 ranks the K*K binary32 sums x1[a] + x2[b] the same way.
+ *           -0.0 compares equal to +0.0.
+ *   score   [units, K] fp32 out: the selected sums, or NULL.
+ *   weight  [units, K] fp32 out: exp(score_j - score_0) / sum_l exp(...).
+ * units = 0 is a valid no-op. */
+int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, int32_t* idx,
+               float* score, float* weight, void* stream);
+
+/* Learned initial state ("Stato Iniziale Appreso"): M[b,h] = M0[h] for every
+ * batch row b.
+ *   M   [B, H, N, d_v] out, fp32 (dtype SDM_F32) or bf16 bits (SDM_BF16,
+ *       rounded to nearest even).
+ *   M0  [H, N, d_v] fp32 in. */
+int sdm_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N, int d_v,
+                   void* stream);
+
+/* T sequential steps of the gated delta write and the sparse read
+ * ("Meccanismo Core", items 3 and 4) on every (b,h) memory, in place.
+ *   M       [B, H, N, d_v] state (fp32 or bf16 bits), updated in place.
+ *   widx    [B, H, T, W] int32 write rows of each step (as sdm_select
+ *           returns them); the W rows of one step must be distinct.
+ *   wk      [B, H, T, W] fp32 write weights k.
+ *   ridx    [B, H, T, R] int32 read rows;  rw [B, H, T, R] fp32 read weights.
+ *   v       [B, H, T, d_v] fp32 values;  alpha, beta [B, H, T] fp32 gates.
+ *   out     [B, H, T, d_v] fp32 out: o_t = sum_j rw_j * M_t[ridx_j], read
+ *           from the state after step t's write (as stored, i.e. after the
+ *           bf16 rounding for bf16 state).
+ * Per step and row: Mt = alpha*M; M = Mt + (beta*k)*(v - Mt), in fp32.
+ * Rows not selected for writing are never touched.  Row indices outside
+ * [0, N) are skipped (no access; a skipped read row contributes 0); repeated
+ * write rows within one step leave those rows unspecified.  T = 0 is a
+ * valid no-op.  The caller may split a sequence into consecutive calls over
+ * consecutive time ranges; the result is identical. */
+int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+             const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+             const float* v, const float* alpha, const float* beta, float* out, void* stream);
+
+/* One single-token step for every (b,h): both selections, the write and the
+ * read, fused in one kernel (the recurrent inference form; page "Riepilogo
+ * Tecnico: Sparse Delta Memory (SDM)", section "Significato e
+ * Rivendicazioni", constant state and compute per token).
+ *   M        [B, H, n*n, d_v] state, updated in place.
+ *   s1, s2   [B, H, n] write half sub-scores;  q1, q2 [B, H, n] read halves.
+ *   v        [B, H, d_v];  alpha, beta [B, H].
+ *   out      [B, H, d_v] fp32 out.
+ *   widx     [B, H, W] int32 out (selected write rows), or NULL.
+ *   ridx     [B, H, R] int32 out (selected read rows), or NULL.
+ * Equal to sdm_select twice followed by sdm_scan with T = 1. */
+int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,
+                    const float* s1, const float* s2, const float* q1, const float* q2,
+                    const float* v, const float* alpha, const float* beta, float* out,
+                    int32_t* widx, int32_t* ridx, void* stream);
+
+/* Static text for a status code. */
+const char* sdm_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* sdm_last_error(void);
+
+/* ABI version of this header (incremented on incompatible change). */
+int sdm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

@@ -1,0 +1,172 @@
+// C-ABI entry points of libsdm.so: argument validation (before any launch),
+// dispatch to the kernels, HIP error mapping and the per-thread error text.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/sdm.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool debug_sync() {
+  static const int on = [] {
+    const char* e = getenv("SDM_DEBUG_SYNC");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+int finish(const char* what, hipError_t launch_err, hipStream_t stream) {
+  if (launch_err != hipSuccess)
+    return fail(SDM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(launch_err));
+  if (debug_sync()) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+      return fail(SDM_ERR_HIP, "%s: kernel failed: %s", what, hipGetErrorString(e));
+  }
+  g_err[0] = '\0';
+  return SDM_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool n_supported(int n) {
+  return (n >= 1 && n <= 64) || n == 128 || n == 256 || n == 512 || n == 1024 || n == 2048;
+}
+
+bool dv_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+int check_n_k(int n, int K, const char* kname) {
+  if (n < 1) return fail(SDM_ERR_INVALID, "n must be >= 1 (got %d)", n);
+  if (K < 1 || K > n) return fail(SDM_ERR_INVALID, "%s must be in [1, n] (got %s=%d, n=%d)",
+                                  kname, kname, K, n);
+  if (!n_supported(n))
+    return fail(SDM_ERR_UNSUPPORTED, "n=%d not compiled (1..64 or 128..2048 powers of two)", n);
+  if (K > 64) return fail(SDM_ERR_UNSUPPORTED, "%s=%d > 64 not compiled", kname, K);
+  return SDM_OK;
+}
+
+int check_scores(const float* p, int n, const char* name) {
+  if (!p) return fail(SDM_ERR_INVALID, "%s is NULL", name);
+  size_t a = n >= 256 ? 16 : 4;
+  if (!aligned(p, a)) return fail(SDM_ERR_INVALID, "%s must be %zu-byte aligned", name, a);
+  return SDM_OK;
+}
+
+int check_state(const void* M, int dtype, int64_t N, int d_v) {
+  if (!M) return fail(SDM_ERR_INVALID, "M is NULL");
+  if (!aligned(M, 16)) return fail(SDM_ERR_INVALID, "M must be 16-byte aligned");
+  if (dtype != SDM_F32 && dtype != SDM_BF16)
+    return fail(SDM_ERR_INVALID, "dtype must be SDM_F32 or SDM_BF16 (got %d)", dtype);
+  if (N < 1 || N >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_INVALID, "N must be in [1, 2^31) (got %lld)", (long long)N);
+  if (d_v < 1) return fail(SDM_ERR_INVALID, "d_v must be >= 1 (got %d)", d_v);
+  if (!dv_supported(d_v))
+    return fail(SDM_ERR_UNSUPPORTED, "d_v=%d not compiled (16, 32, 64, 128, 256)", d_v);
+  return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_abi_version(void) { return 1; }
+
+const char* sdm_status_string(int status) {
+  switch (status) {
+    case SDM_OK: return "SDM_OK";
+    case SDM_ERR_INVALID: return "SDM_ERR_INVALID";
+    case SDM_ERR_UNSUPPORTED: return "SDM_ERR_UNSUPPORTED";
+    case SDM_ERR_HIP: return "SDM_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* sdm_last_error(void) { return g_err; }
+
+int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, int32_t* idx,
+               float* score, float* weight, void* stream) {
+  int rc;
+  if ((rc = check_scores(x1, n, "x1")) || (rc = check_scores(x2, n, "x2"))) return rc;
+  if (!idx || !weight) return fail(SDM_ERR_INVALID, "idx and weight must not be NULL");
+  if (units < 0) return fail(SDM_ERR_INVALID, "units must be >= 0");
+  if ((rc = check_n_k(n, K, "K"))) return rc;
+  if (units > ((int64_t)1 << 32)) return fail(SDM_ERR_INVALID, "units above 2^32");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_select", sdm::launch_select(x1, x2, units, n, K, idx, score, weight, s), s);
+}
+
+int sdm_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N, int d_v,
+                   void* stream) {
+  int rc;
+  if ((rc = check_state(M, dtype, N, d_v))) return rc;
+  if (!M0) return fail(SDM_ERR_INVALID, "M0 is NULL");
+  if (!aligned(M0, 16)) return fail(SDM_ERR_INVALID, "M0 must be 16-byte aligned");
+  if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_state_init", sdm::launch_state_init(M, dtype, M0, B, H, N, d_v, s), s);
+}
+
+int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+             const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+             const float* v, const float* alpha, const float* beta, float* out, void* stream) {
+  int rc;
+  if ((rc = check_state(M, dtype, N, d_v))) return rc;
+  if (!widx || !wk || !ridx || !rw || !v || !alpha || !beta || !out)
+    return fail(SDM_ERR_INVALID, "a scan input or output pointer is NULL");
+  if (!aligned(v, 16) || !aligned(out, 16))
+    return fail(SDM_ERR_INVALID, "v and out must be 16-byte aligned");
+  if (!aligned(widx, 4) || !aligned(wk, 4) || !aligned(ridx, 4) || !aligned(rw, 4) ||
+      !aligned(alpha, 4) || !aligned(beta, 4))
+    return fail(SDM_ERR_INVALID, "index, weight and gate arrays must be 4-byte aligned");
+  if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  if ((int64_t)B * H > (1 << 24)) return fail(SDM_ERR_INVALID, "B*H too large");
+  if (T < 0) return fail(SDM_ERR_INVALID, "T must be >= 0");
+  if (W < 1 || R < 1) return fail(SDM_ERR_INVALID, "W and R must be >= 1");
+  if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W and R above 64 are not compiled");
+  if (W > N || R > N) return fail(SDM_ERR_INVALID, "W and R must not exceed N");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_scan",
+                sdm::launch_scan(M, dtype, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                                 beta, out, s),
+                s);
+}
+
+int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,
+                    const float* s1, const float* s2, const float* q1, const float* q2,
+                    const float* v, const float* alpha, const float* beta, float* out,
+                    int32_t* widx, int32_t* ridx, void* stream) {
+  int rc;
+  if ((rc = check_n_k(n, W, "W")) || (rc = check_n_k(n, R, "R"))) return rc;
+  if ((rc = check_state(M, dtype, (int64_t)n * n, d_v))) return rc;
+  if ((rc = check_scores(s1, n, "s1")) || (rc = check_scores(s2, n, "s2")) ||
+      (rc = check_scores(q1, n, "q1")) || (rc = check_scores(q2, n, "q2")))
+    return rc;
+  if (!v || !alpha || !beta || !out)
+    return fail(SDM_ERR_INVALID, "v, alpha, beta and out must not be NULL");
+  if (!aligned(v, 16) || !aligned(out, 4) || !aligned(alpha, 4) || !aligned(beta, 4))
+    return fail(SDM_ERR_INVALID, "v must be 16-byte aligned; out, alpha, beta 4-byte");
+  if ((widx && !aligned(widx, 4)) || (ridx && !aligned(ridx, 4)))
+    return fail(SDM_ERR_INVALID, "widx and ridx must be 4-byte aligned");
+  if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  if ((int64_t)B * H > 0x7FFFFFFF) return fail(SDM_ERR_INVALID, "B*H too large");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_step_decode",
+                sdm::launch_step_decode(M, dtype, B, H, n, d_v, W, R, s1, s2, q1, q2, v, alpha,
+                                        beta, out, widx, ridx, s),
+                s);
+}
+
+}  // extern "C"

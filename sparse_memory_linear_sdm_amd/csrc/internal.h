@@ -1,0 +1,26 @@
+// Launchers behind the C ABI (host side).  Arguments are validated by the
+// C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm {
+
+hipError_t launch_select(const float* x1, const float* x2, int64_t units, int n, int K,
+                         int32_t* idx, float* score, float* weight, hipStream_t stream);
+
+hipError_t launch_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N,
+                             int d_v, hipStream_t stream);
+
+hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W,
+                       int R, const int32_t* widx, const float* wk, const int32_t* ridx,
+                       const float* rw, const float* v, const float* alpha, const float* beta,
+                       float* out, hipStream_t stream);
+
+hipError_t launch_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,
+                              const float* s1, const float* s2, const float* q1,
+                              const float* q2, const float* v, const float* alpha,
+                              const float* beta, float* out, int32_t* widx, int32_t* ridx,
+                              hipStream_t stream);
+
+}  // namespace sdm

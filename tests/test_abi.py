@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every function include/sdm.h declares,
+and rejects bad arguments before any launch (these calls never reach the GPU,
+so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_memory_linear_sdm_amd as sdm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(sdm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = sdm.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.sdm_abi_version() == 1
+    assert L.sdm_status_string(0) == b"SDM_OK"
+    assert L.sdm_status_string(2) == b"SDM_ERR_UNSUPPORTED"
+
+
+def _err():
+    return sdm.lib().sdm_last_error().decode()
+
+
+def test_select_validation():
+    L = sdm.lib()
+    ok = (FAKE, FAKE, 10, 64, 8, FAKE, FAKE, FAKE, None)
+    bad = [
+        ((None,) + ok[1:], 1, "x1"),
+        (ok[:5] + (None,) + ok[6:], 1, "idx"),
+        (ok[:2] + (-1,) + ok[3:], 1, "units"),
+        (ok[:4] + (0,) + ok[5:], 1, "K"),
+        (ok[:4] + (65,) + ok[5:], 1, "K"),
+        (ok[:3] + (100,) + ok[4:], 2, "n=100"),
+        (ok[:3] + (4096, 64) + ok[5:], 2, "n=4096"),
+        (ok[:3] + (128, 96) + ok[5:], 2, "K=96"),
+        ((FAKE + 4,) + ok[1:3] + (256,) + ok[4:], 1, "aligned"),
+    ]
+    for args, status, word in bad:
+        rc = L.sdm_select(*args)
+        assert rc == status, (args, rc, _err())
+        assert word in _err()
+
+
+def test_state_init_validation():
+    L = sdm.lib()
+    assert L.sdm_state_init(None, 0, FAKE, 1, 1, 16, 16, None) == 1
+    assert L.sdm_state_init(FAKE, 7, FAKE, 1, 1, 16, 16, None) == 1
+    assert L.sdm_state_init(FAKE, 0, FAKE, 1, 1, 16, 24, None) == 2
+    assert L.sdm_state_init(FAKE, 0, FAKE, 0, 1, 16, 16, None) == 1
+    assert L.sdm_state_init(FAKE + 8, 0, FAKE, 1, 1, 16, 16, None) == 1
+    assert L.sdm_state_init(FAKE, 0, FAKE, 1, 1, 1 << 31, 16, None) == 1
+
+
+def test_scan_validation():
+    L = sdm.lib()
+    ok = [FAKE, 0, 1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 9 + [None]
+    assert len(ok) == 19
+
+    def call(**kw):
+        a = list(ok)
+        pos = {"M": 0, "dtype": 1, "B": 2, "H": 3, "N": 4, "d_v": 5, "T": 6, "W": 7, "R": 8,
+               "widx": 9, "v": 13, "out": 16}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return L.sdm_scan(*a)
+
+    assert call(M=None) == 1
+    assert call(dtype=2) == 1
+    assert call(B=0) == 1
+    assert call(T=-1) == 1
+    assert call(W=0) == 1
+    assert call(W=65) == 2
+    assert call(R=100) == 2
+    assert call(d_v=48) == 2
+    assert call(N=4, W=8) == 1
+    assert call(widx=None) == 1
+    assert call(v=FAKE + 4) == 1
+    assert call(out=FAKE + 8) == 1
+
+
+def test_step_decode_validation():
+    L = sdm.lib()
+    ok = [FAKE, 1, 2, 2, 64, 128, 8, 8] + [FAKE] * 8 + [None, None, None]
+    assert L.sdm_step_decode(*([None] + ok[1:])) == 1
+    a = list(ok); a[4] = 100
+    assert L.sdm_step_decode(*a) == 2
+    a = list(ok); a[6] = 65
+    assert L.sdm_step_decode(*a) == 1
+    a = list(ok); a[5] = 100
+    assert L.sdm_step_decode(*a) == 2
+    a = list(ok); a[8] = None
+    assert L.sdm_step_decode(*a) == 1
+    a = list(ok); a[1] = 5
+    assert L.sdm_step_decode(*a) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sdm, "_lib", None)
+    monkeypatch.setattr(sdm, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        sdm.lib()

@@ -1,0 +1,239 @@
+"""GPU parity of every call of the C ABI against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles, waves and blocks
+and leave ragged tails.  Selected indices are compared bit for bit; memory
+and outputs within the stated bars (tests/gpu_util.py)."""
+import numpy as np
+import pytest
+
+import oracle
+import sdm_inputs as S
+from tests.gpu_util import (NAMES, check_selection, check_values, gpu_sequence, host_inputs,
+                            oracle_memory, state_to_host, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = oracle.F32, oracle.BF16
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _sel_case(x1, x2, K):
+    import sparse_memory_linear_sdm_amd as sdm
+
+    torch = _torch()
+    gi, gs, gw = sdm.select(torch.from_numpy(x1).cuda(), torch.from_numpy(x2).cuda(), K)
+    torch.cuda.synchronize()
+    oi, os_, ow = oracle.select(x1, x2, K, threads=8)
+    check_selection(gi.cpu().numpy(), gs.cpu().numpy(), gw.cpu().numpy(), oi, os_, ow,
+                    f"n={x1.shape[-1]} K={K}")
+
+
+@pytest.mark.parametrize("n,K,units", [(8, 8, 33), (16, 5, 70), (37, 9, 129), (64, 64, 257),
+                                       (64, 8, 1000), (128, 32, 301), (256, 32, 515),
+                                       (512, 17, 130), (1024, 64, 1027), (2048, 64, 64),
+                                       (1024, 1, 50), (256, 2, 50)])
+def test_select_random(n, K, units):
+    cfg = S.CONFIGS["tiny"].with_(n=n, T=units, seed=1000 + n + K)
+    x1 = S.host_block(cfg, "s1")[0, 0]
+    x2 = S.host_block(cfg, "s2")[0, 0]
+    _sel_case(x1, x2, K)
+
+
+@pytest.mark.parametrize("n,K", [(8, 3), (64, 17), (256, 32), (1024, 64), (2048, 40)])
+def test_select_integer_ties(n, K):
+    # Small integers: many exactly equal halves and sums; the lower index
+    # (stage 1) and the lower flat index (stage 2) must win every tie.
+    rng = np.random.default_rng(n * 31 + K)
+    x1 = rng.integers(-2, 3, (300, n)).astype(np.float32)
+    x2 = rng.integers(-2, 3, (300, n)).astype(np.float32)
+    _sel_case(x1, x2, K)
+
+
+def test_select_degenerate_inputs():
+    n = 256
+    z = np.zeros((4, n), np.float32)
+    _sel_case(z, z, 64)                       # everything ties
+    neg = z.copy()
+    neg[:, ::2] = -0.0                        # -0 and +0 must compare equal
+    _sel_case(neg, z, 16)
+    one = np.ones((3, 2), np.float32)
+    one[:, 1] = 1.0 + 2.0 ** -23              # rounding tie of the sums
+    two = np.tile(np.array([2.0, -5.0], np.float32), (3, 1))
+    _sel_case(one, two, 1)
+    _sel_case(one, two, 2)
+    big = np.full((2, 64), -1.5e38, np.float32)
+    big[:, 5] = 1.5e38
+    _sel_case(big, big, 8)                    # sums near the binary32 limit
+    ramp = np.tile(np.arange(1024, dtype=np.float32), (2, 1))
+    _sel_case(ramp, ramp[:, ::-1].copy(), 64)
+
+
+def test_state_init_bitwise():
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["small"].with_(B=3, H=2)
+    M0 = S.host_block(cfg, "M0")
+    for dtype, tdt in ((F32, torch.float32), (BF16, torch.bfloat16)):
+        M = sdm.state_init(torch.from_numpy(M0).cuda(), cfg.B, tdt)
+        ref = oracle.state_init(M0, cfg.B, dtype)
+        assert np.array_equal(state_to_host(M), ref)
+
+
+def _full_parity(cfg, dtype=F32, host=None, check_all=True):
+    """Whole [B,H,T] block on the GPU; every memory against the oracle."""
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    host = host or host_inputs(cfg)
+    M0 = S.host_block(cfg, "M0")
+    dev = to_dev(host)
+    tdt = torch.float32 if dtype == F32 else torch.bfloat16
+    M = sdm.state_init(torch.from_numpy(M0).cuda(), cfg.B, tdt)
+    g = gpu_sequence(cfg, dev, M)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in g.items()}
+    Mh = state_to_host(M)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            o = oracle_memory(cfg, host, b, h, M0[h], dtype, threads=8)
+            tag = f"{cfg.name} b={b} h={h}"
+            check_selection(g["widx"][b, h], g["wscore"][b, h], g["wk"][b, h], o["widx"],
+                            o["wscore"], o["wk"], tag + " write")
+            check_selection(g["ridx"][b, h], g["rscore"][b, h], g["rw"][b, h], o["ridx"],
+                            o["rscore"], o["rw"], tag + " read")
+            gm = Mh[b, h] if dtype == F32 else oracle.bf16_bits_to_f32(Mh[b, h])
+            om = o["M"] if dtype == F32 else oracle.bf16_bits_to_f32(o["M"])
+            check_values(gm, om, dtype, tag + " M")
+            check_values(g["out"][b, h], o["out"], dtype, tag + " out")
+    return g, Mh
+
+
+def test_tiny_config_parity():
+    _full_parity(S.CONFIGS["tiny"])
+
+
+def test_small_config_parity_subset():
+    # The small workload's shapes (n=256, d_v=64, W=R=32) on 2 of its 16
+    # memories and its first 512 steps; the full config runs in the
+    # full-size tests.
+    cfg = S.CONFIGS["small"].with_(B=1, H=2, T=512)
+    _full_parity(cfg)
+
+
+@pytest.mark.parametrize("d_v", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_scan_shapes(d_v, dtype):
+    # Ragged: 3 memories (not a multiple of the 8-way XCD grouping), T not a
+    # multiple of the 16-step LDS chunk, W and R not multiples of the rows
+    # one wave instruction covers.
+    cfg = S.CONFIGS["tiny"].with_(B=1, H=3, n=32, d_v=d_v, T=37, W=13, R=29,
+                                  state="f32" if dtype == F32 else "bf16", seed=77 + d_v)
+    _full_parity(cfg, dtype)
+
+
+def test_hazard_same_rows_every_step():
+    # Constant sub-scores: every step writes and reads the same slots, so
+    # each step's loads depend on the previous step's stores.
+    cfg = S.CONFIGS["tiny"].with_(B=1, H=2, T=70, d_v=32)
+    host = host_inputs(cfg)
+    for k in ("s1", "s2", "q1", "q2"):
+        host[k][:] = host[k][:, :, :1]
+    _full_parity(cfg, host=host)
+
+
+def test_hazard_read_rows_equal_write_rows():
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=1, T=50, W=8, R=8)
+    host = host_inputs(cfg)
+    host["q1"], host["q2"] = host["s1"].copy(), host["s2"].copy()
+    _full_parity(cfg, host=host)
+    _full_parity(cfg, BF16, host=host)
+
+
+def test_hazard_dense_reuse_small_table():
+    # n = 8: N = 64 slots and W = R = 8 -- rows repeat constantly.
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=2, n=8, d_v=16, T=300, W=8, R=8)
+    _full_parity(cfg)
+    _full_parity(cfg.with_(state="bf16"), BF16)
+
+
+def test_chunked_scan_bitwise_and_deterministic():
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=2, T=100, n=16, d_v=32)
+    host = host_inputs(cfg)
+    dev = to_dev(host)
+    M0 = torch.from_numpy(S.host_block(cfg, "M0")).cuda()
+    widx, _, wk = sdm.select(dev["s1"], dev["s2"], cfg.W)
+    ridx, _, rw = sdm.select(dev["q1"], dev["q2"], cfg.R)
+    args = (widx, wk, ridx, rw, dev["v"], dev["alpha"], dev["beta"])
+    M1 = sdm.state_init(M0, cfg.B)
+    o1 = sdm.scan(M1, *args)
+    M2 = sdm.state_init(M0, cfg.B)
+    o2 = sdm.scan(M2, *args)
+    M3 = sdm.state_init(M0, cfg.B)
+    parts = []
+    for t0, t1 in ((0, 31), (31, 32), (32, 100)):
+        parts.append(sdm.scan(M3, *(a[:, :, t0:t1].contiguous() for a in args)))
+    torch.cuda.synchronize()
+    assert torch.equal(M1, M2) and torch.equal(o1, o2)
+    assert torch.equal(M1, M3) and torch.equal(o1, torch.cat(parts, dim=2))
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_step_decode_parity(dtype):
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["decode"].with_(B=3, H=2, n=64, T=12, W=16, R=24,
+                                    state="f32" if dtype == F32 else "bf16")
+    host = host_inputs(cfg)
+    dev = to_dev(host)
+    M0 = S.host_block(cfg, "M0")
+    tdt = torch.float32 if dtype == F32 else torch.bfloat16
+    M = sdm.state_init(torch.from_numpy(M0).cuda(), cfg.B, tdt)
+    Mo = oracle.state_init(M0, cfg.B, dtype)
+    for t in range(cfg.T):
+        step = [dev[k][:, :, t].contiguous() for k in NAMES]
+        out, wi, ri = sdm.step_decode(M, *step, cfg.W, cfg.R)
+        oo, owi, ori = oracle.step_decode(Mo, dtype, *(host[k][:, :, t] for k in NAMES), cfg.W,
+                                          cfg.R)
+        torch.cuda.synchronize()
+        assert np.array_equal(wi.cpu().numpy(), owi) and np.array_equal(ri.cpu().numpy(), ori)
+        check_values(out.cpu().numpy(), oo, dtype, f"decode out t={t}")
+    Mh = state_to_host(M)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            gm = Mh[b, h] if dtype == F32 else oracle.bf16_bits_to_f32(Mh[b, h])
+            om = Mo[b, h] if dtype == F32 else oracle.bf16_bits_to_f32(Mo[b, h])
+            check_values(gm, om, dtype, f"decode M b={b} h={h}")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_step_decode_equals_scan(dtype):
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["decode"].with_(B=2, H=2, n=32, T=20, W=12, R=12, d_v=64)
+    dev = to_dev(host_inputs(cfg))
+    M0 = torch.from_numpy(S.host_block(cfg, "M0")).cuda()
+    tdt = torch.float32 if dtype == F32 else torch.bfloat16
+    Md = sdm.state_init(M0, cfg.B, tdt)
+    outs = []
+    for t in range(cfg.T):
+        o, _, _ = sdm.step_decode(Md, *(dev[k][:, :, t].contiguous() for k in NAMES), cfg.W,
+                                  cfg.R)
+        outs.append(o)
+    Ms = sdm.state_init(M0, cfg.B, tdt)
+    g = gpu_sequence(cfg, dev, Ms)
+    torch.cuda.synchronize()
+    assert torch.equal(Md, Ms)
+    # Same rows and weights, same per-element update; the read sums the same
+    # products in a different order, so compare within the bar.
+    check_values(torch.stack(outs, 2).cpu().numpy(), g["out"].cpu().numpy(), F32,
+                 "decode vs scan out")

@@ -66,7 +66,7 @@ def workers() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline(cfg, n_heads: int = 2):
+def cpu_baseline(cfg, n_heads: int = 4):
     """The oracle, as it stands, on memories (b, h) for h < n_heads and all b,
     all T steps; one memory per thread.  Returns the record."""
     import numpy as np

@@ -137,6 +137,8 @@ int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, in
   if (W < 1 || R < 1) return fail(SDM_ERR_INVALID, "W and R must be >= 1");
   if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W and R above 64 are not compiled");
   if (W > N || R > N) return fail(SDM_ERR_INVALID, "W and R must not exceed N");
+  if (N * d_v * (dtype == SDM_F32 ? 4 : 2) >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's table must be below 2 GiB for sdm_scan");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_scan",
                 sdm::launch_scan(M, dtype, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,

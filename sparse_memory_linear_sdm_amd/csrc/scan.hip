@@ -9,32 +9,39 @@
 // are dealt to the 8 XCDs round-robin), so a memory's index, weight and value
 // traffic is fetched into one L2.  Nothing here is a dense contraction, so
 // there is no MFMA: the kernel is bound by HBM traffic, (2W + R) tile rows
-// per step per tile.
+// per step per tile, all random 128-byte accesses.
 //
 // Two wavefronts per workgroup:
-//   producer  stages each step's metadata (row indices, weights, the tile's
-//             v columns, alpha, beta) into an LDS "plan", two chunks of kChunk
-//             steps ahead of the consumer (triple buffer), and resolves all
-//             read-after-write hazards there: for every row of step u it finds
-//             the newest step s in [u - D, u] (s < u for write rows) that
-//             writes the same row.  Each step's write set is recorded as a
-//             bitmap of hashed rows in LDS; a row whose bit is clear in every
-//             window bitmap has no hazard (one LDS read per row and window
-//             step, no per-lane loops).  The rare rows whose bit is set are
-//             resolved exactly, one wave-uniform ballot per candidate against
-//             the write rows of the window steps kept in registers.  Only
-//             indices are involved, so this runs ahead of the data.
+//   producer  stages each step's metadata into an LDS "plan", two chunks of
+//             kChunk steps ahead of the consumer (triple buffer): the byte
+//             offsets of the W write rows and R read rows in the tile, their
+//             weights, the tile's v columns, alpha and beta.  It also resolves
+//             every read-after-write hazard inside the consumer's prefetch
+//             window: for each row of step u, the newest step s in
+//             [u - D, u] (s < u for write rows) writing the same row.  Each
+//             step's write set is recorded as a bitmap of hashed rows; a row
+//             whose bit is clear in every window bitmap has no hazard (one LDS
+//             read per row and window step, no per-lane loops).  The rare
+//             candidates are resolved exactly with wave-uniform ballots
+//             against the window's write rows kept in registers.  The plan
+//             then names, per row, where its current value lives, and marks
+//             in the writing step which updated rows a later step will need.
 //   consumer  keeps the row gathers of D steps in flight in a register ring:
-//             at step u it issues the 16-byte loads of step u + D, then
+//             at step u it issues the 16-byte buffer loads of step u + D, then
 //             updates step u's W rows (Mt = alpha*M; M = Mt + (beta*k)(v - Mt)
-//             in fp32, rounded to the state type), stores them, keeps them in
-//             an LDS ring of the last D + 1 steps, and forms o_u from the R
-//             read rows.  A row that the plan marks as written inside the
-//             window is taken from that LDS ring instead of the (possibly
-//             stale) loaded value.  Loads of step u + D are issued after the
+//             in fp32, rounded to the state type) and stores them, and
+//             accumulates the R read rows.  Rows the plan forwards come from a
+//             small LDS ring of saved updated rows instead of the (possibly
+//             stale) loaded values.  Loads of step u + D are issued after the
 //             stores of every step before u by the same wavefront, so the
 //             only rows they can miss are those written in [u, u + D - 1] --
-//             exactly the window the producer checks.
+//             exactly the window the producer checks.  The read's cross-lane
+//             sum is deferred: per-lane partial sums go to LDS and are reduced
+//             for a whole chunk at once with a transposed lane mapping.
+// Memory operations on the state are raw buffer instructions whose offsets
+// are never branched around: an invalid row gets an offset past the buffer
+// range (loads return zero, stores are dropped), which keeps the compiler's
+// count of outstanding loads exact, so the prefetch survives.
 // The two waves meet at one workgroup barrier per chunk.
 #include "device_common.h"
 #include "internal.h"
@@ -42,13 +49,17 @@
 namespace sdm {
 namespace {
 
-constexpr int kChunk = 8;    // steps per plan chunk
-constexpr int kNBuf = 3;     // plan chunks resident (consumer: c, c+1; producer: c+2)
-constexpr int kBmBits = 14;  // bits of a step's write-set bitmap index (2 KiB per step)
+constexpr int kChunk = 8;     // steps per plan chunk
+constexpr int kNBuf = 3;      // plan chunks resident (consumer: c, c+1; producer: c+2)
+constexpr int kBmBits = 14;   // bits of a step's write-set bitmap index (2 KiB per step)
 constexpr int kBmWords = (1 << kBmBits) / 32;
-constexpr uint32_t kInvalid = 0x80000000u;
-constexpr int kRowBits = 22;  // row index bits in plan entries (N <= 2^22)
-constexpr uint32_t kRowMask = (1u << kRowBits) - 1;
+// Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family GPUs.
+constexpr int kBufWord3 = 0x00020000;
+// Byte offset outside every buffer range the kernel builds (one memory slice
+// is below 2^31 bytes): loads there return zero and stores are dropped.
+constexpr uint32_t kOffNone = 0x80000000u;
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 template <typename DT, int COLS>
 struct Tile {
@@ -60,63 +71,34 @@ struct Tile {
   static constexpr int NI = 64 / RPI;      // instructions for 64 rows
 };
 
-// Per-step plan.  Row entries are stored transposed: entry [lr][k] is row
-// slot j = k * RPI + lr, so a lane reads its NI rows contiguously.  A row entry
-// is the row index | (forward code << 22), or kInvalid.  Forward code 0 means
-// "use the loaded value"; otherwise code - 1 = ring * 64 + j' names the
-// updated row j' of the step held in LDS ring slot `ring`.
+// Per-step plan.  Row entries are stored transposed: entry [lr][k] describes
+// row slot j = k * RPI + lr, so a consumer lane reads its NI rows
+// contiguously.  wsrc / rsrc: 0 = the loaded value is current; otherwise
+// src - 1 = ring * 64 + j' names updated row j' of the step in LDS ring slot
+// `ring`.  wsave bit j: write slot j's updated row is needed by a later step
+// of the window (or by this step's read) and must be kept in the ring.
 template <int COLS>
 struct StepPlan {
-  uint32_t wrow[64];
-  uint32_t rrow[64];
+  uint32_t wofs[64];
+  uint32_t rofs[64];
   float wk[64];
   float rw[64];
-  float v[COLS];
+  uint16_t wsrc[64];
+  uint16_t rsrc[64];
+  uint64_t wsave;
+  uint32_t fwd;  // nonzero when some row of this step is forwarded
   float a, b;
-  float pad[2];
+  float pad;
+  float v[COLS];
 };
-
-__device__ __forceinline__ uint32_t row_hash(uint32_t row) {
-  return (row * 2654435761u) >> (32 - kBmBits);
-}
-
-template <typename DT>
-__device__ __forceinline__ void unpack(const uint4& q, float (&f)[16 / sizeof(DT)]) {
-  if constexpr (sizeof(DT) == 4) {
-    f[0] = __uint_as_float(q.x);
-    f[1] = __uint_as_float(q.y);
-    f[2] = __uint_as_float(q.z);
-    f[3] = __uint_as_float(q.w);
-  } else {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-}
-
-template <typename DT>
-__device__ __forceinline__ uint4 pack(const float (&f)[16 / sizeof(DT)]) {
-  if constexpr (sizeof(DT) == 4) {
-    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                      __float_as_uint(f[3]));
-  } else {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16_rne(f[2 * i]) | ((uint32_t)f32_to_bf16_rne(f[2 * i + 1]) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
 
 template <typename DT, int COLS, int D>
 struct ScanShared {
   using TL = Tile<DT, COLS>;
   StepPlan<COLS> plan[kNBuf][kChunk];
-  uint4 upd[D + 1][64 * TL::LPR];  // updated rows of the last D + 1 steps, as stored
-  uint32_t bm[D + 1][kBmWords];    // producer: write-set bitmaps of the last D + 1 steps
+  uint4 upd[D + 1][64 * TL::LPR];            // saved updated rows, as stored
+  float part[kChunk][TL::RPI][COLS];          // per-lane partial read sums
+  uint32_t bm[D + 1][kBmWords];               // producer: write-set bitmaps
 };
 
 // Producer state carried from chunk to chunk: lane j's write row of step
@@ -143,6 +125,43 @@ struct ScanArgs {
   int ntiles;
 };
 
+__device__ __forceinline__ uint32_t row_hash(uint32_t row) {
+  return (row * 2654435761u) >> (32 - kBmBits);
+}
+
+template <typename DT>
+__device__ __forceinline__ void unpack(const u32x4v& q, float (&f)[16 / sizeof(DT)]) {
+  if constexpr (sizeof(DT) == 4) {
+    f[0] = __uint_as_float(q.x);
+    f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z);
+    f[3] = __uint_as_float(q.w);
+  } else {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <typename DT>
+__device__ __forceinline__ u32x4v pack(const float (&f)[16 / sizeof(DT)]) {
+  if constexpr (sizeof(DT) == 4) {
+    return u32x4v{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                  __float_as_uint(f[3])};
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16_rne(f[2 * i]) | ((uint32_t)f32_to_bf16_rne(f[2 * i + 1]) << 16);
+    return u32x4v{w[0], w[1], w[2], w[3]};
+  }
+}
+
+__device__ __forceinline__ u32x4v lds_u4(const uint4& x) { return u32x4v{x.x, x.y, x.z, x.w}; }
+
 // ---------------------------------------------------------------- producer
 
 template <typename DT, int COLS, int D>
@@ -156,6 +175,7 @@ __device__ __forceinline__ void produce_chunk(ScanShared<DT, COLS, D>& sh, Produ
   StepPlan<COLS>* P = sh.plan[c % kNBuf];
   const int64_t base = (int64_t)mem * A.T + t0;
   const uint32_t Nu = (uint32_t)A.N;
+  const uint32_t row_bytes = (uint32_t)(A.d_v * (int)sizeof(DT));
   // Issue all of the chunk's metadata loads first, then consume them.
   int32_t wi[kChunk], ri[kChunk];
   float wkv[kChunk], rwv[kChunk], vv[kChunk], ab[kChunk];
@@ -189,12 +209,13 @@ __device__ __forceinline__ void produce_chunk(ScanShared<DT, COLS, D>& sh, Produ
     if (s >= steps) break;
     const int64_t u = t0 + s;
     const int cur = (int)(u % (D + 1));
+    StepPlan<COLS>& p = P[s];
     const bool wvalid = lane < A.W && (uint32_t)wi[s] < Nu;
     const bool rvalid = lane < A.R && (uint32_t)ri[s] < Nu;
     const int32_t wrow = wvalid ? wi[s] : -1;
     const uint32_t hw = row_hash((uint32_t)wi[s]), hr = row_hash((uint32_t)ri[s]);
-    // write rows: window steps u-1 .. u-D (bitmaps read before this step's
-    // bitmap slot, which held step u-D-1, is recycled)
+    // write rows: window steps u-1 .. u-D (read before this step's bitmap
+    // slot, which held step u-D-1, is recycled)
     bool wcand = false;
 #pragma unroll
     for (int a = 1; a <= D; ++a) {
@@ -204,8 +225,9 @@ __device__ __forceinline__ void produce_chunk(ScanShared<DT, COLS, D>& sh, Produ
     }
     wcand = wcand && wvalid;
     uint4* clr = reinterpret_cast<uint4*>(sh.bm[cur]);
-#pragma unroll
-    for (int i = lane; i < kBmWords / 4; i += kWave) clr[i] = make_uint4(0, 0, 0, 0);
+    clr[lane] = make_uint4(0, 0, 0, 0);
+    clr[lane + kWave] = make_uint4(0, 0, 0, 0);
+    if (lane == 0) p.wsave = 0;
     wave_sync();
     if (wvalid) atomicOr(&sh.bm[cur][hw >> 5], 1u << (hw & 31));
     wave_sync();
@@ -218,65 +240,63 @@ __device__ __forceinline__ void produce_chunk(ScanShared<DT, COLS, D>& sh, Produ
       rcand |= (u - a >= 0) && ((word >> (hr & 31)) & 1u);
     }
     rcand = rcand && rvalid;
-    // exact resolution of the candidates, newest writer first
-    uint32_t wcode = 0, rcode = 0;
+    // exact resolution of the candidates, newest writer first; the writer
+    // step is told to keep that row in the ring
+    uint32_t wsrc = 0, rsrc = 0;
     for (uint64_t m = __ballot(wcand); m; m &= m - 1) {
       const int L = __ffsll((unsigned long long)m) - 1;
       const int32_t row = __builtin_amdgcn_readlane(wi[s], L);
-      uint32_t code = 0;
 #pragma unroll
       for (int a = 1; a <= D; ++a) {
         const uint64_t hit = __ballot(ring.prev[a - 1] == row);
         if (hit) {
-          code = 1 + (uint32_t)((u - a) % (D + 1)) * 64 + (uint32_t)(__ffsll((unsigned long long)hit) - 1);
+          const int jj = __ffsll((unsigned long long)hit) - 1;
+          const int64_t sw = u - a;
+          const uint32_t src = 1 + (uint32_t)(sw % (D + 1)) * 64 + (uint32_t)jj;
+          if (lane == L) wsrc = src;
+          if (lane == 0) sh.plan[(sw / kChunk) % kNBuf][sw % kChunk].wsave |= 1ull << jj;
           break;
         }
       }
-      if (lane == L) wcode = code;
+      wave_sync();
     }
     for (uint64_t m = __ballot(rcand); m; m &= m - 1) {
       const int L = __ffsll((unsigned long long)m) - 1;
       const int32_t row = __builtin_amdgcn_readlane(ri[s], L);
-      uint32_t code = 0;
-      const uint64_t hit0 = __ballot(wrow == row);
-      if (hit0) {
-        code = 1 + (uint32_t)cur * 64 + (uint32_t)(__ffsll((unsigned long long)hit0) - 1);
-      } else {
 #pragma unroll
-        for (int a = 1; a <= D; ++a) {
-          const uint64_t hit = __ballot(ring.prev[a - 1] == row);
-          if (hit) {
-            code = 1 + (uint32_t)((u - a) % (D + 1)) * 64 + (uint32_t)(__ffsll((unsigned long long)hit) - 1);
-            break;
-          }
+      for (int a = 0; a <= D; ++a) {
+        const uint64_t hit = __ballot((a == 0 ? wrow : ring.prev[a > 0 ? a - 1 : 0]) == row);
+        if (hit) {
+          const int jj = __ffsll((unsigned long long)hit) - 1;
+          const int64_t sw = u - a;
+          const uint32_t src = 1 + (uint32_t)(sw % (D + 1)) * 64 + (uint32_t)jj;
+          if (lane == L) rsrc = src;
+          if (lane == 0) sh.plan[(sw / kChunk) % kNBuf][sw % kChunk].wsave |= 1ull << jj;
+          break;
         }
       }
-      if (lane == L) rcode = code;
+      wave_sync();
     }
 #pragma unroll
     for (int a = D - 1; a > 0; --a) ring.prev[a] = ring.prev[a - 1];
     ring.prev[0] = wrow;
-    StepPlan<COLS>& p = P[s];
-    p.wrow[tslot] = wvalid ? ((uint32_t)wi[s] | (wcode << kRowBits)) : kInvalid;
-    p.rrow[tslot] = rvalid ? ((uint32_t)ri[s] | (rcode << kRowBits)) : kInvalid;
+    p.wofs[tslot] = wvalid ? (uint32_t)wi[s] * row_bytes : kOffNone;
+    p.rofs[tslot] = rvalid ? (uint32_t)ri[s] * row_bytes : kOffNone;
     p.wk[tslot] = wkv[s];
-    p.rw[tslot] = rwv[s];
-    if (lane < COLS) p.v[lane] = vv[s];
-    if (lane == 0) p.a = ab[s];
+    p.rw[tslot] = rvalid ? rwv[s] : 0.0f;
+    p.wsrc[tslot] = (uint16_t)wsrc;
+    p.rsrc[tslot] = (uint16_t)rsrc;
+    const bool anyfwd = __ballot(wsrc != 0 || rsrc != 0) != 0;
+    if (lane == 0) {
+      p.fwd = anyfwd ? 1u : 0u;
+      p.a = ab[s];
+    }
     if (lane == 1) p.b = ab[s];
+    if (lane < COLS) p.v[lane] = vv[s];
   }
 }
 
 // ---------------------------------------------------------------- consumer
-
-// Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family GPUs.
-constexpr int kBufWord3 = 0x00020000;
-// Byte offset that is outside every buffer range the kernel builds (memory
-// slices are at most 2^31 bytes): loads there return zero and stores are
-// dropped, so invalid rows need no branch around their memory operations.
-constexpr uint32_t kOffNone = 0x80000000u;
-
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 template <typename DT, int COLS, int D>
 struct Consumer {
@@ -286,7 +306,6 @@ struct Consumer {
   u32x4v wv[D + 1][NI];
   u32x4v rv[D + 1][NI];
   __amdgpu_buffer_rsrc_t mres;  // this memory's tile column, range = the memory slice
-  uint32_t row_bytes;            // d_v * sizeof(DT)
   uint32_t lane_off;             // lc * 16
 
   __device__ __forceinline__ const StepPlan<COLS>& plan(ScanShared<DT, COLS, D>& sh,
@@ -294,11 +313,7 @@ struct Consumer {
     return sh.plan[(u / kChunk) % kNBuf][u % kChunk];
   }
 
-  __device__ __forceinline__ uint32_t offset_of(uint32_t entry) const {
-    return (entry & kInvalid) ? kOffNone : (entry & kRowMask) * row_bytes + lane_off;
-  }
-
-  // Gathers of step u (all rows invalid when u is past the end).
+  // Gathers of step u (nothing is fetched when u is past the end).
   template <int SLOT>
   __device__ __forceinline__ void issue(ScanShared<DT, COLS, D>& sh, int lr, int64_t u,
                                         int64_t T) {
@@ -307,89 +322,123 @@ struct Consumer {
     uint32_t wo[NI], ro[NI];
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-      wo[k] = live ? offset_of(p.wrow[lr * NI + k]) : kOffNone;
-      ro[k] = live ? offset_of(p.rrow[lr * NI + k]) : kOffNone;
+      const uint32_t w = p.wofs[lr * NI + k], r = p.rofs[lr * NI + k];
+      wo[k] = live ? w + lane_off : kOffNone;
+      ro[k] = live ? r + lane_off : kOffNone;
     }
 #pragma unroll
-    for (int k = 0; k < NI; ++k) wv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, wo[k], 0, 0);
+    for (int k = 0; k < NI; ++k)
+      wv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, wo[k], 0, 0);
 #pragma unroll
-    for (int k = 0; k < NI; ++k) rv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ro[k], 0, 0);
+    for (int k = 0; k < NI; ++k)
+      rv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ro[k], 0, 0);
+  }
+
+  // Sum the chunk's per-lane partials into out: lane g handles float4 group
+  // g of the chunk's kChunk x COLS outputs.
+  __device__ __forceinline__ void reduce_chunk(ScanShared<DT, COLS, D>& sh, float* out_mem,
+                                               int d_v, int64_t T, int tile, int64_t t0) {
+    constexpr int G4 = COLS / 4;
+    const int lane = lane_id();
+#pragma unroll
+    for (int g0 = 0; g0 < kChunk * G4; g0 += kWave) {
+      const int g = g0 + lane;
+      if (g < kChunk * G4) {
+        const int s = g / G4, c4 = g % G4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int r = 0; r < RPI; ++r) {
+          const float4 x = *reinterpret_cast<const float4*>(&sh.part[s][r][c4 * 4]);
+          acc.x += x.x;
+          acc.y += x.y;
+          acc.z += x.z;
+          acc.w += x.w;
+        }
+        if (t0 + s < T)
+          *reinterpret_cast<float4*>(out_mem + (t0 + s) * d_v + tile * COLS + c4 * 4) = acc;
+      }
+    }
   }
 
   template <int SLOT>
   __device__ __forceinline__ void step(ScanShared<DT, COLS, D>& sh, float* out_mem, int d_v,
-                                       int64_t T, int64_t col0, int lr, int lc, int64_t u) {
+                                       int64_t T, int tile, int lr, int lc, int64_t u) {
     issue<(SLOT + D) % (D + 1)>(sh, lr, u + D, T);
     const StepPlan<COLS>& p = plan(sh, u);
-    uint32_t wr[NI], rr[NI];
+    uint32_t wo[NI];
     float wkk[NI], rwk[NI], vv[EPL];
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-      wr[k] = p.wrow[lr * NI + k];
-      rr[k] = p.rrow[lr * NI + k];
+      wo[k] = p.wofs[lr * NI + k] + lane_off;  // kOffNone + lane_off is still out of range
       wkk[k] = p.wk[lr * NI + k];
       rwk[k] = p.rw[lr * NI + k];
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) vv[e] = p.v[lc * EPL + e];
     const float a = p.a, b = p.b;
-    uint4* const upd = sh.upd[SLOT];
+    const uint32_t fwd = p.fwd;
+    const uint64_t save = p.wsave;
+    if (fwd) {  // rare: take forwarded rows from the ring
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const uint32_t src = p.wsrc[lr * NI + k];
+        if (src) wv[SLOT][k] = lds_u4(sh.upd[(src - 1) >> 6][((src - 1) & 63) * LPR + lc]);
+      }
+    }
     // gated delta write
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-      const uint32_t code = (wr[k] >> kRowBits) & 0x1FFu;
-      u32x4v q = wv[SLOT][k];
-      if (code && !(wr[k] & kInvalid)) {
-        const uint4 f = sh.upd[(code - 1) >> 6][((code - 1) & 63) * LPR + lc];
-        q = u32x4v{f.x, f.y, f.z, f.w};
-      }
       float m[EPL];
-      unpack<DT>(make_uint4(q.x, q.y, q.z, q.w), m);
+      unpack<DT>(wv[SLOT][k], m);
       const float g = b * wkk[k];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const float mt = a * m[e];
         m[e] = fmaf(g, vv[e] - mt, mt);
       }
-      const uint4 st = pack<DT>(m);
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4v{st.x, st.y, st.z, st.w}, mres,
-                                             offset_of(wr[k]), 0, 0);
-      upd[(k * RPI + lr) * LPR + lc] = st;
+      wv[SLOT][k] = pack<DT>(m);
+      __builtin_amdgcn_raw_buffer_store_b128(wv[SLOT][k], mres, wo[k], 0, 0);
     }
-    wave_sync();
-    // sparse read of the rows as stored after the write
+    if (save) {  // rare: keep the rows a later step (or this read) needs
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int j = k * RPI + lr;
+        if ((save >> j) & 1ull) {
+          const u32x4v q = wv[SLOT][k];
+          sh.upd[SLOT][j * LPR + lc] = make_uint4(q.x, q.y, q.z, q.w);
+        }
+      }
+      wave_sync();
+    }
+    if (fwd) {
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const uint32_t src = p.rsrc[lr * NI + k];
+        if (src) rv[SLOT][k] = lds_u4(sh.upd[(src - 1) >> 6][((src - 1) & 63) * LPR + lc]);
+      }
+    }
+    // sparse read (invalid rows carry weight 0 and load as zero)
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-      const uint32_t code = (rr[k] >> kRowBits) & 0x1FFu;
-      u32x4v q = rv[SLOT][k];
-      if (code && !(rr[k] & kInvalid)) {
-        const uint4 f = sh.upd[(code - 1) >> 6][((code - 1) & 63) * LPR + lc];
-        q = u32x4v{f.x, f.y, f.z, f.w};
-      }
       float m[EPL];
-      unpack<DT>(make_uint4(q.x, q.y, q.z, q.w), m);
-      const float r = (rr[k] & kInvalid) ? 0.0f : rwk[k];
+      unpack<DT>(rv[SLOT][k], m);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(r, m[e], acc[e]);
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(rwk[k], m[e], acc[e]);
     }
+    float* dst = &sh.part[u % kChunk][lr][lc * EPL];
 #pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o);
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    // end of a plan chunk (the last one may be partial): reduce its reads,
+    // then meet the producer, which passes one barrier per chunk
+    if ((u % kChunk) == kChunk - 1 || u == T - 1) {
+      wave_sync();
+      reduce_chunk(sh, out_mem, d_v, T, tile, u - (u % kChunk));
+      __syncthreads();
     }
-    if (lr == 0) {
-      float* o = out_mem + u * d_v + col0;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(o + e) = make_float4(acc[e], acc[e + 1], acc[e + 2],
-                                                        acc[e + 3]);
-    }
-    // end of a plan chunk (the last one may be partial): meet the producer,
-    // which passes one barrier per chunk
-    if ((u % kChunk) == kChunk - 1 || u == T - 1) __syncthreads();
   }
 };
 
@@ -430,11 +479,9 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   const int lr = lane / TL::LPR;
   const int lc = lane % TL::LPR;
   const int d_v = A.d_v;
-  const int64_t col0 = (int64_t)tile * COLS + lc * TL::EPL;
   DT* const Mm = M + (int64_t)mem * A.N * d_v;
   float* const out_mem = A.out + (int64_t)mem * T * d_v;
   Consumer<DT, COLS, D> cs;
-  cs.row_bytes = (uint32_t)(d_v * sizeof(DT));
   cs.lane_off = (uint32_t)(lc * 16);
   cs.mres = __builtin_amdgcn_make_buffer_rsrc(
       Mm + (int64_t)tile * COLS, 0,
@@ -447,16 +494,16 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   if constexpr (D >= 3) cs.template issue<2>(sh, lr, 2, T);
   int64_t u = 0;
   for (; u + D + 1 <= T; u += D + 1) {
-    cs.template step<0>(sh, out_mem, d_v, T, col0, lr, lc, u);
-    cs.template step<1 % (D + 1)>(sh, out_mem, d_v, T, col0, lr, lc, u + 1);
-    if constexpr (D >= 2) cs.template step<2 % (D + 1)>(sh, out_mem, d_v, T, col0, lr, lc, u + 2);
-    if constexpr (D >= 3) cs.template step<3 % (D + 1)>(sh, out_mem, d_v, T, col0, lr, lc, u + 3);
+    cs.template step<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
+    cs.template step<1 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 1);
+    if constexpr (D >= 2) cs.template step<2 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 2);
+    if constexpr (D >= 3) cs.template step<3 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 3);
   }
   // tail: fewer than D + 1 steps
-  if (u < T) cs.template step<0>(sh, out_mem, d_v, T, col0, lr, lc, u);
-  if (u + 1 < T) cs.template step<1 % (D + 1)>(sh, out_mem, d_v, T, col0, lr, lc, u + 1);
+  if (u < T) cs.template step<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
+  if (u + 1 < T) cs.template step<1 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 1);
   if constexpr (D >= 3) {
-    if (u + 2 < T) cs.template step<2 % (D + 1)>(sh, out_mem, d_v, T, col0, lr, lc, u + 2);
+    if (u + 2 < T) cs.template step<2 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 2);
   }
 }
 

@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="mid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs the SDM step on one GPU only: each (b,h) memory is independent, "
@@ -149,6 +152,15 @@ def main():
     rw = torch.empty((B, H, T, R), dtype=f32, device=dev)
     out = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
     torch.cuda.synchronize()
+
+    if args.calib_copy_mib > 0:
+        nelem = args.calib_copy_mib * (1 << 20) // 4
+        csrc = torch.ones(nelem, dtype=f32, device=dev)
+        cdst = torch.empty_like(csrc)
+        torch.cuda.synchronize()
+        cdst.copy_(csrc)
+        torch.cuda.synchronize()
+        del csrc, cdst
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731

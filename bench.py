@@ -7,7 +7,10 @@
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: the learned-state copy M[b,h] = M0[h] (sdm_state_init),
 the write and read product-key selections (sdm_select x2) and the T-step
-gated-delta write + sparse read (sdm_scan).  The default workload is the
+gated-delta write + sparse read (sdm_scan).  The state copy (HBM-bound) and the
+two selections (ALU-bound, independent of it) run concurrently on two HIP
+streams; the scan follows both (--no-overlap runs them back to back).  The
+default workload is the
 N = 2^20, d_v = 128 configuration "mid" (B8 H8 n1024 T4096 W=R=64, fp32
 state); the others are parity-test cases.
 
@@ -105,6 +108,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="mid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the step's kernels back to back on one stream")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")
@@ -163,18 +168,35 @@ def main():
         del csrc, cdst
 
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(record=None):
-        e = [ev() for _ in range(5)] if record is not None else None
-        if e: e[0].record(stream)
-        sdm.state_init(M0, B, out=M)
-        if e: e[1].record(stream)
-        sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk))
-        sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw))
-        if e: e[2].record(stream)
-        sdm.scan(M, widx, wk, ridx, rw, inp["v"], inp["alpha"], inp["beta"], out=out)
-        if e: e[3].record(stream)
+        """init on the main stream; the two selections on the side stream (they
+        are independent of the init, and ALU-bound while the init is
+        HBM-bound); the scan on the main stream after both."""
+        e = [ev() for _ in range(6)]
+        e[0].record(stream)
+        if args.no_overlap:
+            sdm.state_init(M0, B, out=M, stream=stream)
+            e[1].record(stream)
+            e[2].record(stream)
+            sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk), stream=stream)
+            sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw), stream=stream)
+            e[3].record(stream)
+        else:
+            side.wait_event(e[0])  # the previous scan has consumed the selections
+            sdm.state_init(M0, B, out=M, stream=stream)
+            e[1].record(stream)
+            e[2].record(side)
+            sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk), stream=side)
+            sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw), stream=side)
+            e[3].record(side)
+            stream.wait_event(e[3])
+        e[4].record(stream)
+        sdm.scan(M, widx, wk, ridx, rw, inp["v"], inp["alpha"], inp["beta"], out=out,
+                 stream=stream)
+        e[5].record(stream)
         if record is not None:
             record.append(e)
 
@@ -193,8 +215,8 @@ def main():
     ms_total = g0.elapsed_time(g1)
     ms_step = ms_total / args.steps
     init_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / args.steps
-    sel_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
-    scan_ms = sum(r[2].elapsed_time(r[3]) for r in recs) / args.steps
+    sel_ms = sum(r[2].elapsed_time(r[3]) for r in recs) / args.steps
+    scan_ms = sum(r[4].elapsed_time(r[5]) for r in recs) / args.steps
 
     tokens_per_step = B * T
     head_tokens = B * H * T
@@ -221,7 +243,8 @@ def main():
                      "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "kernel": "scan_kernel<float,32>",
                      "algorithmic_bytes_per_launch": slot_bytes},
-        "breakdown_ms": {"state_init": init_ms, "select_write_read": sel_ms, "scan": scan_ms},
+        "breakdown_ms": {"state_init": init_ms, "select_write_read": sel_ms, "scan": scan_ms,
+                         "overlap": "select || state_init" if not args.no_overlap else "none"},
         "scan_tokens_per_s": tokens_per_step / (scan_ms * 1e-3),
         "wall_s": wall,
     }

@@ -101,44 +101,37 @@ def cpu_baseline(cfg, n_heads: int = 4):
             "seconds": dt}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="mid")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-overlap", action="store_true",
-                    help="run the step's kernels back to back on one stream")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="before the steps, run one plain device copy of this many MiB "
-                         "(a known-size kernel for scaling HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs the SDM step on one GPU only: each (b,h) memory is independent, "
-              "so several GPUs would each run their own share with no exchange; "
-              "use --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def _common_record(cfg, args, value, unit, ms_step, dtype, workload, roofline, extra):
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded Philox4x32-10 inputs generated on the GPU)",
+        "config": {"workload": workload, "B": cfg.B, "H": cfg.H, "n": cfg.n, "N": cfg.N,
+                   "d_v": cfg.d_v, "T": cfg.T, "W": cfg.W, "R": cfg.R, "state": args.state},
+        "roofline": roofline,
+    }
+    rec.update(extra)
+    return rec
 
-    import torch
 
-    import sdm_inputs as S
-    import sparse_memory_linear_sdm_amd as sdm
-
-    if not os.path.exists(sdm.LIB_PATH) or not os.path.exists(S.DEV_LIB):
-        import __graft_entry__
-
-        __graft_entry__.build()
-
-    cfg = S.CONFIGS[args.config]
-    if cfg.decode:
-        raise SystemExit("the decode configuration is a parity-test case, not a bench line")
-    assert cfg.state == "f32"
+def run_prefill(cfg, args, torch, S, sdm):
+    """One step = state init + two selections + the T-step scan over the whole
+    [B, H, T] batch (the headline workload)."""
     dev = torch.device("cuda:0")
     B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
-    print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} T{T} W{W} R{R}; generating "
-          f"inputs on the GPU", file=sys.stderr, flush=True)
-
+    sdt = torch.float32 if args.state == "f32" else torch.bfloat16
+    es = 4 if args.state == "f32" else 2
+    print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} T{T} W{W} R{R} {args.state} "
+          f"state; generating inputs on the GPU", file=sys.stderr, flush=True)
     f32 = torch.float32
     inp = {}
     for k in ("s1", "s2", "q1", "q2"):
@@ -150,7 +143,7 @@ def main():
         S.device_block(cfg, k, t)
     M0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
     S.device_block(cfg, "M0", M0)
-    M = torch.empty((B, H, N, d_v), dtype=f32, device=dev)
+    M = torch.empty((B, H, N, d_v), dtype=sdt, device=dev)
     widx = torch.empty((B, H, T, W), dtype=torch.int32, device=dev)
     wk = torch.empty((B, H, T, W), dtype=f32, device=dev)
     ridx = torch.empty((B, H, T, R), dtype=torch.int32, device=dev)
@@ -212,48 +205,208 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = g0.elapsed_time(g1)
-    ms_step = ms_total / args.steps
+    ms_step = g0.elapsed_time(g1) / args.steps
     init_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / args.steps
     sel_ms = sum(r[2].elapsed_time(r[3]) for r in recs) / args.steps
     scan_ms = sum(r[4].elapsed_time(r[5]) for r in recs) / args.steps
 
     tokens_per_step = B * T
-    head_tokens = B * H * T
-    slot_bytes = head_tokens * (2 * W + R) * d_v * 4  # algorithmic, one scan launch
+    slot_bytes = B * H * T * (2 * W + R) * d_v * es  # algorithmic, one scan launch
     scan_gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = measured_traffic(slot_bytes)
-    res = {
-        "metric": METRIC,
-        "value": tokens_per_step / (ms_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded Philox4x32-10 inputs generated on the GPU)",
-        "config": {"workload": f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
-                               f"fp32 state", "B": B, "H": H, "n": n, "N": N, "d_v": d_v,
-                   "T": T, "W": W, "R": R, "state": cfg.state},
-        "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "kernel": "scan_kernel<float,32>",
-                     "algorithmic_bytes_per_launch": slot_bytes},
-        "breakdown_ms": {"state_init": init_ms, "select_write_read": sel_ms, "scan": scan_ms,
-                         "overlap": "select || state_init" if not args.no_overlap else "none"},
-        "scan_tokens_per_s": tokens_per_step / (scan_ms * 1e-3),
-        "wall_s": wall,
-    }
-    if not args.no_cpu_baseline:
+    kname = "scan_kernel<float,32,2>" if es == 4 else "scan_kernel<bf16,64,2>"
+    traffic = measured_traffic(slot_bytes) if (cfg.name == "mid" and es == 4) else None
+    workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
+                f"{args.state} state")
+    roofline = {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": traffic, "kernel": kname,
+                "algorithmic_bytes_per_launch": slot_bytes}
+    extra = {"breakdown_ms": {"state_init": init_ms, "select_write_read": sel_ms,
+                              "scan": scan_ms,
+                              "overlap": "select || state_init" if not args.no_overlap
+                              else "none"},
+             "scan_tokens_per_s": tokens_per_step / (scan_ms * 1e-3),
+             "wall_s": wall}
+    rec = _common_record(cfg, args, tokens_per_step / (ms_step * 1e-3), "tokens/s", ms_step,
+                         "f32" if es == 4 else "f32 math, bf16 state", workload, roofline,
+                         extra)
+    if not args.no_cpu_baseline and es == 4:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg)
+        rec["cpu_baseline"] = cpu_baseline(cfg)
     else:
-        res["cpu_baseline"] = None
-    print(json.dumps(res), flush=True)
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def run_decode(cfg, args, torch, S, sdm):
+    """One step = the T single-token calls of one batch of sequences
+    (sdm_step_decode on every (b,h)); the state is initialised once before the
+    timed steps and persists, as in generation."""
+    dev = torch.device("cuda:0")
+    B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
+    sdt = torch.bfloat16 if args.state == "bf16" else torch.float32
+    es = 2 if args.state == "bf16" else 4
+    print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} {T} calls W{W} R{R} {args.state} "
+          f"state", file=sys.stderr, flush=True)
+    f32 = torch.float32
+    # per-call inputs laid out [T, B, H, ...] so each call's slice is contiguous
+    inp = {}
+    for k in ("s1", "s2", "q1", "q2", "v", "alpha", "beta"):
+        last = (n,) if k in ("s1", "s2", "q1", "q2") else ((d_v,) if k == "v" else ())
+        tmp = torch.empty((B, H, T) + last, dtype=f32, device=dev)
+        S.device_block(cfg, k, tmp)
+        inp[k] = tmp.movedim(2, 0).contiguous()
+        del tmp
+    M0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
+    S.device_block(cfg, "M0", M0)
+    M = sdm.state_init(M0, B, sdt)
+    del M0
+    torch.cuda.empty_cache()
+    out = torch.empty((B, H, d_v), dtype=f32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    names = ("s1", "s2", "q1", "q2", "v", "alpha", "beta")
+
+    def calls():
+        for t in range(T):
+            sdm.step_decode(M, *(inp[k][t] for k in names), W, R, out=out, want_idx=False)
+
+    # The T calls are captured once into a HIP graph and replayed, so the host
+    # launch cost of T small kernels is not what gets measured.
+    calls()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0, g1 = ev(), ev()
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = g0.elapsed_time(g1) / args.steps
+    per_call_us = ms_step * 1e3 / T
+    call_bytes = B * H * ((2 * W + R) * d_v * es + 4 * n * 4 + d_v * 4 * 2)
+    gbps = call_bytes / (per_call_us * 1e-6) / 1e9
+    workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} {T} single-token calls "
+                f"W={W} R={R} {args.state} state")
+    roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": "decode_kernel<16,bf16>" if es == 2 else "decode_kernel<16,f32>",
+                "algorithmic_bytes_per_launch": call_bytes}
+    extra = {"us_per_call": per_call_us, "wall_s": wall, "cpu_baseline": None}
+    return _common_record(cfg, args, B * T / (ms_step * 1e-3), "tokens/s", ms_step,
+                          "f32 math, bf16 state" if es == 2 else "f32", workload, roofline,
+                          extra)
+
+
+def run_long(cfg, args, torch, S, sdm):
+    """One step = the whole T = 2^20 stream in chunks of 16384 steps (inputs of
+    each chunk generated on the GPU before it; only the selections and the
+    scan are timed, with HIP events)."""
+    dev = torch.device("cuda:0")
+    B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
+    C = 16384
+    f32 = torch.float32
+    print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} T{T} in chunks of {C}",
+          file=sys.stderr, flush=True)
+    M0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
+    S.device_block(cfg, "M0", M0)
+    M = sdm.state_init(M0, B)
+    del M0
+    inp = {}
+    for k in ("s1", "s2", "q1", "q2"):
+        inp[k] = torch.empty((B, H, C, n), dtype=f32, device=dev)
+    inp["v"] = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
+    inp["alpha"] = torch.empty((B, H, C), dtype=f32, device=dev)
+    inp["beta"] = torch.empty((B, H, C), dtype=f32, device=dev)
+    widx = torch.empty((B, H, C, W), dtype=torch.int32, device=dev)
+    wk = torch.empty((B, H, C, W), dtype=f32, device=dev)
+    ridx = torch.empty((B, H, C, R), dtype=torch.int32, device=dev)
+    rw = torch.empty((B, H, C, R), dtype=f32, device=dev)
+    out = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    sel_ms = scan_ms = 0.0
+    steps = max(1, args.steps)
+    t0w = time.perf_counter()
+    for rep in range(steps):
+        for c in range(T // C):
+            for k, t in inp.items():
+                S.device_block(cfg, k, t, 0, 0, c * C)
+            e = [ev() for _ in range(3)]
+            e[0].record(stream)
+            sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk))
+            sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw))
+            e[1].record(stream)
+            sdm.scan(M, widx, wk, ridx, rw, inp["v"], inp["alpha"], inp["beta"], out=out)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            sel_ms += e[0].elapsed_time(e[1])
+            scan_ms += e[1].elapsed_time(e[2])
+    wall = time.perf_counter() - t0w
+    sel_ms /= steps
+    scan_ms /= steps
+    ms_step = sel_ms + scan_ms
+    slot_bytes = B * H * T * (2 * W + R) * d_v * 4
+    gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
+    workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
+    roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": "scan_kernel<float,32,2>", "algorithmic_bytes_per_launch":
+                slot_bytes // (T // C)}
+    extra = {"breakdown_ms": {"select_write_read": sel_ms, "scan": scan_ms},
+             "wall_s": wall, "cpu_baseline": None}
+    return _common_record(cfg, args, B * T / (ms_step * 1e-3), "tokens/s", ms_step, "f32",
+                          workload, roofline, extra)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="mid",
+                    help="mid (default, the headline), small, decode or long")
+    ap.add_argument("--state", default=None, help="f32 or bf16 (default: the config's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the step's kernels back to back on one stream")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs the SDM step on one GPU only: each (b,h) memory is independent, "
+              "so several GPUs would each run their own share with no exchange; "
+              "use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sdm_inputs as S
+    import sparse_memory_linear_sdm_amd as sdm
+
+    if not os.path.exists(sdm.LIB_PATH) or not os.path.exists(S.DEV_LIB):
+        import __graft_entry__
+
+        __graft_entry__.build()
+
+    cfg = S.CONFIGS[args.config]
+    if args.state is None:
+        args.state = cfg.state
+    if cfg.decode:
+        rec = run_decode(cfg, args, torch, S, sdm)
+    elif cfg.name == "long":
+        rec = run_long(cfg, args, torch, S, sdm)
+    else:
+        rec = run_prefill(cfg, args, torch, S, sdm)
+    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

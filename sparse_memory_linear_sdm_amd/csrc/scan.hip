@@ -3,13 +3,16 @@
 // "Meccanismo Core", items 3 and 4) for every (b,h) memory.
 //
 // Layout and parallelism.  The update is independent per column, so each
-// memory's d_v columns are split into tiles of 128 bytes (one cache line of a
-// slot row); one workgroup owns one (b,h,tile) and walks t = 0..T-1.  Blocks
+// memory's d_v columns are split into tiles of 32 columns (128 bytes of an
+// fp32 row = one cache line; 64 bytes of a bf16 row, which keeps the same
+// number of workgroups as fp32 -- measured faster than 128-byte bf16 tiles
+// at half the workgroups); one workgroup owns one (b,h,tile) and walks
+// t = 0..T-1.  Blocks
 // are numbered so that all tiles of one memory land on the same XCD (blocks
 // are dealt to the 8 XCDs round-robin), so a memory's index, weight and value
 // traffic is fetched into one L2.  Nothing here is a dense contraction, so
 // there is no MFMA: the kernel is bound by HBM traffic, (2W + R) tile rows
-// per step per tile, all random 128-byte accesses.
+// per step per tile, all random accesses of one tile row each.
 //
 // Two wavefronts per workgroup:
 //   producer  stages each step's metadata into an LDS "plan", two chunks of
@@ -526,16 +529,15 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
                        float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0};
-  // tile = 128 bytes of a row (the whole row when it is shorter)
-  const int cols = dtype == 0 ? (d_v < 32 ? d_v : 32) : (d_v < 64 ? d_v : 64);
+  // tile = 32 columns of a row (the whole row when it is shorter)
+  const int cols = d_v < 32 ? d_v : 32;
   A.ntiles = d_v / cols;
   if (dtype == 0) {
     if (d_v == 16) return launch<float, 16>(M, A, stream);
     return launch<float, 32>(M, A, stream);
   }
   if (d_v == 16) return launch<uint16_t, 16>(M, A, stream);
-  if (d_v == 32) return launch<uint16_t, 32>(M, A, stream);
-  return launch<uint16_t, 64>(M, A, stream);
+  return launch<uint16_t, 32>(M, A, stream);
 }
 
 }  // namespace sdm

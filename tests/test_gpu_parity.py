@@ -237,3 +237,40 @@ def test_step_decode_equals_scan(dtype):
     # products in a different order, so compare within the bar.
     check_values(torch.stack(outs, 2).cpu().numpy(), g["out"].cpu().numpy(), F32,
                  "decode vs scan out")
+
+
+def test_step_decode_graph_replays_match_eager():
+    # The decode calls of several tokens captured in a HIP graph and replayed
+    # three times, with eager work and synchronisations in between; every
+    # replay must equal the same calls run eagerly from the same state.
+    import sparse_memory_linear_sdm_amd as sdm
+
+    torch = _torch()
+    cfg = S.CONFIGS["decode"].with_(B=4, H=2, n=64, T=6, W=16, R=16)
+    dev = to_dev(host_inputs(cfg))
+    steps = [[dev[k][:, :, t].contiguous() for k in NAMES] for t in range(cfg.T)]
+    M0 = torch.from_numpy(S.host_block(cfg, "M0")).cuda()
+    Mg = sdm.state_init(M0, cfg.B, torch.bfloat16)
+    out_g = torch.empty((cfg.B, cfg.H, cfg.d_v), dtype=torch.float32, device="cuda")
+
+    def calls(M, out):
+        for st in steps:
+            sdm.step_decode(M, *st, cfg.W, cfg.R, out=out, want_idx=False)
+
+    calls(Mg, out_g)  # warm up outside the capture
+    torch.cuda.synchronize()
+    Mg.copy_(sdm.state_init(M0, cfg.B, torch.bfloat16))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(Mg, out_g)
+    torch.cuda.synchronize()
+    Mg.copy_(sdm.state_init(M0, cfg.B, torch.bfloat16))
+    Me = sdm.state_init(M0, cfg.B, torch.bfloat16)
+    out_e = torch.empty_like(out_g)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        calls(Me, out_e)
+        torch.cuda.synchronize()
+        assert torch.equal(Mg, Me), f"replay {rep}: state differs"
+        assert torch.equal(out_g, out_e), f"replay {rep}: output differs"

@@ -8,30 +8,84 @@
 //
 // Method, per unit, on one wave of 64 lanes and no sorting of the inputs:
 //   stage 1  each lane holds P = n/64 order-preserving uint32 keys.  The K-th
-//            largest key is found by bisection on the key value, counting
-//            with ballots; the search stops as soon as a probe threshold has
-//            exactly K keys at or above it.  Ties at the final threshold are
-//            resolved by a second bisection on the index.
-//   stage 2  the K stage-1 survivors of x2 are bitonic-sorted (one per lane).
-//            Lane i owns candidate row i (value x1[A_i]); for any threshold
-//            t the row's candidates with key(fl(x1[A_i] + x2[B_j])) >= t form
-//            a prefix j < L_i(t) of the sorted B, because binary32 addition
-//            is monotone.  Bisection on t with counts sum_i L_i(t) (each L_i
-//            found by a per-lane binary search inside the bracket left by
-//            the previous probe) gives the K best candidates, again with a
-//            second bisection on f for ties.  Only those K are sorted.
+//            largest key is found by bisection on the key value; each probe
+//            counts in registers and sums over the wave with DPP.  The search
+//            stops as soon as a probe has exactly K keys at or above it.  Ties
+//            at the final threshold are resolved by bisection on the index.
+//   stage 2  both survivor lists are sorted (rank r for x1, c for x2).  With
+//            both sorted, key(r, c) = key(fl(A_r + B_c)) does not increase
+//            along a row or a column (binary32 addition is monotone), so the
+//            set {key >= t} is a staircase.  A staircase holding at least K
+//            candidates holds at least K of the set
+//                P+ = {(r, c) : (r+1)(c+1) <= K}
+//                     plus, per row, the first pair past that bound,
+//            and one holding exactly K of P+ lies inside P+ (a staircase that
+//            leaves P+ contains a row prefix reaching past the bound, which
+//            already holds K pairs of P+, plus that row's boundary pair).
+//            P+ has at most 343 pairs for K <= 64, so every lane keeps <= 6
+//            of their keys in registers and the bisection of stage 1 applies
+//            to P+ unchanged.  Ties at the K-th key are broken by bisection
+//            on f.  Ties only extend past P+ through a boundary pair; in that
+//            rare case the affected rows' tied runs are added from LDS.
 //   weights  softmax of the K selected sums in fp32 (expf).
 #pragma once
 #include "device_common.h"
 
 namespace sdm {
 
+// ---- the pair lists P+ for every K in 1..64, row-major, entry (r << 8) | c
+namespace pairtab {
+constexpr int kMaxK = 64;
+constexpr int kSlots = 6;  // ceil(max over K of |P+| / 64)
+constexpr int row_len(int K, int r) { return K / (r + 1) + 1 < K ? K / (r + 1) + 1 : K; }
+constexpr int list_len(int K) {
+  int s = 0;
+  for (int r = 0; r < K; ++r) s += row_len(K, r);
+  return s;
+}
+constexpr int total_len() {
+  int s = 0;
+  for (int K = 1; K <= kMaxK; ++K) s += list_len(K);
+  return s;
+}
+constexpr int kTotal = total_len();
+struct Table {
+  uint16_t start[kMaxK + 1];
+  uint16_t len[kMaxK + 1];
+  uint16_t rc[kTotal];
+};
+constexpr Table make() {
+  Table t{};
+  int o = 0;
+  for (int K = 1; K <= kMaxK; ++K) {
+    t.start[K] = (uint16_t)o;
+    t.len[K] = (uint16_t)list_len(K);
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < row_len(K, r); ++c) t.rc[o++] = (uint16_t)((r << 8) | c);
+  }
+  return t;
+}
+static_assert(list_len(kMaxK) <= kSlots * 64, "slot count");
+}  // namespace pairtab
+
+static __constant__ const pairtab::Table kPairTab = pairtab::make();
+
 struct SelectLds {
-  uint32_t akey[64];  // stage-1 survivors of x1: key, index
-  int32_t aidx[64];
-  uint32_t bkey[64];  // stage-1 survivors of x2, sorted by (key desc, idx asc)
-  int32_t bidx[64];
-  uint64_t cand[64];  // stage-2 survivors: (key << 32) | ~f
+  // Stage 1 writes the survivors here (key, index); after sorting, the same
+  // bytes hold the sorted lists as 64-bit words (key << 32) | ~index.
+  union {
+    struct {
+      uint32_t akey[64];
+      int32_t aidx[64];
+      uint32_t bkey[64];
+      int32_t bidx[64];
+    } s1;
+    struct {
+      uint64_t a[64];
+      uint64_t b[64];
+    } sorted;
+  };
+  uint64_t cand[64];  // the K selected: (key << 32) | ~f
 };
 
 // Index of register slot p of a lane: groups of 4 consecutive elements per
@@ -42,6 +96,8 @@ __device__ __forceinline__ int elem_index(int p, int lane) {
   else return p * 64 + lane;
 }
 
+// Keys of one half; slots past n hold 0, below every key of a finite value
+// (those are >= 0x007FFFFF).
 template <int P>
 __device__ __forceinline__ void load_keys(const float* __restrict__ x, int n, int lane,
                                           uint32_t (&u)[P]) {
@@ -64,98 +120,96 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ x, int n, in
   }
 }
 
+// Number of keys >= t over the wave (wave-uniform).  Every threshold used is
+// >= 1, so slots holding 0 never count.
 template <int P>
-__device__ __forceinline__ int count_ge(const uint32_t (&u)[P], uint32_t t, int n, int lane) {
+__device__ __forceinline__ int count_ge(const uint32_t (&u)[P], uint32_t t) {
   int c = 0;
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    bool valid = (P > 1) || (lane < n);
-    c += __popcll(__ballot(valid && u[p] >= t));
-  }
-  return c;
+  for (int p = 0; p < P; ++p) c += u[p] >= t ? 1 : 0;
+  return wave_sum_i32(c);
 }
 
-// Stage 1 for one half: writes the K survivors (key, index) to LDS in index
-// order of their register slots (not sorted).
+// Bisection for the K-th largest of the wave's keys, from lo with
+// count(>= lo) >= K and hi with count(>= hi) < K.  Returns the threshold;
+// *exact tells whether exactly K keys are >= it (else it is the K-th key
+// itself, held by more than one key, and ties at it must be broken).
 template <int P>
-__device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int lane,
-                                       uint32_t* out_key, int32_t* out_idx) {
-  const bool full = (P > 1) || (n >= 64);
-  uint32_t lmax = 0, lmin = 0xFFFFFFFFu;
-  bool any = false;
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    bool valid = (P > 1) || (lane < n);
-    if (valid) {
-      lmax = u[p] > lmax ? u[p] : lmax;
-      lmin = u[p] < lmin ? u[p] : lmin;
-      any = true;
-    }
-  }
-  uint64_t hi = (uint64_t)wave_max_u32(any ? lmax : 0u) + 1;
-  // Every lane holds at least one key when the wave is full, so the smallest
-  // lane maximum has >= 64 >= K keys at or above it.
-  uint64_t lo = full ? (uint64_t)wave_min_u32(lmax) : (uint64_t)wave_min_u32(lmin);
-  int clo = count_ge<P>(u, (uint32_t)lo, n, lane);
-  bool exact = (clo == K);
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&u)[P], int K, uint64_t lo, uint64_t hi,
+                                            bool* exact_out) {
+  bool exact = count_ge<P>(u, (uint32_t)lo) == K;
   while (!exact && hi - lo > 1) {
-    uint64_t mid = lo + ((hi - lo) >> 1);
-    int c = count_ge<P>(u, (uint32_t)mid, n, lane);
-    if (c == K) {
+    const uint64_t mid = lo + ((hi - lo) >> 1);
+    const int c = count_ge<P>(u, (uint32_t)mid);
+    if (c >= K) {
       lo = mid;
-      exact = true;
-    } else if (c > K) {
-      lo = mid;
+      exact = (c == K);
     } else {
       hi = mid;
     }
   }
-  const uint32_t tau = (uint32_t)lo;
+  *exact_out = exact;
+  return (uint32_t)lo;
+}
+
+// Stage 1 for one half: writes the K survivors (key, index) to LDS, in no
+// particular order.
+template <int P>
+__device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int lane,
+                                       uint32_t* out_key, int32_t* out_idx) {
+  uint32_t lmax = 0, lmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    lmax = u[p] > lmax ? u[p] : lmax;
+    lmin = (u[p] != 0u && u[p] < lmin) ? u[p] : lmin;
+  }
+  const uint64_t hi = (uint64_t)wave_max_u32(lmax) + 1;
+  // With n >= 64 every lane holds a key, so the smallest lane maximum has
+  // >= 64 >= K keys at or above it; otherwise start from the smallest key.
+  const uint64_t lo = (n >= 64) ? (uint64_t)wave_min_u32(lmax) : (uint64_t)wave_min_u32(lmin);
+  bool exact;
+  const uint32_t tau = kth_key<P>(u, K, lo, hi, &exact);
   // Tie handling: keys > tau all go in; m = K - #(> tau) of the keys == tau
   // with the lowest indices go in.  ibound = first index NOT taken.
   int ibound = 0x7FFFFFFF;
   if (!exact) {
-    int cgt = count_ge<P>(u, tau + 1u, n, lane);  // tau < 0xFFFFFFFF here
-    int m = K - cgt;
-    int ilo = 0, ihi = n;  // smallest ibound with #(== tau, idx < ibound) >= m
+    const int m = K - count_ge<P>(u, tau + 1u);  // keys of finite values stay below 0xFFFFFFFF
+    int ilo = 1, ihi = n;  // smallest ib with #(== tau, idx < ib) >= m
     while (ilo < ihi) {
-      int mid = (ilo + ihi) >> 1;
+      const int mid = (ilo + ihi) >> 1;
       int c = 0;
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        bool valid = (P > 1) || (lane < n);
-        c += __popcll(__ballot(valid && u[p] == tau && elem_index<P>(p, lane) < mid + 1));
-      }
-      if (c >= m) ihi = mid;
+      for (int p = 0; p < P; ++p) c += (u[p] == tau && elem_index<P>(p, lane) < mid) ? 1 : 0;
+      if (wave_sum_i32(c) >= m) ihi = mid;
       else ilo = mid + 1;
     }
-    ibound = ilo + 1;
+    ibound = ilo;
   }
-  int base = 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int cnt = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    cnt += (u[p] > tau || (u[p] == tau && elem_index<P>(p, lane) < ibound)) ? 1 : 0;
+  int pos = wave_excl_scan_i32(cnt);
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    bool valid = (P > 1) || (lane < n);
-    int i = elem_index<P>(p, lane);
-    bool sel = valid && (exact ? (u[p] >= tau)
-                               : (u[p] > tau || (u[p] == tau && i < ibound)));
-    uint64_t mask = __ballot(sel);
-    if (sel) {
-      int pos = base + __popcll(mask & below);
+    const int i = elem_index<P>(p, lane);
+    if (u[p] > tau || (u[p] == tau && i < ibound)) {
       out_key[pos] = u[p];
       out_idx[pos] = i;
+      ++pos;
     }
-    base += __popcll(mask);
   }
 }
 
-// Number of j in [l, r) (prefix property) with key(a + B_j) >= t, returned as
-// the prefix end.
-__device__ __forceinline__ int prefix_end(float a, const uint32_t* bkey, int l, int r,
-                                          uint32_t t) {
+__device__ __forceinline__ float sorted_val(uint64_t w) { return okey_inv((uint32_t)(w >> 32)); }
+__device__ __forceinline__ int32_t sorted_idx(uint64_t w) { return (int32_t)(~(uint32_t)w); }
+
+// Number of c in [l, r) with key(a + B_c) >= t (a prefix of [l, r) by
+// monotonicity), returned as the prefix end.
+__device__ __forceinline__ int prefix_end(float a, const uint64_t* b, int l, int r, uint32_t t) {
   while (l < r) {
-    int m = (l + r) >> 1;
-    if (okey(a + okey_inv(bkey[m])) >= t) l = m + 1;
+    const int m = (l + r) >> 1;
+    if (okey(a + sorted_val(b[m])) >= t) l = m + 1;
     else r = m;
   }
   return l;
@@ -167,96 +221,117 @@ template <int P>
 __device__ void select_unit(const float* __restrict__ x1, const float* __restrict__ x2, int n,
                             int K, SelectLds& s, int32_t* __restrict__ idx_out,
                             float* __restrict__ score_out, float* __restrict__ weight_out) {
+  constexpr int S = pairtab::kSlots;
   const int lane = lane_id();
-  uint32_t u[P];
+
+  // The pair list of this K, fetched first so that its latency hides under
+  // stage 1.
+  const int plen = kPairTab.len[K];
+  const uint16_t* prc = kPairTab.rc + kPairTab.start[K];
+  uint32_t rc[S];
+#pragma unroll
+  for (int p = 0; p < S; ++p) {
+    const int q = p * 64 + lane;
+    rc[p] = q < plen ? prc[q] : 0xFFFFu;
+  }
 
   // ---- stage 1, both halves
+  uint32_t u[P];
   load_keys<P>(x1, n, lane, u);
-  stage1<P>(u, n, K, lane, s.akey, s.aidx);
+  stage1<P>(u, n, K, lane, s.s1.akey, s.s1.aidx);
   load_keys<P>(x2, n, lane, u);
-  stage1<P>(u, n, K, lane, s.bkey, s.bidx);
+  stage1<P>(u, n, K, lane, s.s1.bkey, s.s1.bidx);
   wave_sync();
 
-  // ---- sort B survivors by (key desc, index asc)
-  {
-    uint64_t kb = 0;
-    if (lane < K) kb = ((uint64_t)s.bkey[lane] << 32) | (uint32_t)(~(uint32_t)s.bidx[lane]);
-    kb = wave_sort_desc_u64(kb);
-    wave_sync();
-    if (lane < K) {
-      s.bkey[lane] = (uint32_t)(kb >> 32);
-      s.bidx[lane] = (int32_t)(~(uint32_t)kb);
-    }
-    wave_sync();
+  // ---- sort both survivor lists by (key desc, index asc)
+  uint64_t ka = 0, kb = 0;
+  if (lane < K) {
+    ka = ((uint64_t)s.s1.akey[lane] << 32) | (uint32_t)(~(uint32_t)s.s1.aidx[lane]);
+    kb = ((uint64_t)s.s1.bkey[lane] << 32) | (uint32_t)(~(uint32_t)s.s1.bidx[lane]);
   }
+  wave_sort2_desc_u64(ka, kb);
+  wave_sync();
+  s.sorted.a[lane] = ka;
+  s.sorted.b[lane] = kb;
+  wave_sync();
 
-  // ---- stage 2: lane i owns candidate row A_i
-  const bool row = lane < K;
-  const float a = row ? okey_inv(s.akey[lane]) : 0.0f;
-  const int32_t arow = row ? s.aidx[lane] : 0;
-  const float amax = okey_inv(wave_max_u32(row ? s.akey[lane] : 0u));
-  const float b0 = okey_inv(s.bkey[0]);
-  const float bl = okey_inv(s.bkey[K - 1]);
-  uint64_t lo = okey(amax + bl);            // the row of amax has K candidates >= lo
-  uint64_t hi = (uint64_t)okey(amax + b0) + 1;  // no candidate reaches hi
-  int Llo = 0;                              // L_i(hi)
-  int Lhi = row ? prefix_end(a, s.bkey, 0, K, (uint32_t)lo) : 0;  // L_i(lo)
-  bool exact = (wave_sum_i32(Lhi) == K);
-  int Lsel = Lhi;
-  while (!exact && hi - lo > 1) {
-    uint64_t mid = lo + ((hi - lo) >> 1);
-    int L = row ? prefix_end(a, s.bkey, Llo, Lhi, (uint32_t)mid) : 0;
-    int c = wave_sum_i32(L);
-    if (c == K) {
-      exact = true;
-      Lsel = L;
-    } else if (c > K) {
-      lo = mid;
-      Lhi = L;
-    } else {
-      hi = mid;
-      Llo = L;
+  // ---- stage 2 over P+: slot keys and flat indices in registers
+  uint32_t sk[S];
+  int32_t sf[S];
+  uint32_t bnd = 0;  // bit p: slot p is a boundary pair, (r+1)(c+1) > K
+#pragma unroll
+  for (int p = 0; p < S; ++p) {
+    sk[p] = 0u;
+    sf[p] = 0x7FFFFFFF;
+    if (rc[p] != 0xFFFFu) {
+      const int r = (int)(rc[p] >> 8), c = (int)(rc[p] & 0xFFu);
+      const uint64_t wa = s.sorted.a[r], wb = s.sorted.b[c];
+      sk[p] = okey(sorted_val(wa) + sorted_val(wb));
+      sf[p] = sorted_idx(wa) * n + sorted_idx(wb);
+      bnd |= ((r + 1) * (c + 1) > K) ? (1u << p) : 0u;
     }
   }
-  // Selected candidates of this lane's row: j < Lsel (exact case), or
-  // j < Llo plus the ties j in [Llo, Lhi) (all with key == lo) whose flat
-  // index is below fbound.
-  int fbound = 0;
+  const float a0 = sorted_val(s.sorted.a[0]);
+  // Row 0 holds K pairs of P+ with key >= key(A_0 + B_{K-1}); none reaches
+  // key(A_0 + B_0) + 1.
+  const uint64_t lo0 = okey(a0 + sorted_val(s.sorted.b[K - 1]));
+  const uint64_t hi0 = (uint64_t)okey(a0 + sorted_val(s.sorted.b[0])) + 1;
+  bool exact;
+  const uint32_t tau = kth_key<S>(sk, K, lo0, hi0, &exact);
+
+  // Ties at tau (not exact): m of them go in, lowest f first.  Tied pairs
+  // outside P+ exist only in rows whose boundary pair ties; lane r then adds
+  // the tied columns (cb, xhi) of row r.
+  int fbound = 0x7FFFFFFF;
+  int xlo = 0, xhi = 0;
+  int32_t arow_idx = 0;
   if (!exact) {
-    int cgt = wave_sum_i32(Llo);
-    int m = K - cgt;
-    const int nn = n * n;
-    int flo = 0, fhi = nn;  // smallest fb with #(ties with f < fb) >= m
+    const int m = K - count_ge<S>(sk, tau + 1u);
+    bool btie = false;
+#pragma unroll
+    for (int p = 0; p < S; ++p) btie |= ((bnd >> p) & 1u) && sk[p] == tau;
+    if (__ballot(btie) != 0ull && lane < K) {
+      const int cb = K / (lane + 1);
+      if (cb < K) {
+        const uint64_t wa = s.sorted.a[lane];
+        const float arow = sorted_val(wa);
+        if (okey(arow + sorted_val(s.sorted.b[cb])) == tau) {
+          arow_idx = sorted_idx(wa);
+          xlo = cb + 1;
+          xhi = prefix_end(arow, s.sorted.b, cb + 1, K, tau);
+        }
+      }
+    }
+    int flo = 1, fhi = n * n;  // smallest fb with #(ties, f < fb) >= m
     while (flo < fhi) {
-      int fm = flo + ((fhi - flo) >> 1);
+      const int fm = flo + ((fhi - flo) >> 1);
       int c = 0;
-      if (row)
-        for (int j = Llo; j < Lhi; ++j) c += (arow * n + s.bidx[j] < fm + 1) ? 1 : 0;
-      c = wave_sum_i32(c);
-      if (c >= m) fhi = fm;
+#pragma unroll
+      for (int p = 0; p < S; ++p) c += (sk[p] == tau && sf[p] < fm) ? 1 : 0;
+      for (int j = xlo; j < xhi; ++j) c += (arow_idx * n + sorted_idx(s.sorted.b[j]) < fm) ? 1 : 0;
+      if (wave_sum_i32(c) >= m) fhi = fm;
       else flo = fm + 1;
     }
-    fbound = flo + 1;
+    fbound = flo;
   }
-  // Compact the K selected candidates into LDS.
+
+  // ---- compact the K selected pairs into LDS
   {
     int cnt = 0;
-    if (row) {
-      if (exact) cnt = Lsel;
-      else {
-        cnt = Llo;
-        for (int j = Llo; j < Lhi; ++j) cnt += (arow * n + s.bidx[j] < fbound) ? 1 : 0;
-      }
-    }
+#pragma unroll
+    for (int p = 0; p < S; ++p)
+      cnt += (sk[p] > tau || (sk[p] == tau && (exact || sf[p] < fbound))) ? 1 : 0;
+    for (int j = xlo; j < xhi; ++j)
+      cnt += (arow_idx * n + sorted_idx(s.sorted.b[j]) < fbound) ? 1 : 0;
     int pos = wave_excl_scan_i32(cnt);
-    if (row) {
-      int end = exact ? Lsel : Lhi;
-      for (int j = 0; j < end; ++j) {
-        int32_t f = arow * n + s.bidx[j];
-        if (!exact && j >= Llo && f >= fbound) continue;
-        float sig = a + okey_inv(s.bkey[j]);
-        s.cand[pos++] = ((uint64_t)okey(sig) << 32) | (uint32_t)(~(uint32_t)f);
-      }
+#pragma unroll
+    for (int p = 0; p < S; ++p) {
+      if (sk[p] > tau || (sk[p] == tau && (exact || sf[p] < fbound)))
+        s.cand[pos++] = ((uint64_t)sk[p] << 32) | (uint32_t)(~(uint32_t)sf[p]);
+    }
+    for (int j = xlo; j < xhi; ++j) {
+      const int32_t f = arow_idx * n + sorted_idx(s.sorted.b[j]);
+      if (f < fbound) s.cand[pos++] = ((uint64_t)tau << 32) | (uint32_t)(~(uint32_t)f);
     }
     wave_sync();
   }
@@ -265,7 +340,7 @@ __device__ void select_unit(const float* __restrict__ x1, const float* __restric
   uint64_t kc = lane < K ? s.cand[lane] : 0ull;
   kc = wave_sort_desc_u64(kc);
   const float sig = okey_inv((uint32_t)(kc >> 32));
-  const float top = __shfl(sig, 0);
+  const float top = lane0_f32(sig);
   const float e = lane < K ? expf(sig - top) : 0.0f;
   const float z = wave_sum_f32(e);
   if (lane < K) {

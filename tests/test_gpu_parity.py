@@ -53,6 +53,20 @@ def test_select_integer_ties(n, K):
     _sel_case(x1, x2, K)
 
 
+@pytest.mark.parametrize("n,K,spread", [(64, 64, 0.9), (256, 64, 3.0), (1024, 33, 0.9),
+                                        (1024, 64, 5.0), (128, 7, 3.0)])
+def test_select_rounding_ties(n, K, spread):
+    # x1 on even integers near 2^24 (ulp 2) and x2 small: binary32 sums round
+    # back onto the x1 grid, so whole rows of stage-2 pairs tie although the
+    # x2 values differ; ties run far past any small candidate set and the
+    # lower flat index must still win every one of them.
+    rng = np.random.default_rng(n * 7 + K)
+    x1 = (2.0 ** 24 + 2.0 * rng.integers(0, 6, (200, n))).astype(np.float32)
+    x2 = rng.uniform(-spread, spread, (200, n)).astype(np.float32)
+    _sel_case(x1, x2, K)
+    _sel_case(x2, x1, K)
+
+
 def test_select_degenerate_inputs():
     n = 256
     z = np.zeros((4, n), np.float32)

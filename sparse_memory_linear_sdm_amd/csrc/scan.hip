@@ -23,12 +23,15 @@
 //             window: for each row of step u, the newest step s in
 //             [u - D, u] (s < u for write rows) writing the same row.  Each
 //             step's write set is recorded as a bitmap of hashed rows; a row
-//             whose bit is clear in every window bitmap has no hazard (one LDS
-//             read per row and window step, no per-lane loops).  The rare
-//             candidates are resolved exactly with wave-uniform ballots
+//             whose bit is clear in every window bitmap has no hazard.  The
+//             rare candidates are resolved exactly with wave-uniform ballots
 //             against the window's write rows kept in registers.  The plan
 //             then names, per row, where its current value lives, and marks
 //             in the writing step which updated rows a later step will need.
+//             A chunk is handled in batches (clear its bitmaps, set them, probe
+//             them, resolve, write the plan), so the producer pays a few LDS
+//             round trips per chunk rather than per step, and the metadata of
+//             the next chunk is loaded while the current one is processed.
 //   consumer  keeps the row gathers of D steps in flight in a register ring:
 //             at step u it issues the 16-byte buffer loads of step u + D, then
 //             updates step u's W rows (Mt = alpha*M; M = Mt + (beta*k)(v - Mt)
@@ -56,6 +59,7 @@ constexpr int kChunk = 8;     // steps per plan chunk
 constexpr int kNBuf = 3;      // plan chunks resident (consumer: c, c+1; producer: c+2)
 constexpr int kBmBits = 14;   // bits of a step's write-set bitmap index (2 KiB per step)
 constexpr int kBmWords = (1 << kBmBits) / 32;
+constexpr int kBmSlots = 2 * kChunk;  // bitmaps of the last two chunks' steps, slot = u % 16
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family GPUs.
 constexpr int kBufWord3 = 0x00020000;
 // Byte offset outside every buffer range the kernel builds (one memory slice
@@ -76,23 +80,25 @@ struct Tile {
 
 // Per-step plan.  Row entries are stored transposed: entry [lr][k] describes
 // row slot j = k * RPI + lr, so a consumer lane reads its NI rows
-// contiguously.  wsrc / rsrc: 0 = the loaded value is current; otherwise
-// src - 1 = ring * 64 + j' names updated row j' of the step in LDS ring slot
-// `ring`.  wsave bit j: write slot j's updated row is needed by a later step
-// of the window (or by this step's read) and must be kept in the ring.
+// contiguously.  src: low half for the write row, high half for the read
+// row; 0 = the loaded value is current, otherwise src - 1 = ring * 64 + j'
+// names updated row j' of the step in LDS ring slot `ring`.  wsave bit j:
+// write slot j's updated row is needed by a later step of the window (or by
+// this step's read) and must be kept in the ring.  Every producer lane writes
+// one entry of v and sc (entries past COLS, and sc past 2, are unused), so
+// the plan is written without branches.
+enum { kScAlpha = 0, kScBeta = 1, kScFwd = 2 };
 template <int COLS>
 struct StepPlan {
   uint32_t wofs[64];
   uint32_t rofs[64];
   float wk[64];
   float rw[64];
-  uint16_t wsrc[64];
-  uint16_t rsrc[64];
+  uint32_t src[64];
+  float v[64];
+  uint32_t sc[64];  // alpha, beta (float bits), forward flag
   uint64_t wsave;
-  uint32_t fwd;  // nonzero when some row of this step is forwarded
-  float a, b;
-  float pad;
-  float v[COLS];
+  uint64_t pad;
 };
 
 template <typename DT, int COLS, int D>
@@ -101,14 +107,9 @@ struct ScanShared {
   StepPlan<COLS> plan[kNBuf][kChunk];
   uint4 upd[D + 1][64 * TL::LPR];            // saved updated rows, as stored
   float part[kChunk][TL::RPI][COLS];          // per-lane partial read sums
-  uint32_t bm[D + 1][kBmWords];               // producer: write-set bitmaps
-};
-
-// Producer state carried from chunk to chunk: lane j's write row of step
-// u - a in prev[a - 1] (-1 when that slot wrote nothing valid).
-template <int D>
-struct ProducerRing {
-  int32_t prev[D];
+  uint32_t bm[kBmSlots][kBmWords];            // producer: write-set bitmaps
+  int32_t wrows[kBmSlots][64];                // producer: write rows, slot = u % 16
+  int32_t rrows[kChunk][64];                  // producer: read rows of the current chunk
 };
 
 struct ScanArgs {
@@ -128,8 +129,16 @@ struct ScanArgs {
   int ntiles;
 };
 
-__device__ __forceinline__ uint32_t row_hash(uint32_t row) {
-  return (row * 2654435761u) >> (32 - kBmBits);
+// Write-set filter: a row sets two bits of one 32-bit word of the step's
+// bitmap (word and bit positions from two multiplicative hashes), and a probe
+// is a candidate only when both bits are set.  Set and probe are one LDS
+// operation each, and false candidates are far rarer than with one bit.
+struct RowKey {
+  uint32_t word, mask;
+};
+__device__ __forceinline__ RowKey row_key(uint32_t row) {
+  const uint32_t h1 = row * 2654435761u, h2 = row * 0x85EBCA77u;
+  return RowKey{h1 >> (32 - (kBmBits - 5)), (1u << (h2 >> 27)) | (1u << ((h2 >> 22) & 31u))};
 }
 
 template <typename DT>
@@ -167,137 +176,166 @@ __device__ __forceinline__ u32x4v lds_u4(const uint4& x) { return u32x4v{x.x, x.
 
 // ---------------------------------------------------------------- producer
 
-template <typename DT, int COLS, int D>
-__device__ __forceinline__ void produce_chunk(ScanShared<DT, COLS, D>& sh, ProducerRing<D>& ring,
-                                              const ScanArgs A, int mem, int tile, int64_t c) {
-  using TL = Tile<DT, COLS>;
-  const int lane = lane_id();
-  const int64_t t0 = c * kChunk;
-  if (t0 >= A.T) return;
-  const int steps = (int)((A.T - t0) < kChunk ? (A.T - t0) : kChunk);
-  StepPlan<COLS>* P = sh.plan[c % kNBuf];
-  const int64_t base = (int64_t)mem * A.T + t0;
-  const uint32_t Nu = (uint32_t)A.N;
-  const uint32_t row_bytes = (uint32_t)(A.d_v * (int)sizeof(DT));
-  // Issue all of the chunk's metadata loads first, then consume them.
+// One chunk's metadata as loaded by the producer wave: lane j holds write
+// slot j and read slot j of every step; lanes < COLS hold v; lanes 0, 1 hold
+// alpha, beta.
+struct ChunkMeta {
   int32_t wi[kChunk], ri[kChunk];
-  float wkv[kChunk], rwv[kChunk], vv[kChunk], ab[kChunk];
+  float wk[kChunk], rw[kChunk], v[kChunk], ab[kChunk];
+};
+
+template <typename DT, int COLS, int D>
+struct Producer {
+  using TL = Tile<DT, COLS>;
+
+  // Issue the loads of chunk c (nothing past the end); no wait here.
+  __device__ __forceinline__ void load(ChunkMeta& m, const ScanArgs& A, int mem, int tile,
+                                       int64_t c) const {
+    const int lane = lane_id();
+    const int64_t t0 = c * kChunk;
+    const int64_t base = (int64_t)mem * A.T + t0;
 #pragma unroll
-  for (int s = 0; s < kChunk; ++s) {
-    wi[s] = -1;
-    ri[s] = -1;
-    wkv[s] = 0.f;
-    rwv[s] = 0.f;
-    vv[s] = 0.f;
-    ab[s] = 0.f;
-    if (s < steps) {
-      const int64_t t = base + s;
-      if (lane < A.W) {
-        wi[s] = A.widx[t * A.W + lane];
-        wkv[s] = A.wk[t * A.W + lane];
+    for (int s = 0; s < kChunk; ++s) {
+      m.wi[s] = -1;
+      m.ri[s] = -1;
+      m.wk[s] = 0.f;
+      m.rw[s] = 0.f;
+      m.v[s] = 0.f;
+      m.ab[s] = 0.f;
+      if (t0 + s < A.T) {
+        const int64_t t = base + s;
+        if (lane < A.W) {
+          m.wi[s] = A.widx[t * A.W + lane];
+          m.wk[s] = A.wk[t * A.W + lane];
+        }
+        if (lane < A.R) {
+          m.ri[s] = A.ridx[t * A.R + lane];
+          m.rw[s] = A.rw[t * A.R + lane];
+        }
+        if (lane < COLS) m.v[s] = A.v[t * A.d_v + (int64_t)tile * COLS + lane];
+        if (lane == 0) m.ab[s] = A.alpha[t];
+        if (lane == 1) m.ab[s] = A.beta[t];
       }
-      if (lane < A.R) {
-        ri[s] = A.ridx[t * A.R + lane];
-        rwv[s] = A.rw[t * A.R + lane];
-      }
-      if (lane < COLS) vv[s] = A.v[t * A.d_v + (int64_t)tile * COLS + lane];
-      if (lane == 0) ab[s] = A.alpha[t];
-      if (lane == 1) ab[s] = A.beta[t];
     }
   }
-  const int lr = lane % TL::RPI, k = lane / TL::RPI;
-  const int tslot = lr * TL::NI + k;  // transposed position of row slot j = lane
+
+  // Build the plan of chunk c from its loaded metadata.
+  __device__ __forceinline__ void produce(ScanShared<DT, COLS, D>& sh, const ChunkMeta& m,
+                                          const ScanArgs& A, int64_t c) {
+    const int lane = lane_id();
+    const int64_t t0 = c * kChunk;
+    if (t0 >= A.T) return;
+    const int steps = (int)((A.T - t0) < kChunk ? (A.T - t0) : kChunk);
+    StepPlan<COLS>* P = sh.plan[c % kNBuf];
+    const uint32_t Nu = (uint32_t)A.N;
+    const uint32_t row_bytes = (uint32_t)(A.d_v * (int)sizeof(DT));
+    const int slot0 = (int)(t0 % kBmSlots);  // 0 or kChunk
+    int32_t wrow[kChunk], rrow[kChunk];
+    RowKey hw[kChunk], hr[kChunk];
 #pragma unroll
-  for (int s = 0; s < kChunk; ++s) {
-    if (s >= steps) break;
-    const int64_t u = t0 + s;
-    const int cur = (int)(u % (D + 1));
-    StepPlan<COLS>& p = P[s];
-    const bool wvalid = lane < A.W && (uint32_t)wi[s] < Nu;
-    const bool rvalid = lane < A.R && (uint32_t)ri[s] < Nu;
-    const int32_t wrow = wvalid ? wi[s] : -1;
-    const uint32_t hw = row_hash((uint32_t)wi[s]), hr = row_hash((uint32_t)ri[s]);
-    // write rows: window steps u-1 .. u-D (read before this step's bitmap
-    // slot, which held step u-D-1, is recycled)
-    bool wcand = false;
-#pragma unroll
-    for (int a = 1; a <= D; ++a) {
-      const int sl = (int)((u - a + (D + 1)) % (D + 1));
-      const uint32_t word = sh.bm[sl][hw >> 5];
-      wcand |= (u - a >= 0) && ((word >> (hw & 31)) & 1u);
+    for (int s = 0; s < kChunk; ++s) {
+      const bool wv = s < steps && lane < A.W && (uint32_t)m.wi[s] < Nu;
+      const bool rv = s < steps && lane < A.R && (uint32_t)m.ri[s] < Nu;
+      wrow[s] = wv ? m.wi[s] : -1;
+      rrow[s] = rv ? m.ri[s] : -1;
+      hw[s] = row_key((uint32_t)m.wi[s]);
+      hr[s] = row_key((uint32_t)m.ri[s]);
     }
-    wcand = wcand && wvalid;
-    uint4* clr = reinterpret_cast<uint4*>(sh.bm[cur]);
-    clr[lane] = make_uint4(0, 0, 0, 0);
-    clr[lane + kWave] = make_uint4(0, 0, 0, 0);
-    if (lane == 0) p.wsave = 0;
+    // 1. clear this chunk's bitmaps (they held the steps of chunk c - 2) and
+    //    the wsave masks of its steps
+    {
+      uint4* clr = reinterpret_cast<uint4*>(sh.bm[slot0]);
+      constexpr int kVec = kChunk * kBmWords / 4;
+#pragma unroll
+      for (int i = 0; i < kVec / kWave; ++i) clr[i * kWave + lane] = make_uint4(0, 0, 0, 0);
+      P[lane & (kChunk - 1)].wsave = 0;  // every lane clears one mask; all 8 get cleared
+    }
     wave_sync();
-    if (wvalid) atomicOr(&sh.bm[cur][hw >> 5], 1u << (hw & 31));
+    // 2. record each step's write set, and stage its rows for exact checks
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s) {
+      atomicOr(&sh.bm[slot0 + s][hw[s].word], wrow[s] >= 0 ? hw[s].mask : 0u);
+      sh.wrows[slot0 + s][lane] = wrow[s];
+      sh.rrows[s][lane] = rrow[s];
+    }
     wave_sync();
-    // read rows: window steps u .. u-D
-    bool rcand = false;
+    // 3. probe: write rows against steps u-1 .. u-D, read rows against u .. u-D
+    uint32_t wcand = 0, rcand = 0;  // bit s: this lane's row of step s is a candidate
 #pragma unroll
-    for (int a = 0; a <= D; ++a) {
-      const int sl = (int)((u - a + (D + 1)) % (D + 1));
-      const uint32_t word = sh.bm[sl][hr >> 5];
-      rcand |= (u - a >= 0) && ((word >> (hr & 31)) & 1u);
-    }
-    rcand = rcand && rvalid;
-    // exact resolution of the candidates, newest writer first; the writer
-    // step is told to keep that row in the ring
-    uint32_t wsrc = 0, rsrc = 0;
-    for (uint64_t m = __ballot(wcand); m; m &= m - 1) {
-      const int L = __ffsll((unsigned long long)m) - 1;
-      const int32_t row = __builtin_amdgcn_readlane(wi[s], L);
-#pragma unroll
-      for (int a = 1; a <= D; ++a) {
-        const uint64_t hit = __ballot(ring.prev[a - 1] == row);
-        if (hit) {
-          const int jj = __ffsll((unsigned long long)hit) - 1;
-          const int64_t sw = u - a;
-          const uint32_t src = 1 + (uint32_t)(sw % (D + 1)) * 64 + (uint32_t)jj;
-          if (lane == L) wsrc = src;
-          if (lane == 0) sh.plan[(sw / kChunk) % kNBuf][sw % kChunk].wsave |= 1ull << jj;
-          break;
-        }
-      }
-      wave_sync();
-    }
-    for (uint64_t m = __ballot(rcand); m; m &= m - 1) {
-      const int L = __ffsll((unsigned long long)m) - 1;
-      const int32_t row = __builtin_amdgcn_readlane(ri[s], L);
+    for (int s = 0; s < kChunk; ++s) {
+      const int64_t u = t0 + s;
+      bool wc = false, rc = false;
 #pragma unroll
       for (int a = 0; a <= D; ++a) {
-        const uint64_t hit = __ballot((a == 0 ? wrow : ring.prev[a > 0 ? a - 1 : 0]) == row);
-        if (hit) {
-          const int jj = __ffsll((unsigned long long)hit) - 1;
-          const int64_t sw = u - a;
-          const uint32_t src = 1 + (uint32_t)(sw % (D + 1)) * 64 + (uint32_t)jj;
-          if (lane == L) rsrc = src;
-          if (lane == 0) sh.plan[(sw / kChunk) % kNBuf][sw % kChunk].wsave |= 1ull << jj;
-          break;
+        const int sl = (slot0 + s - a + kBmSlots) % kBmSlots;
+        const bool live = u - a >= 0;
+        if (a > 0) wc |= live && (sh.bm[sl][hw[s].word] & hw[s].mask) == hw[s].mask;
+        rc |= live && (sh.bm[sl][hr[s].word] & hr[s].mask) == hr[s].mask;
+      }
+      wcand |= (wc && wrow[s] >= 0) ? (1u << s) : 0u;
+      rcand |= (rc && rrow[s] >= 0) ? (1u << s) : 0u;
+    }
+    // 4. the plan, with every row taken as loaded
+    const int lr = lane % TL::RPI, k = lane / TL::RPI;
+    const int tslot = lr * TL::NI + k;  // transposed position of row slot j = lane
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s) {
+      if (s < steps) {
+        StepPlan<COLS>& p = P[s];
+        p.wofs[tslot] = wrow[s] >= 0 ? (uint32_t)wrow[s] * row_bytes : kOffNone;
+        p.rofs[tslot] = rrow[s] >= 0 ? (uint32_t)rrow[s] * row_bytes : kOffNone;
+        p.wk[tslot] = m.wk[s];
+        p.rw[tslot] = rrow[s] >= 0 ? m.rw[s] : 0.0f;
+        p.src[tslot] = 0u;
+        p.v[lane] = m.v[s];
+        p.sc[lane] = lane == kScFwd ? 0u : __float_as_uint(m.ab[s]);
+      }
+    }
+    wave_sync();
+    // 5. exact resolution of the (rare) candidates, newest writer first: the
+    //    row's source in the plan becomes the writer's ring entry, the step
+    //    is flagged, and the writer step is told to keep that row
+    if (__ballot((wcand | rcand) != 0u) != 0ull) resolve(sh, wcand, rcand, t0, steps, slot0, tslot);
+  }
+
+  __device__ void resolve(ScanShared<DT, COLS, D>& sh, uint32_t wcand, uint32_t rcand,
+                          int64_t t0, int steps, int slot0, int tslot) {
+    const int lane = lane_id();
+#pragma unroll 1
+    for (int s = 0; s < steps; ++s) {
+      const uint64_t wm = __ballot((wcand >> s) & 1u), rm = __ballot((rcand >> s) & 1u);
+      if ((wm | rm) == 0ull) continue;
+      const int64_t u = t0 + s;
+      uint32_t src = 0;
+      for (int pass = 0; pass < 2; ++pass) {  // write rows (a >= 1), then read rows (a >= 0)
+        const int a0 = pass == 0 ? 1 : 0;
+        for (uint64_t mk = pass == 0 ? wm : rm; mk; mk &= mk - 1) {
+          const int L = __ffsll((unsigned long long)mk) - 1;
+          const int32_t row = pass == 0 ? sh.wrows[slot0 + s][L] : sh.rrows[s][L];
+          for (int a = a0; a <= D && u - a >= 0; ++a) {
+            const int sl = (slot0 + s - a + kBmSlots) % kBmSlots;
+            const uint64_t hit = __ballot(sh.wrows[sl][lane] == row);
+            if (hit) {
+              const int jj = __ffsll((unsigned long long)hit) - 1;
+              const int64_t sw = u - a;
+              const uint32_t code = 1 + (uint32_t)(sw % (D + 1)) * 64 + (uint32_t)jj;
+              if (lane == L) src |= pass == 0 ? code : code << 16;
+              if (lane == 0) sh.plan[(sw / kChunk) % kNBuf][sw % kChunk].wsave |= 1ull << jj;
+              break;
+            }
+          }
         }
+      }
+      const bool any = __ballot(src != 0u) != 0ull;
+      if (any) {
+        StepPlan<COLS>& p = sh.plan[(u / kChunk) % kNBuf][u % kChunk];
+        p.src[tslot] = src;
+        if (lane == 0) p.sc[kScFwd] = 1u;
       }
       wave_sync();
     }
-#pragma unroll
-    for (int a = D - 1; a > 0; --a) ring.prev[a] = ring.prev[a - 1];
-    ring.prev[0] = wrow;
-    p.wofs[tslot] = wvalid ? (uint32_t)wi[s] * row_bytes : kOffNone;
-    p.rofs[tslot] = rvalid ? (uint32_t)ri[s] * row_bytes : kOffNone;
-    p.wk[tslot] = wkv[s];
-    p.rw[tslot] = rvalid ? rwv[s] : 0.0f;
-    p.wsrc[tslot] = (uint16_t)wsrc;
-    p.rsrc[tslot] = (uint16_t)rsrc;
-    const bool anyfwd = __ballot(wsrc != 0 || rsrc != 0) != 0;
-    if (lane == 0) {
-      p.fwd = anyfwd ? 1u : 0u;
-      p.a = ab[s];
-    }
-    if (lane == 1) p.b = ab[s];
-    if (lane < COLS) p.v[lane] = vv[s];
   }
-}
+};
 
 // ---------------------------------------------------------------- consumer
 
@@ -378,13 +416,13 @@ struct Consumer {
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) vv[e] = p.v[lc * EPL + e];
-    const float a = p.a, b = p.b;
-    const uint32_t fwd = p.fwd;
+    const float a = __uint_as_float(p.sc[kScAlpha]), b = __uint_as_float(p.sc[kScBeta]);
+    const uint32_t fwd = p.sc[kScFwd];
     const uint64_t save = p.wsave;
     if (fwd) {  // rare: take forwarded rows from the ring
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
-        const uint32_t src = p.wsrc[lr * NI + k];
+        const uint32_t src = p.src[lr * NI + k] & 0xFFFFu;
         if (src) wv[SLOT][k] = lds_u4(sh.upd[(src - 1) >> 6][((src - 1) & 63) * LPR + lc]);
       }
     }
@@ -416,7 +454,7 @@ struct Consumer {
     if (fwd) {
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
-        const uint32_t src = p.rsrc[lr * NI + k];
+        const uint32_t src = p.src[lr * NI + k] >> 16;
         if (src) rv[SLOT][k] = lds_u4(sh.upd[(src - 1) >> 6][((src - 1) & 63) * LPR + lc]);
       }
     }
@@ -443,6 +481,37 @@ struct Consumer {
       __syncthreads();
     }
   }
+
+  // Gathers of steps 0 .. D-1.
+  template <int S>
+  __device__ __forceinline__ void prologue(ScanShared<DT, COLS, D>& sh, int lr, int64_t T) {
+    if constexpr (S < D) {
+      issue<S>(sh, lr, S, T);
+      prologue<S + 1>(sh, lr, T);
+    }
+  }
+
+  // Steps u .. u + D (u a multiple of D + 1, so step u + S uses ring slot S).
+  template <int S>
+  __device__ __forceinline__ void round(ScanShared<DT, COLS, D>& sh, float* out_mem, int d_v,
+                                        int64_t T, int tile, int lr, int lc, int64_t u) {
+    if constexpr (S <= D) {
+      step<S>(sh, out_mem, d_v, T, tile, lr, lc, u + S);
+      round<S + 1>(sh, out_mem, d_v, T, tile, lr, lc, u);
+    }
+  }
+
+  // The last steps (fewer than D + 1) from u on.
+  template <int S>
+  __device__ __forceinline__ void tail(ScanShared<DT, COLS, D>& sh, float* out_mem, int d_v,
+                                       int64_t T, int tile, int lr, int lc, int64_t u) {
+    if constexpr (S < D) {
+      if (u + S < T) {
+        step<S>(sh, out_mem, d_v, T, tile, lr, lc, u + S);
+        tail<S + 1>(sh, out_mem, d_v, T, tile, lr, lc, u);
+      }
+    }
+  }
 };
 
 template <typename DT, int COLS, int D>
@@ -464,16 +533,26 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   const int64_t nchunks = (T + kChunk - 1) / kChunk;
 
   if (wave == 1) {
-    // producer
-    ProducerRing<D> ring;
-#pragma unroll
-    for (int a = 0; a < D; ++a) ring.prev[a] = -1;
-    produce_chunk<DT, COLS, D>(sh, ring, A, mem, tile, 0);
-    produce_chunk<DT, COLS, D>(sh, ring, A, mem, tile, 1);
+    // producer: chunks 0 and 1 before the consumer starts, then chunk c + 2
+    // while the consumer runs chunk c; the metadata of the next chunk is in
+    // flight while one is processed (two register sets, loop unrolled by 2)
+    Producer<DT, COLS, D> pr;
+    ChunkMeta ma, mb;
+    pr.load(ma, A, mem, tile, 0);
+    pr.load(mb, A, mem, tile, 1);
+    pr.produce(sh, ma, A, 0);
+    pr.load(ma, A, mem, tile, 2);
+    pr.produce(sh, mb, A, 1);
     __syncthreads();
-    for (int64_t c = 0; c < nchunks; ++c) {
-      produce_chunk<DT, COLS, D>(sh, ring, A, mem, tile, c + 2);
+    for (int64_t c = 0; c < nchunks; c += 2) {
+      pr.load(mb, A, mem, tile, c + 3);
+      pr.produce(sh, ma, A, c + 2);
       __syncthreads();
+      if (c + 1 < nchunks) {
+        pr.load(ma, A, mem, tile, c + 4);
+        pr.produce(sh, mb, A, c + 3);
+        __syncthreads();
+      }
     }
     return;
   }
@@ -491,29 +570,17 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
       (int)(A.N * d_v * (int64_t)sizeof(DT) - (int64_t)tile * COLS * (int64_t)sizeof(DT)),
       kBufWord3);
   __syncthreads();
-  // prologue: gathers of steps 0 .. D-1
-  cs.template issue<0>(sh, lr, 0, T);
-  if constexpr (D >= 2) cs.template issue<1>(sh, lr, 1, T);
-  if constexpr (D >= 3) cs.template issue<2>(sh, lr, 2, T);
+  cs.template prologue<0>(sh, lr, T);
   int64_t u = 0;
-  for (; u + D + 1 <= T; u += D + 1) {
-    cs.template step<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
-    cs.template step<1 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 1);
-    if constexpr (D >= 2) cs.template step<2 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 2);
-    if constexpr (D >= 3) cs.template step<3 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 3);
-  }
-  // tail: fewer than D + 1 steps
-  if (u < T) cs.template step<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
-  if (u + 1 < T) cs.template step<1 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 1);
-  if constexpr (D >= 3) {
-    if (u + 2 < T) cs.template step<2 % (D + 1)>(sh, out_mem, d_v, T, tile, lr, lc, u + 2);
-  }
+  for (; u + D + 1 <= T; u += D + 1) cs.template round<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
+  cs.template tail<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
 }
 
-template <typename DT, int COLS>
-hipError_t launch(void* M, const ScanArgs& A, hipStream_t stream) {
-  constexpr int D = 2;
-  static_assert(D >= 1 && D <= 3 && D <= kChunk, "prefetch depth");
+template <typename DT, int COLS, int D>
+hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
+  static_assert(D >= 1 && D <= kChunk, "prefetch depth");
+  static_assert(3 * Tile<DT, COLS>::NI * D <= 63, "outstanding vector memory operations");
+  A.ntiles = A.d_v / COLS;
   const int groups = (A.n_mem + 7) / 8;
   const int64_t blocks = (int64_t)groups * A.ntiles * 8;
   hipLaunchKernelGGL((scan_kernel<DT, COLS, D>), dim3((unsigned)blocks), dim3(2 * kWave), 0,
@@ -528,16 +595,16 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
                        const float* rw, const float* v, const float* alpha, const float* beta,
                        float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0};
-  // tile = 32 columns of a row (the whole row when it is shorter)
-  const int cols = d_v < 32 ? d_v : 32;
-  A.ntiles = d_v / cols;
+  const ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0};
+  // Tiles of 32 columns (16 when d_v = 16) and one step of gathers in flight:
+  // measured fastest for both state types on the mid and long-stream
+  // workloads (deeper prefetch and narrower tiles were slower).
   if (dtype == 0) {
-    if (d_v == 16) return launch<float, 16>(M, A, stream);
-    return launch<float, 32>(M, A, stream);
+    if (d_v == 16) return launch<float, 16, 1>(M, A, stream);
+    return launch<float, 32, 1>(M, A, stream);
   }
-  if (d_v == 16) return launch<uint16_t, 16>(M, A, stream);
-  return launch<uint16_t, 32>(M, A, stream);
+  if (d_v == 16) return launch<uint16_t, 16, 1>(M, A, stream);
+  return launch<uint16_t, 32, 1>(M, A, stream);
 }
 
 }  // namespace sdm

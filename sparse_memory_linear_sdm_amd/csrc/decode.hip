@@ -1,10 +1,13 @@
-// Fused single-token step: for one (b,h) per 256-thread block, wave 0 forms
-// the write selection from (s1, s2), wave 1 the read selection from (q1, q2)
-// (product-key top-K, page "Riepilogo Tecnico: Sparse Delta Memory (SDM)",
-// "Meccanismo Core" item 2), the other waves stage v; then the whole block
-// applies the gated delta write to the W rows (item 3), and after a block
-// barrier (which makes the block's stores visible to its own loads) reads
-// the R rows and forms o = sum_j r_j M[g_j] (item 4).
+// Fused single-token step for one (b,h) per 256-thread block (page "Riepilogo
+// Tecnico: Sparse Delta Memory (SDM)", "Meccanismo Core" items 2-4):
+//   1. each of the four waves runs stage 1 of one half (s1, s2, q1, q2) of the
+//      product-key top-K; waves 0 and 1 then finish the write and the read
+//      selection (item 2);
+//   2. the whole block applies the gated delta write to the W rows (item 3);
+//   3. after a block barrier (which makes the block's stores visible to its
+//      own loads) it reads the R rows and forms o = sum_j r_j M[g_j] (item 4).
+// In 2 and 3 every thread issues all of its row loads before using any of
+// them; an invalid row loads row 0 (always inside the table) and is masked.
 #include "internal.h"
 #include "select_wave.h"
 
@@ -12,6 +15,37 @@ namespace sdm {
 namespace {
 
 constexpr int kDecThreads = 256;
+
+template <bool BF16>
+__device__ __forceinline__ void unpack16(const uint4& q, float (&m)[BF16 ? 8 : 4]) {
+  if constexpr (BF16) {
+    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = __uint_as_float(wq[i] << 16);
+      m[2 * i + 1] = __uint_as_float(wq[i] & 0xFFFF0000u);
+    }
+  } else {
+    m[0] = __uint_as_float(q.x);
+    m[1] = __uint_as_float(q.y);
+    m[2] = __uint_as_float(q.z);
+    m[3] = __uint_as_float(q.w);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint4 pack16(const float (&m)[BF16 ? 8 : 4]) {
+  if constexpr (BF16) {
+    uint32_t wq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wq[i] = (uint32_t)f32_to_bf16_rne(m[2 * i]) | ((uint32_t)f32_to_bf16_rne(m[2 * i + 1]) << 16);
+    return make_uint4(wq[0], wq[1], wq[2], wq[3]);
+  } else {
+    return make_uint4(__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]),
+                      __float_as_uint(m[3]));
+  }
+}
 
 template <int P, bool BF16>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
@@ -21,6 +55,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     float* __restrict__ out, int32_t* __restrict__ widx_out, int32_t* __restrict__ ridx_out) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPL = 16 / ES;
+  constexpr int kU = BF16 ? 4 : 8;  // 16-byte chunks per thread in flight (one batch at d_v = 128)
   __shared__ SelectLds sl[2];
   __shared__ int32_t s_widx[64], s_ridx[64];
   __shared__ float s_wk[64], s_rw[64];
@@ -30,16 +65,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   const int mem = blockIdx.x;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
-  if (w == 0) {
-    select_unit<P>(s1 + (int64_t)mem * n, s2 + (int64_t)mem * n, n, W, sl[0], s_widx, nullptr,
-                   s_wk);
-  } else if (w == 1) {
-    select_unit<P>(q1 + (int64_t)mem * n, q2 + (int64_t)mem * n, n, R, sl[1], s_ridx, nullptr,
-                   s_rw);
-  } else {
-    for (int c = tid - 2 * kWave; c < d_v; c += kDecThreads - 2 * kWave)
-      s_v[c] = v[(int64_t)mem * d_v + c];
+
+  // 1. selections: wave w runs stage 1 of half w into the LDS of its selection
+  uint32_t rc[pairtab::kSlots];
+  if (w < 2) pair_slots(w == 0 ? W : R, rc);
+  {
+    const float* x = w == 0 ? s1 : w == 1 ? s2 : w == 2 ? q1 : q2;
+    SelectLds& S = sl[w >> 1];
+    stage1_half<P>(x + (int64_t)mem * n, n, w < 2 ? W : R, (w & 1) ? S.s1.bkey : S.s1.akey,
+                   (w & 1) ? S.s1.bidx : S.s1.aidx);
   }
+  for (int c = tid; c < d_v; c += kDecThreads) s_v[c] = v[(int64_t)mem * d_v + c];
+  __syncthreads();
+  if (w == 0) select_finish(n, W, sl[0], rc, s_widx, nullptr, s_wk);
+  else if (w == 1) select_finish(n, R, sl[1], rc, s_ridx, nullptr, s_rw);
   __syncthreads();
   if (widx_out && tid < W) widx_out[(int64_t)mem * W + tid] = s_widx[tid];
   if (ridx_out && tid < R) ridx_out[(int64_t)mem * R + tid] = s_ridx[tid];
@@ -49,76 +88,68 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   char* const Mb = reinterpret_cast<char*>(Mv) + (int64_t)mem * N * d_v * ES;
   const float a = alpha[mem], b = beta[mem];
 
-  // gated delta write of the W rows
-  for (int c = tid; c < W * CPR; c += kDecThreads) {
-    const int j = c / CPR, p = c - j * CPR;
-    const int32_t row = s_widx[j];
-    if ((uint32_t)row >= Nu) continue;
-    uint4* ptr = reinterpret_cast<uint4*>(Mb + ((int64_t)row * d_v + p * EPL) * ES);
-    uint4 q = *ptr;
-    const float g = b * s_wk[j];
-    float m[EPL];
-    if constexpr (BF16) {
-      const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+  // 2. gated delta write of the W rows
+  const int nch = W * CPR;
+  for (int c0 = 0; c0 < nch; c0 += kDecThreads * kU) {
+    uint4 q[kU];
+    int64_t off[kU];
+    int jj[kU], pp[kU];
+    bool ok[kU];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m[2 * i] = __uint_as_float(wq[i] << 16);
-        m[2 * i + 1] = __uint_as_float(wq[i] & 0xFFFF0000u);
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * kDecThreads + tid;
+      const int j = c / CPR;
+      pp[u] = c - j * CPR;
+      jj[u] = c < nch ? j : 0;
+      const int32_t row = c < nch ? s_widx[j] : -1;
+      ok[u] = (uint32_t)row < Nu;
+      off[u] = ((int64_t)(ok[u] ? row : 0) * d_v + pp[u] * EPL) * ES;
+      q[u] = *reinterpret_cast<const uint4*>(Mb + off[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (!ok[u]) continue;
+      float m[EPL];
+      unpack16<BF16>(q[u], m);
+      const float g = b * s_wk[jj[u]];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float mt = a * m[e];
+        m[e] = fmaf(g, s_v[pp[u] * EPL + e] - mt, mt);
       }
-    } else {
-      m[0] = __uint_as_float(q.x);
-      m[1] = __uint_as_float(q.y);
-      m[2] = __uint_as_float(q.z);
-      m[3] = __uint_as_float(q.w);
+      *reinterpret_cast<uint4*>(Mb + off[u]) = pack16<BF16>(m);
     }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float mt = a * m[e];
-      m[e] = fmaf(g, s_v[p * EPL + e] - mt, mt);
-    }
-    if constexpr (BF16) {
-      uint32_t wq[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wq[i] = (uint32_t)f32_to_bf16_rne(m[2 * i]) | ((uint32_t)f32_to_bf16_rne(m[2 * i + 1]) << 16);
-      q = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-    } else {
-      q = make_uint4(__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]),
-                     __float_as_uint(m[3]));
-    }
-    *ptr = q;
   }
   __syncthreads();
 
-  // sparse read of the R rows after the write
+  // 3. sparse read of the R rows after the write
   const int RG = kDecThreads / CPR;  // row groups
   const int p = tid % CPR, rg = tid / CPR;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  if (rg < RG) {
-    for (int j = rg; j < R; j += RG) {
-      const int32_t row = s_ridx[j];
-      if ((uint32_t)row >= Nu) continue;
-      const uint4 q = *reinterpret_cast<const uint4*>(Mb + ((int64_t)row * d_v + p * EPL) * ES);
-      const float r = s_rw[j];
-      if constexpr (BF16) {
-        const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+  for (int j0 = rg; j0 < R; j0 += RG * kU) {
+    uint4 q[kU];
+    float r[kU];
+    bool ok[kU];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(r, __uint_as_float(wq[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(r, __uint_as_float(wq[i] & 0xFFFF0000u), acc[2 * i + 1]);
-        }
-      } else {
-        acc[0] = fmaf(r, __uint_as_float(q.x), acc[0]);
-        acc[1] = fmaf(r, __uint_as_float(q.y), acc[1]);
-        acc[2] = fmaf(r, __uint_as_float(q.z), acc[2]);
-        acc[3] = fmaf(r, __uint_as_float(q.w), acc[3]);
-      }
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u * RG;
+      const int32_t row = j < R ? s_ridx[j] : -1;
+      ok[u] = (uint32_t)row < Nu;
+      r[u] = ok[u] ? s_rw[j] : 0.0f;
+      q[u] = *reinterpret_cast<const uint4*>(Mb + ((int64_t)(ok[u] ? row : 0) * d_v + p * EPL) * ES);
     }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_red[rg * d_v + p * EPL + e] = acc[e];
+    for (int u = 0; u < kU; ++u) {
+      float m[EPL];
+      unpack16<BF16>(q[u], m);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = ok[u] ? fmaf(r[u], m[e], acc[e]) : acc[e];
+    }
   }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_red[rg * d_v + p * EPL + e] = acc[e];
   __syncthreads();
   for (int c = tid; c < d_v; c += kDecThreads) {
     float sum = 0.0f;

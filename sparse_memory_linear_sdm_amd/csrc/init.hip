@@ -61,7 +61,8 @@ hipError_t launch_state_init(void* M, int dtype, const float* M0, int B, int H, 
   const int64_t per4 = N * d_v / 4;
   const int64_t total = (int64_t)H * per4 / (dtype == 1 ? 2 : 1);
   int64_t blocks = (total + 256 * kU - 1) / (256 * kU);
-  if (blocks > 256 * 8) blocks = 256 * 8;  // 8 blocks per CU: measured best for this copy
+  if (blocks > 256 * 4) blocks = 256 * 4;  // 4 blocks per CU: fastest alone, and leaves wave slots for
+                                          // the selections that run beside it
   if (dtype == 1)
     hipLaunchKernelGGL(init_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
                        reinterpret_cast<const f32x4*>(M0), B, H, per4);

@@ -215,33 +215,36 @@ __device__ __forceinline__ int prefix_end(float a, const uint64_t* b, int l, int
   return l;
 }
 
-// Full selection of one unit.  x1, x2 point at this unit's n values.
-// Writes K outputs per unit (lanes j < K write slot j).
-template <int P>
-__device__ void select_unit(const float* __restrict__ x1, const float* __restrict__ x2, int n,
-                            int K, SelectLds& s, int32_t* __restrict__ idx_out,
-                            float* __restrict__ score_out, float* __restrict__ weight_out) {
-  constexpr int S = pairtab::kSlots;
+// Entries of the pair list P+ of this K held by this lane (issued early so
+// that their latency hides under stage 1).
+__device__ __forceinline__ void pair_slots(int K, uint32_t (&rc)[pairtab::kSlots]) {
   const int lane = lane_id();
-
-  // The pair list of this K, fetched first so that its latency hides under
-  // stage 1.
   const int plen = kPairTab.len[K];
   const uint16_t* prc = kPairTab.rc + kPairTab.start[K];
-  uint32_t rc[S];
 #pragma unroll
-  for (int p = 0; p < S; ++p) {
+  for (int p = 0; p < pairtab::kSlots; ++p) {
     const int q = p * 64 + lane;
     rc[p] = q < plen ? prc[q] : 0xFFFFu;
   }
+}
 
-  // ---- stage 1, both halves
+// Stage 1 of one half, from its n values in memory to its K survivors in LDS.
+template <int P>
+__device__ __forceinline__ void stage1_half(const float* __restrict__ x, int n, int K,
+                                            uint32_t* out_key, int32_t* out_idx) {
   uint32_t u[P];
-  load_keys<P>(x1, n, lane, u);
-  stage1<P>(u, n, K, lane, s.s1.akey, s.s1.aidx);
-  load_keys<P>(x2, n, lane, u);
-  stage1<P>(u, n, K, lane, s.s1.bkey, s.s1.bidx);
-  wave_sync();
+  load_keys<P>(x, n, lane_id(), u);
+  stage1<P>(u, n, K, lane_id(), out_key, out_idx);
+}
+
+// Everything after stage 1: both halves' survivors are in s.s1 (written by
+// this wave, or by others before a barrier).  Writes K outputs per unit
+// (lanes j < K write slot j).
+__device__ inline void select_finish(int n, int K, SelectLds& s, const uint32_t (&rc)[pairtab::kSlots],
+                              int32_t* __restrict__ idx_out, float* __restrict__ score_out,
+                              float* __restrict__ weight_out) {
+  constexpr int S = pairtab::kSlots;
+  const int lane = lane_id();
 
   // ---- sort both survivor lists by (key desc, index asc)
   uint64_t ka = 0, kb = 0;
@@ -349,6 +352,20 @@ __device__ void select_unit(const float* __restrict__ x1, const float* __restric
     weight_out[lane] = e / z;
   }
   wave_sync();
+}
+
+// Full selection of one unit by one wave.  x1, x2 point at this unit's n
+// values.
+template <int P>
+__device__ void select_unit(const float* __restrict__ x1, const float* __restrict__ x2, int n,
+                            int K, SelectLds& s, int32_t* __restrict__ idx_out,
+                            float* __restrict__ score_out, float* __restrict__ weight_out) {
+  uint32_t rc[pairtab::kSlots];
+  pair_slots(K, rc);
+  stage1_half<P>(x1, n, K, s.s1.akey, s.s1.aidx);
+  stage1_half<P>(x2, n, K, s.s1.bkey, s.s1.bidx);
+  wave_sync();
+  select_finish(n, K, s, rc, idx_out, score_out, weight_out);
 }
 
 }  // namespace sdm

@@ -213,7 +213,7 @@ def run_prefill(cfg, args, torch, S, sdm):
     tokens_per_step = B * T
     slot_bytes = B * H * T * (2 * W + R) * d_v * es  # algorithmic, one scan launch
     scan_gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
-    kname = "scan_kernel<float,32,2>" if es == 4 else "scan_kernel<bf16,64,2>"
+    kname = "scan_kernel<float,32,1>" if es == 4 else "scan_kernel<uint16_t(bf16),32,1>"
     traffic = measured_traffic(slot_bytes) if (cfg.name == "mid" and es == 4) else None
     workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
                 f"{args.state} state")
@@ -358,7 +358,7 @@ def run_long(cfg, args, torch, S, sdm):
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": "scan_kernel<float,32,2>", "algorithmic_bytes_per_launch":
+                "kernel": "scan_kernel<float,32,1>", "algorithmic_bytes_per_launch":
                 slot_bytes // (T // C)}
     extra = {"breakdown_ms": {"select_write_read": sel_ms, "scan": scan_ms},
              "wall_s": wall, "cpu_baseline": None}

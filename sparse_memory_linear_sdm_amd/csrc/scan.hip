@@ -188,34 +188,32 @@ template <typename DT, int COLS, int D>
 struct Producer {
   using TL = Tile<DT, COLS>;
 
-  // Issue the loads of chunk c (nothing past the end); no wait here.
+  // Issue the loads of chunk c; no wait here.  Branch-free: every address is
+  // clamped into its array (steps past the end read the chunk's last step,
+  // lanes past W, R or COLS read lane 0), and produce() masks those entries by
+  // step and lane.  A chunk wholly past the end loads nothing.
   __device__ __forceinline__ void load(ChunkMeta& m, const ScanArgs& A, int mem, int tile,
                                        int64_t c) const {
-    const int lane = lane_id();
     const int64_t t0 = c * kChunk;
+    if (t0 >= A.T) return;  // never read: produce() returns before using m
+    const int lane = lane_id();
+    const int last = (int)((A.T - t0) < kChunk ? (A.T - t0) : kChunk) - 1;
     const int64_t base = (int64_t)mem * A.T + t0;
+    const int32_t* const pwi = A.widx + base * A.W + (lane < A.W ? lane : 0);
+    const float* const pwk = A.wk + base * A.W + (lane < A.W ? lane : 0);
+    const int32_t* const pri = A.ridx + base * A.R + (lane < A.R ? lane : 0);
+    const float* const prw = A.rw + base * A.R + (lane < A.R ? lane : 0);
+    const float* const pv = A.v + base * A.d_v + (int64_t)tile * COLS + (lane < COLS ? lane : 0);
+    const float* const pab = (lane == 1 ? A.beta : A.alpha) + base;
 #pragma unroll
     for (int s = 0; s < kChunk; ++s) {
-      m.wi[s] = -1;
-      m.ri[s] = -1;
-      m.wk[s] = 0.f;
-      m.rw[s] = 0.f;
-      m.v[s] = 0.f;
-      m.ab[s] = 0.f;
-      if (t0 + s < A.T) {
-        const int64_t t = base + s;
-        if (lane < A.W) {
-          m.wi[s] = A.widx[t * A.W + lane];
-          m.wk[s] = A.wk[t * A.W + lane];
-        }
-        if (lane < A.R) {
-          m.ri[s] = A.ridx[t * A.R + lane];
-          m.rw[s] = A.rw[t * A.R + lane];
-        }
-        if (lane < COLS) m.v[s] = A.v[t * A.d_v + (int64_t)tile * COLS + lane];
-        if (lane == 0) m.ab[s] = A.alpha[t];
-        if (lane == 1) m.ab[s] = A.beta[t];
-      }
+      const int ss = s < last ? s : last;
+      m.wi[s] = pwi[ss * A.W];
+      m.wk[s] = pwk[ss * A.W];
+      m.ri[s] = pri[ss * A.R];
+      m.rw[s] = prw[ss * A.R];
+      m.v[s] = pv[(int64_t)ss * A.d_v];
+      m.ab[s] = pab[ss];
     }
   }
 

@@ -358,7 +358,7 @@ def run_long(cfg, args, torch, S, sdm):
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": "scan_kernel<float,32,1>", "algorithmic_bytes_per_launch":
+                "kernel": "scan_kernel<float,16,2>", "algorithmic_bytes_per_launch":
                 slot_bytes // (T // C)}
     extra = {"breakdown_ms": {"select_write_read": sel_ms, "scan": scan_ms},
              "wall_s": wall, "cpu_baseline": None}

@@ -586,6 +586,20 @@ hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W,
@@ -594,14 +608,19 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
                        float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0};
-  // Tiles of 32 columns (16 when d_v = 16) and one step of gathers in flight:
-  // measured fastest for both state types on the mid and long-stream
-  // workloads (deeper prefetch and narrower tiles were slower).
+  // Tile width and prefetch depth, measured on the mid (64 memories) and
+  // long-stream (16 memories) workloads.  Each workgroup walks its steps at a
+  // rate set by the latency of a step's gathers, so with few memories the
+  // chip is filled by splitting rows into more, narrower tiles (16 columns),
+  // whose fewer memory instructions per step leave room for a deeper
+  // prefetch.  When 16-column tiles would need more workgroups than there
+  // are compute units, 32-column tiles with one step in flight are fastest.
+  const bool narrow = d_v >= 32 && (int64_t)A.n_mem * (d_v / 16) <= compute_units();
   if (dtype == 0) {
-    if (d_v == 16) return launch<float, 16, 1>(M, A, stream);
+    if (d_v == 16 || narrow) return launch<float, 16, 2>(M, A, stream);
     return launch<float, 32, 1>(M, A, stream);
   }
-  if (d_v == 16) return launch<uint16_t, 16, 1>(M, A, stream);
+  if (d_v == 16 || narrow) return launch<uint16_t, 16, 3>(M, A, stream);
   return launch<uint16_t, 32, 1>(M, A, stream);
 }
 

@@ -306,12 +306,16 @@ def run_decode(cfg, args, torch, S, sdm):
 
 
 def run_long(cfg, args, torch, S, sdm):
-    """One step = the whole T = 2^20 stream in chunks of 16384 steps (inputs of
-    each chunk generated on the GPU before it; only the selections and the
-    scan are timed, with HIP events)."""
+    """One step = the whole T = 2^20 stream in chunks of 16384 steps.  The
+    inputs of each chunk are generated on the GPU outside the timed spans.
+    Timed: the selections of chunk 0, then per chunk c one span holding the
+    scan of chunk c on the main stream and, beside it on a second stream,
+    the selections of chunk c + 1 (the scan's workgroups leave compute units
+    free).  --no-overlap times selections and scan of each chunk in turn."""
     dev = torch.device("cuda:0")
     B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
     C = 16384
+    nch = T // C
     f32 = torch.float32
     print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} T{T} in chunks of {C}",
           file=sys.stderr, flush=True)
@@ -319,49 +323,94 @@ def run_long(cfg, args, torch, S, sdm):
     S.device_block(cfg, "M0", M0)
     M = sdm.state_init(M0, B)
     del M0
-    inp = {}
-    for k in ("s1", "s2", "q1", "q2"):
-        inp[k] = torch.empty((B, H, C, n), dtype=f32, device=dev)
-    inp["v"] = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
-    inp["alpha"] = torch.empty((B, H, C), dtype=f32, device=dev)
-    inp["beta"] = torch.empty((B, H, C), dtype=f32, device=dev)
-    widx = torch.empty((B, H, C, W), dtype=torch.int32, device=dev)
-    wk = torch.empty((B, H, C, W), dtype=f32, device=dev)
-    ridx = torch.empty((B, H, C, R), dtype=torch.int32, device=dev)
-    rw = torch.empty((B, H, C, R), dtype=f32, device=dev)
+    nbuf = 1 if args.no_overlap else 2
+    inp, sel = [], []
+    for _ in range(nbuf):
+        d = {k: torch.empty((B, H, C, n), dtype=f32, device=dev) for k in ("s1", "s2", "q1", "q2")}
+        d["v"] = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
+        d["alpha"] = torch.empty((B, H, C), dtype=f32, device=dev)
+        d["beta"] = torch.empty((B, H, C), dtype=f32, device=dev)
+        inp.append(d)
+        sel.append((torch.empty((B, H, C, W), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, C, W), dtype=f32, device=dev),
+                    torch.empty((B, H, C, R), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, C, R), dtype=f32, device=dev)))
     out = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    sel_ms = scan_ms = 0.0
+
+    def generate(c):
+        for k, t in inp[c % nbuf].items():
+            S.device_block(cfg, k, t, 0, 0, c * C)
+
+    def select(c, s):
+        x, (wi, wkk, ri, rww) = inp[c % nbuf], sel[c % nbuf]
+        sdm.select(x["s1"], x["s2"], W, out=(wi, None, wkk), stream=s)
+        sdm.select(x["q1"], x["q2"], R, out=(ri, None, rww), stream=s)
+
+    def scan(c):
+        x, (wi, wkk, ri, rww) = inp[c % nbuf], sel[c % nbuf]
+        sdm.scan(M, wi, wkk, ri, rww, x["v"], x["alpha"], x["beta"], out=out, stream=stream)
+
+    def timed(fn):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        fn(e0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    sel_ms = scan_ms = span_ms = 0.0
     steps = max(1, args.steps)
     t0w = time.perf_counter()
     for rep in range(steps):
-        for c in range(T // C):
-            for k, t in inp.items():
-                S.device_block(cfg, k, t, 0, 0, c * C)
-            e = [ev() for _ in range(3)]
-            e[0].record(stream)
-            sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk))
-            sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw))
-            e[1].record(stream)
-            sdm.scan(M, widx, wk, ridx, rw, inp["v"], inp["alpha"], inp["beta"], out=out)
-            e[2].record(stream)
+        if args.no_overlap:
+            for c in range(nch):
+                generate(c)
+                torch.cuda.synchronize()
+                sel_ms += timed(lambda e0, c=c: select(c, stream))
+                scan_ms += timed(lambda e0, c=c: scan(c))
+        else:
+            generate(0)
             torch.cuda.synchronize()
-            sel_ms += e[0].elapsed_time(e[1])
-            scan_ms += e[1].elapsed_time(e[2])
+            sel_ms += timed(lambda e0: select(0, stream))
+            for c in range(nch):
+                if c + 1 < nch:
+                    generate(c + 1)  # the buffers of chunk c - 1, whose scan has finished
+                    torch.cuda.synchronize()
+
+                es = [ev(), ev()]
+
+                def body(e0, c=c, es=es):
+                    if c + 1 < nch:
+                        side.wait_event(e0)
+                        select(c + 1, side)
+                        e_side = torch.cuda.Event()
+                        e_side.record(side)
+                    es[0].record(stream)
+                    scan(c)
+                    es[1].record(stream)
+                    if c + 1 < nch:
+                        stream.wait_event(e_side)
+                span_ms += timed(body)
+                scan_ms += es[0].elapsed_time(es[1])  # the scan kernel alone, on its stream
     wall = time.perf_counter() - t0w
     sel_ms /= steps
     scan_ms /= steps
-    ms_step = sel_ms + scan_ms
+    span_ms /= steps
+    ms_step = sel_ms + scan_ms if args.no_overlap else sel_ms + span_ms
     slot_bytes = B * H * T * (2 * W + R) * d_v * 4
     gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
                 "kernel": "scan_kernel<float,16,2>", "algorithmic_bytes_per_launch":
-                slot_bytes // (T // C)}
-    extra = {"breakdown_ms": {"select_write_read": sel_ms, "scan": scan_ms},
-             "wall_s": wall, "cpu_baseline": None}
+                slot_bytes // nch}
+    bd = ({"select_write_read": sel_ms, "scan": scan_ms} if args.no_overlap else
+          {"select_chunk0": sel_ms, "spans": span_ms, "scan": scan_ms,
+           "overlap": "selections of chunk c+1 || scan of chunk c"})
+    extra = {"breakdown_ms": bd, "wall_s": wall, "cpu_baseline": None}
     return _common_record(cfg, args, B * T / (ms_step * 1e-3), "tokens/s", ms_step, "f32",
                           workload, roofline, extra)
 

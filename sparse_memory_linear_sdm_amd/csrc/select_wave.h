@@ -124,10 +124,18 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ x, int n, in
 // >= 1, so slots holding 0 never count.
 template <int P>
 __device__ __forceinline__ int count_ge(const uint32_t (&u)[P], uint32_t t) {
+  // one vector compare per key into a scalar mask, four masks live at a time
+  // (independent scalar registers), popcounts and adds on the scalar unit
   int c = 0;
 #pragma unroll
-  for (int p = 0; p < P; ++p) c += u[p] >= t ? 1 : 0;
-  return wave_sum_i32(c);
+  for (int p = 0; p < P; p += 4) {
+    uint64_t b[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (p + q < P) b[q] = __ballot(u[p + q] >= t);
+    c += (__popcll(b[0]) + __popcll(b[1])) + (__popcll(b[2]) + __popcll(b[3]));
+  }
+  return c;
 }
 
 // Bisection for the K-th largest of the wave's keys, from lo with

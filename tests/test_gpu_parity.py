@@ -154,6 +154,16 @@ def test_scan_shapes(d_v, dtype):
     _full_parity(cfg, dtype)
 
 
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_scan_wide_tiles(dtype):
+    # 96 memories x d_v 64: too many for 16-column tiles on one pass of the
+    # chip, so the scan takes 32-column tiles with one step in flight (the
+    # mid workload's configuration), here checked element by element.
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=48, n=32, d_v=64, T=45, W=13, R=29,
+                                  state="f32" if dtype == F32 else "bf16", seed=991)
+    _full_parity(cfg, dtype)
+
+
 def test_hazard_same_rows_every_step():
     # Constant sub-scores: every step writes and reads the same slots, so
     # each step's loads depend on the previous step's stores.

@@ -66,6 +66,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   const int tid = threadIdx.x;
   const int w = tid / kWave;
 
+  // the step's v, alpha and beta are loaded first; their latency hides under
+  // the selections
+  const float vreg = tid < d_v ? v[(int64_t)mem * d_v + tid] : 0.0f;
+  const float a = alpha[mem], b = beta[mem];
+
   // 1. selections: wave w runs stage 1 of half w into the LDS of its selection
   uint32_t rc[pairtab::kSlots];
   if (w < 2) pair_slots(w == 0 ? W : R, rc);
@@ -73,9 +78,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const float* x = w == 0 ? s1 : w == 1 ? s2 : w == 2 ? q1 : q2;
     SelectLds& S = sl[w >> 1];
     stage1_half<P>(x + (int64_t)mem * n, n, w < 2 ? W : R, (w & 1) ? S.s1.bkey : S.s1.akey,
-                   (w & 1) ? S.s1.bidx : S.s1.aidx);
+                   (w & 1) ? S.s1.bidx : S.s1.aidx, S.trash);
   }
-  for (int c = tid; c < d_v; c += kDecThreads) s_v[c] = v[(int64_t)mem * d_v + c];
+  if (tid < d_v) s_v[tid] = vreg;
   __syncthreads();
   if (w == 0) select_finish(n, W, sl[0], rc, s_widx, nullptr, s_wk);
   else if (w == 1) select_finish(n, R, sl[1], rc, s_ridx, nullptr, s_rw);
@@ -86,7 +91,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   const int CPR = d_v * ES / 16;  // 16-byte chunks per row
   const uint32_t Nu = (uint32_t)N;
   char* const Mb = reinterpret_cast<char*>(Mv) + (int64_t)mem * N * d_v * ES;
-  const float a = alpha[mem], b = beta[mem];
 
   // 2. gated delta write of the W rows
   const int nch = W * CPR;

@@ -86,6 +86,7 @@ struct SelectLds {
     } sorted;
   };
   uint64_t cand[64];  // the K selected: (key << 32) | ~f
+  uint32_t trash[64];  // per-lane sink of stage 1's branch-free compaction
 };
 
 // Index of register slot p of a lane: groups of 4 consecutive elements per
@@ -161,10 +162,11 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&u)[P], int K, uint6
 }
 
 // Stage 1 for one half: writes the K survivors (key, index) to LDS, in no
-// particular order.
+// particular order.  Every slot is stored; a slot that is not selected goes
+// to the lane's own trash word, so the compaction has no branches.
 template <int P>
 __device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int lane,
-                                       uint32_t* out_key, int32_t* out_idx) {
+                                       uint32_t* out_key, int32_t* out_idx, uint32_t* trash) {
   uint32_t lmax = 0, lmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -201,11 +203,12 @@ __device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int i = elem_index<P>(p, lane);
-    if (u[p] > tau || (u[p] == tau && i < ibound)) {
-      out_key[pos] = u[p];
-      out_idx[pos] = i;
-      ++pos;
-    }
+    const bool sel = u[p] > tau || (u[p] == tau && i < ibound);
+    uint32_t* const kd = sel ? out_key + pos : trash + lane;
+    int32_t* const id = sel ? out_idx + pos : reinterpret_cast<int32_t*>(trash + lane);
+    *kd = u[p];
+    *id = i;
+    pos += sel ? 1 : 0;
   }
 }
 
@@ -239,10 +242,10 @@ __device__ __forceinline__ void pair_slots(int K, uint32_t (&rc)[pairtab::kSlots
 // Stage 1 of one half, from its n values in memory to its K survivors in LDS.
 template <int P>
 __device__ __forceinline__ void stage1_half(const float* __restrict__ x, int n, int K,
-                                            uint32_t* out_key, int32_t* out_idx) {
+                                            uint32_t* out_key, int32_t* out_idx, uint32_t* trash) {
   uint32_t u[P];
   load_keys<P>(x, n, lane_id(), u);
-  stage1<P>(u, n, K, lane_id(), out_key, out_idx);
+  stage1<P>(u, n, K, lane_id(), out_key, out_idx, trash);
 }
 
 // Everything after stage 1: both halves' survivors are in s.s1 (written by
@@ -370,8 +373,8 @@ __device__ void select_unit(const float* __restrict__ x1, const float* __restric
                             float* __restrict__ score_out, float* __restrict__ weight_out) {
   uint32_t rc[pairtab::kSlots];
   pair_slots(K, rc);
-  stage1_half<P>(x1, n, K, s.s1.akey, s.s1.aidx);
-  stage1_half<P>(x2, n, K, s.s1.bkey, s.s1.bidx);
+  stage1_half<P>(x1, n, K, s.s1.akey, s.s1.aidx, s.trash);
+  stage1_half<P>(x2, n, K, s.s1.bkey, s.s1.bidx, s.trash);
   wave_sync();
   select_finish(n, K, s, rc, idx_out, score_out, weight_out);
 }

@@ -267,6 +267,36 @@ def test_step_decode_equals_scan(dtype):
                  "decode vs scan out")
 
 
+@pytest.mark.parametrize("n,W,R", [(64, 16, 64), (256, 64, 37), (1024, 64, 64)])
+def test_step_decode_selection_ties(n, W, R):
+    # The fused decode step runs its own search variant; its write and read
+    # indices must equal the oracle's selection bit for bit on inputs full of
+    # exact ties (small integers) and binary32 rounding ties.
+    import sparse_memory_linear_sdm_amd as sdm
+
+    torch = _torch()
+    rng = np.random.default_rng(n + W + R)
+    B, H, d_v = 3, 4, 32
+    for kind in ("integers", "rounding"):
+        if kind == "integers":
+            x = rng.integers(-2, 3, (4, B, H, n)).astype(np.float32)
+        else:
+            x = np.stack([(2.0 ** 24 + 2.0 * rng.integers(0, 6, (B, H, n))),
+                          rng.uniform(-3, 3, (B, H, n)), (2.0 ** 24 + 2.0 * rng.integers(0, 6, (B, H, n))),
+                          rng.uniform(-0.9, 0.9, (B, H, n))]).astype(np.float32)
+        v = rng.standard_normal((B, H, d_v)).astype(np.float32)
+        a = np.full((B, H), 0.9, np.float32)
+        b = np.full((B, H), 0.5, np.float32)
+        M = torch.zeros((B, H, n * n, d_v), dtype=torch.float32, device="cuda")
+        dev = [torch.from_numpy(t.copy()).cuda() for t in (*x, v, a, b)]
+        _, wi, ri = sdm.step_decode(M, *dev, W, R)
+        torch.cuda.synchronize()
+        ow, _, _ = oracle.select(x[0].reshape(-1, n), x[1].reshape(-1, n), W, threads=8)
+        orr, _, _ = oracle.select(x[2].reshape(-1, n), x[3].reshape(-1, n), R, threads=8)
+        assert np.array_equal(wi.cpu().numpy().reshape(-1, W), ow), f"{kind}: write indices"
+        assert np.array_equal(ri.cpu().numpy().reshape(-1, R), orr), f"{kind}: read indices"
+
+
 def test_step_decode_graph_replays_match_eager():
     # The decode calls of several tokens captured in a HIP graph and replayed
     # three times, with eager work and synchronisations in between; every

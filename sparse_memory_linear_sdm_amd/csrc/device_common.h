@@ -127,12 +127,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return __uint_as_float(uniform_u32(__float_as_uint(v)));
 }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __uint_as_float(lane_xor(__float_as_uint(v), o)));
-  return __uint_as_float(uniform_u32(__float_as_uint(v)));
-}
-
 // Exclusive prefix sum of a per-lane count across the wave: inclusive scans
 // inside each row of 16 by DPP row_shr 1, 2, 4, 8 (lanes shifted in from
 // outside the row read 0), then each row adds the totals of the rows below.
@@ -198,11 +192,7 @@ __device__ __forceinline__ void wave_sort2_desc_u64(uint64_t& x, uint64_t& z) {
   }
 }
 
-// bf16 storage: widening is exact; narrowing rounds to nearest even.
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float((uint32_t)h << 16);
-}
-
+// bf16 storage: narrowing rounds to nearest even (widening is a 16-bit shift).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
   b += 0x7FFFu + ((b >> 16) & 1u);

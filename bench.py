@@ -405,7 +405,8 @@ def run_long(cfg, args, torch, S, sdm):
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": "scan_kernel<float,16,2>", "algorithmic_bytes_per_launch":
+                "kernel": "scan_kernel<float,16,3>, two row shards (duration includes the "
+                          "output zero fill of the same call)", "algorithmic_bytes_per_launch":
                 slot_bytes // nch}
     bd = ({"select_write_read": sel_ms, "scan": scan_ms} if args.no_overlap else
           {"select_chunk0": sel_ms, "spans": span_ms, "scan": scan_ms,

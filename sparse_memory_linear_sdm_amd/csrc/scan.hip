@@ -7,10 +7,13 @@
 // fp32 row = one cache line; 64 bytes of a bf16 row, which keeps the same
 // number of workgroups as fp32 -- measured faster than 128-byte bf16 tiles
 // at half the workgroups); one workgroup owns one (b,h,tile) and walks
-// t = 0..T-1.  Blocks
-// are numbered so that all tiles of one memory land on the same XCD (blocks
-// are dealt to the 8 XCDs round-robin), so a memory's index, weight and value
-// traffic is fetched into one L2.  Nothing here is a dense contraction, so
+// t = 0..T-1.  With few memories (narrow 16-column tiles and still room on
+// the chip) the rows of a memory are further split between two workgroups by
+// a hash of the row index; each adds its part of the read into the zeroed
+// output.  Blocks are numbered so that all tiles and shards of one memory
+// land on the same XCD (blocks are dealt to the 8 XCDs round-robin), so a
+// memory's index, weight and value traffic, and the rows its tiles share,
+// are fetched into one L2.  Nothing here is a dense contraction, so
 // there is no MFMA: the kernel is bound by HBM traffic, (2W + R) tile rows
 // per step per tile, all random accesses of one tile row each.
 //
@@ -127,7 +130,13 @@ struct ScanArgs {
   const float* beta;
   float* out;
   int ntiles;
+  int shards;  // 1, or 2: rows split between two workgroups by row_shard()
 };
+
+// Row sharding (few memories): the workgroups of one (memory, tile) pair
+// split the rows by a hash of the row index, so each row is always handled by
+// the same workgroup and all hazard reasoning stays inside one workgroup.
+__device__ __forceinline__ uint32_t row_shard(uint32_t row) { return (row * 0xC2B2AE35u) >> 31; }
 
 // Write-set filter: a row sets two bits of one 32-bit word of the step's
 // bitmap (word and bit positions from two multiplicative hashes), and a probe
@@ -218,6 +227,12 @@ struct Producer {
   }
 
   // Build the plan of chunk c from its loaded metadata.
+  int shard;  // this workgroup's row shard (0 when the rows are not split)
+
+  __device__ __forceinline__ bool owns(int32_t row, int shards) const {
+    return shards == 1 || row_shard((uint32_t)row) == (uint32_t)shard;
+  }
+
   __device__ __forceinline__ void produce(ScanShared<DT, COLS, D>& sh, const ChunkMeta& m,
                                           const ScanArgs& A, int64_t c) {
     const int lane = lane_id();
@@ -232,8 +247,9 @@ struct Producer {
     RowKey hw[kChunk], hr[kChunk];
 #pragma unroll
     for (int s = 0; s < kChunk; ++s) {
-      const bool wv = s < steps && lane < A.W && (uint32_t)m.wi[s] < Nu;
-      const bool rv = s < steps && lane < A.R && (uint32_t)m.ri[s] < Nu;
+      // rows of another shard are handled like empty slots
+      const bool wv = s < steps && lane < A.W && (uint32_t)m.wi[s] < Nu && owns(m.wi[s], A.shards);
+      const bool rv = s < steps && lane < A.R && (uint32_t)m.ri[s] < Nu && owns(m.ri[s], A.shards);
       wrow[s] = wv ? m.wi[s] : -1;
       rrow[s] = rv ? m.ri[s] : -1;
       hw[s] = row_key((uint32_t)m.wi[s]);
@@ -346,6 +362,7 @@ struct Consumer {
   u32x4v rv[D + 1][NI];
   __amdgpu_buffer_rsrc_t mres;  // this memory's tile column, range = the memory slice
   uint32_t lane_off;             // lc * 16
+  bool accumulate;               // rows split over two workgroups: add into out
 
   __device__ __forceinline__ const StepPlan<COLS>& plan(ScanShared<DT, COLS, D>& sh,
                                                         int64_t u) const {
@@ -375,6 +392,8 @@ struct Consumer {
 
   // Sum the chunk's per-lane partials into out: lane g handles float4 group
   // g of the chunk's kChunk x COLS outputs.
+  // With two row shards each adds its partial sum to the zeroed output; two
+  // additions onto zero give the same bits in either order.
   __device__ __forceinline__ void reduce_chunk(ScanShared<DT, COLS, D>& sh, float* out_mem,
                                                int d_v, int64_t T, int tile, int64_t t0) {
     constexpr int G4 = COLS / 4;
@@ -393,8 +412,17 @@ struct Consumer {
           acc.z += x.z;
           acc.w += x.w;
         }
-        if (t0 + s < T)
-          *reinterpret_cast<float4*>(out_mem + (t0 + s) * d_v + tile * COLS + c4 * 4) = acc;
+        if (t0 + s < T) {
+          float* const o = out_mem + (t0 + s) * d_v + tile * COLS + c4 * 4;
+          if (accumulate) {
+            unsafeAtomicAdd(o + 0, acc.x);
+            unsafeAtomicAdd(o + 1, acc.y);
+            unsafeAtomicAdd(o + 2, acc.z);
+            unsafeAtomicAdd(o + 3, acc.w);
+          } else {
+            *reinterpret_cast<float4*>(o) = acc;
+          }
+        }
       }
     }
   }
@@ -480,11 +508,21 @@ struct Consumer {
     }
   }
 
-  // Gathers of steps 0 .. D-1.
+  // Gathers of steps 0 .. D-1.  Each is followed by NI stores to an offset
+  // past the buffer range (dropped by the hardware), so that the memory
+  // operations enter the loop in the same pattern as a step leaves them (a
+  // step's gathers, then its stores).  The compiler's wait counts at the loop
+  // head are the tighter of the two paths into it; without this they would be
+  // sized for the store-free prologue and wait on the next step's gathers.
   template <int S>
   __device__ __forceinline__ void prologue(ScanShared<DT, COLS, D>& sh, int lr, int64_t T) {
     if constexpr (S < D) {
       issue<S>(sh, lr, S, T);
+      const u32x4v zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < NI; ++k)  // distinct offsets: identical stores would be merged
+        __builtin_amdgcn_raw_buffer_store_b128(zero, mres, kOffNone + (uint32_t)(S * NI + k) * 16u,
+                                               0, 0);
       prologue<S + 1>(sh, lr, T);
     }
   }
@@ -517,12 +555,14 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   using TL = Tile<DT, COLS>;
   __shared__ ScanShared<DT, COLS, D> sh;
 
-  // XCD-aware numbering: bid = ((g * ntiles) + tile) * 8 + x, memory = g*8 + x.
+  // XCD-aware numbering: bid = (((g * shards) + shard) * ntiles + tile) * 8 + x,
+  // memory = g*8 + x, so every tile and shard of a memory shares one XCD's L2.
   const int bid = blockIdx.x;
   const int x = bid & 7;
   const int rest = bid >> 3;
   const int tile = rest % A.ntiles;
-  const int mem = (rest / A.ntiles) * 8 + x;
+  const int shard = (rest / A.ntiles) % A.shards;
+  const int mem = (rest / A.ntiles / A.shards) * 8 + x;
   if (mem >= A.n_mem) return;  // whole workgroup leaves together
 
   const int wave = threadIdx.x / kWave;
@@ -535,6 +575,7 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
     // while the consumer runs chunk c; the metadata of the next chunk is in
     // flight while one is processed (two register sets, loop unrolled by 2)
     Producer<DT, COLS, D> pr;
+    pr.shard = shard;
     ChunkMeta ma, mb;
     pr.load(ma, A, mem, tile, 0);
     pr.load(mb, A, mem, tile, 1);
@@ -563,6 +604,7 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   float* const out_mem = A.out + (int64_t)mem * T * d_v;
   Consumer<DT, COLS, D> cs;
   cs.lane_off = (uint32_t)(lc * 16);
+  cs.accumulate = A.shards > 1;
   cs.mres = __builtin_amdgcn_make_buffer_rsrc(
       Mm + (int64_t)tile * COLS, 0,
       (int)(A.N * d_v * (int64_t)sizeof(DT) - (int64_t)tile * COLS * (int64_t)sizeof(DT)),
@@ -574,13 +616,24 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   cs.template tail<0>(sh, out_mem, d_v, T, tile, lr, lc, u);
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 template <typename DT, int COLS, int D>
 hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
   static_assert(D >= 1 && D <= kChunk, "prefetch depth");
   static_assert(3 * Tile<DT, COLS>::NI * D <= 63, "outstanding vector memory operations");
   A.ntiles = A.d_v / COLS;
   const int groups = (A.n_mem + 7) / 8;
-  const int64_t blocks = (int64_t)groups * A.ntiles * 8;
+  const int64_t blocks = (int64_t)groups * A.shards * A.ntiles * 8;
+  if (A.shards > 1) {  // the shards add into out
+    const int64_t n4 = (int64_t)A.n_mem * A.T * A.d_v / 4;
+    const int64_t zb = (n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream,
+                       reinterpret_cast<float4*>(A.out), n4);
+  }
   hipLaunchKernelGGL((scan_kernel<DT, COLS, D>), dim3((unsigned)blocks), dim3(2 * kWave), 0,
                      stream, reinterpret_cast<DT*>(M), A);
   return hipGetLastError();
@@ -607,7 +660,7 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
                        const float* rw, const float* v, const float* alpha, const float* beta,
                        float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0};
+  ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0, 1};
   // Tile width and prefetch depth, measured on the mid (64 memories) and
   // long-stream (16 memories) workloads.  Each workgroup walks its steps at a
   // rate set by the latency of a step's gathers, so with few memories the
@@ -615,13 +668,21 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
   // whose fewer memory instructions per step leave room for a deeper
   // prefetch.  When 16-column tiles would need more workgroups than there
   // are compute units, 32-column tiles with one step in flight are fastest.
-  const bool narrow = d_v >= 32 && (int64_t)A.n_mem * (d_v / 16) <= compute_units();
+  // With room for twice as many narrow workgroups still, each (memory, tile)
+  // is split into two row shards on two compute units: a step's gathers are
+  // then spread over twice the units, and the tiles of one memory, which
+  // fetch the same rows at about the same time, share them in L2 (long-stream
+  // scan 2.27 -> 2.82 TB/s; three steps in flight are then best for fp32 too).
+  const int cus = compute_units();
+  const bool narrow = d_v == 16 || (int64_t)A.n_mem * (d_v / 16) <= cus;
+  if (narrow && 2 * (int64_t)A.n_mem * (d_v / 16) <= cus) A.shards = 2;
   if (dtype == 0) {
-    if (d_v == 16 || narrow) return launch<float, 16, 2>(M, A, stream);
-    return launch<float, 32, 1>(M, A, stream);
+    if (!narrow) return launch<float, 32, 1>(M, A, stream);
+    if (A.shards == 2) return launch<float, 16, 3>(M, A, stream);
+    return launch<float, 16, 2>(M, A, stream);
   }
-  if (d_v == 16 || narrow) return launch<uint16_t, 16, 3>(M, A, stream);
-  return launch<uint16_t, 32, 1>(M, A, stream);
+  if (!narrow) return launch<uint16_t, 32, 1>(M, A, stream);
+  return launch<uint16_t, 16, 3>(M, A, stream);
 }
 
 }  // namespace sdm

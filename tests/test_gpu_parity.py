@@ -164,6 +164,17 @@ def test_scan_wide_tiles(dtype):
     _full_parity(cfg, dtype)
 
 
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_scan_narrow_tiles_one_shard(dtype):
+    # 20 memories x d_v 128 on 256 compute units: 16-column tiles fit (160
+    # workgroups) but two row shards would not (320), so each (memory, tile)
+    # is one workgroup handling every row.  The smaller configurations run
+    # the two-shard path and the 96-memory case above the wide tiles.
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=10, n=32, d_v=128, T=45, W=13, R=29,
+                                  state="f32" if dtype == F32 else "bf16", seed=992)
+    _full_parity(cfg, dtype)
+
+
 def test_hazard_same_rows_every_step():
     # Constant sub-scores: every step writes and reads the same slots, so
     # each step's loads depend on the previous step's stores.

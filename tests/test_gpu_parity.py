@@ -175,6 +175,66 @@ def test_scan_narrow_tiles_one_shard(dtype):
     _full_parity(cfg, dtype)
 
 
+def _scan_row_shard(N):
+    # The scan's row-shard hash, restated here only to build worst cases for
+    # the two-shard path: row r belongs to shard (r * 0xC2B2AE35 mod 2^32) >> 31.
+    r = np.arange(N, dtype=np.uint64)
+    return ((r * 0xC2B2AE35) & 0xFFFFFFFF) >> 31
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_scan_row_shards_crowded_steps(dtype):
+    # Two memories (so the rows are split between two workgroups), W = R = 64,
+    # and index lists built so that one shard holds anywhere from 0 to all 64
+    # of a step's rows, for writes and reads, in shuffled slot order.  The rows
+    # come from pools of 72 per shard, so nearly every row recurs within the
+    # prefetch window and many are read in the step that writes them.
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(B=1, H=2, n=32, d_v=32, T=70, W=64, R=64,
+                                  state="f32" if dtype == F32 else "bf16", seed=993)
+    H, T, N, d_v = cfg.H, cfg.T, cfg.N, cfg.d_v
+    owner = _scan_row_shard(N)
+    rng = np.random.default_rng(993)
+    pools = [rng.choice(np.flatnonzero(owner == k), 72, replace=False) for k in (0, 1)]
+
+    def lists(pattern, h):
+        idx = np.empty((T, 64), np.int32)
+        for t in range(T):
+            k0 = pattern[(t + 3 * h) % len(pattern)]
+            rows = np.concatenate([rng.choice(pools[0], k0, replace=False),
+                                   rng.choice(pools[1], 64 - k0, replace=False)])
+            idx[t] = rng.permutation(rows)
+        return idx
+
+    widx = np.stack([lists([64, 56, 49, 48, 40, 32, 16, 15, 8, 0], h) for h in range(H)])[None]
+    ridx = np.stack([lists([0, 15, 33, 49, 64, 60, 20, 52, 48, 5], h) for h in range(H)])[None]
+    counts = (owner[widx] == 0).sum(-1)
+    assert counts.max() == 64 and counts.min() == 0  # each shard gets every row of some step
+    wk = rng.uniform(0.0, 0.05, widx.shape).astype(np.float32)
+    rw = rng.uniform(0.0, 0.05, ridx.shape).astype(np.float32)
+    v = rng.standard_normal((1, H, T, d_v)).astype(np.float32)
+    alpha = rng.uniform(0.9, 1.0, (1, H, T)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (1, H, T)).astype(np.float32)
+    M0 = S.host_block(cfg, "M0")
+
+    tdt = torch.float32 if dtype == F32 else torch.bfloat16
+    M = sdm.state_init(torch.from_numpy(M0).cuda(), 1, tdt)
+    out = sdm.scan(M, *(torch.from_numpy(a).cuda() for a in (widx, wk, ridx, rw, v, alpha, beta)))
+    torch.cuda.synchronize()
+    gout = out.cpu().numpy()
+    Mh = state_to_host(M)
+    for h in range(H):
+        Mo = oracle.state_init(M0[h:h + 1], 1, dtype)[0, 0]
+        oo = oracle.scan(Mo, dtype, widx[0, h], wk[0, h], ridx[0, h], rw[0, h], v[0, h],
+                         alpha[0, h], beta[0, h])
+        gm = Mh[0, h] if dtype == F32 else oracle.bf16_bits_to_f32(Mh[0, h])
+        om = Mo if dtype == F32 else oracle.bf16_bits_to_f32(Mo)
+        check_values(gm, om, dtype, f"crowded shards h={h} M")
+        check_values(gout[0, h], oo, dtype, f"crowded shards h={h} out")
+
+
 def test_hazard_same_rows_every_step():
     # Constant sub-scores: every step writes and reads the same slots, so
     # each step's loads depend on the previous step's stores.

@@ -138,16 +138,18 @@ struct ScanArgs {
 // the same workgroup and all hazard reasoning stays inside one workgroup.
 __device__ __forceinline__ uint32_t row_shard(uint32_t row) { return (row * 0xC2B2AE35u) >> 31; }
 
-// Write-set filter: a row sets two bits of one 32-bit word of the step's
+// Write-set filter: a row sets three bits of one 32-bit word of the step's
 // bitmap (word and bit positions from two multiplicative hashes), and a probe
-// is a candidate only when both bits are set.  Set and probe are one LDS
-// operation each, and false candidates are far rarer than with one bit.
+// is a candidate only when all three are set.  Set and probe are one LDS
+// operation each; with ~64 rows per 512-word bitmap a probe of an absent row
+// is a false candidate about once in 10^4 (two bits: once in 10^3).
 struct RowKey {
   uint32_t word, mask;
 };
 __device__ __forceinline__ RowKey row_key(uint32_t row) {
   const uint32_t h1 = row * 2654435761u, h2 = row * 0x85EBCA77u;
-  return RowKey{h1 >> (32 - (kBmBits - 5)), (1u << (h2 >> 27)) | (1u << ((h2 >> 22) & 31u))};
+  return RowKey{h1 >> (32 - (kBmBits - 5)),
+                (1u << (h2 >> 27)) | (1u << ((h2 >> 22) & 31u)) | (1u << ((h2 >> 17) & 31u))};
 }
 
 template <typename DT>
@@ -300,8 +302,7 @@ struct Producer {
         p.rofs[tslot] = rrow[s] >= 0 ? (uint32_t)rrow[s] * row_bytes : kOffNone;
         p.wk[tslot] = m.wk[s];
         p.rw[tslot] = rrow[s] >= 0 ? m.rw[s] : 0.0f;
-        p.src[tslot] = 0u;
-        p.v[lane] = m.v[s];
+        p.v[lane] = m.v[s];  // src is read only when the step is flagged, and then written by resolve()
         p.sc[lane] = lane == kScFwd ? 0u : __float_as_uint(m.ab[s]);
       }
     }
@@ -312,23 +313,35 @@ struct Producer {
     if (__ballot((wcand | rcand) != 0u) != 0ull) resolve(sh, wcand, rcand, t0, steps, slot0, tslot);
   }
 
+  // Steps with candidates only.  For such a step the write rows of its
+  // window (steps u - D .. u) are read from LDS once, all together; each
+  // candidate then takes the newest matching writer with one ballot per
+  // window step.  Every lane writes its src entry of a flagged step.
   __device__ void resolve(ScanShared<DT, COLS, D>& sh, uint32_t wcand, uint32_t rcand,
                           int64_t t0, int steps, int slot0, int tslot) {
     const int lane = lane_id();
+    uint32_t todo = 0;  // bit s: step s has a candidate
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s)
+      todo |= __ballot(((wcand | rcand) >> s) & 1u) != 0ull ? 1u << s : 0u;
 #pragma unroll 1
-    for (int s = 0; s < steps; ++s) {
-      const uint64_t wm = __ballot((wcand >> s) & 1u), rm = __ballot((rcand >> s) & 1u);
-      if ((wm | rm) == 0ull) continue;
+    for (; todo; todo &= todo - 1) {
+      const int s = __ffs(todo) - 1;
+      if (s >= steps) break;
       const int64_t u = t0 + s;
+      int32_t win[D + 1];  // write rows of steps u - a, one per lane
+#pragma unroll
+      for (int a = 0; a <= D; ++a) win[a] = sh.wrows[(slot0 + s - a + kBmSlots) % kBmSlots][lane];
+      const uint64_t wm = __ballot((wcand >> s) & 1u), rm = __ballot((rcand >> s) & 1u);
       uint32_t src = 0;
       for (int pass = 0; pass < 2; ++pass) {  // write rows (a >= 1), then read rows (a >= 0)
-        const int a0 = pass == 0 ? 1 : 0;
         for (uint64_t mk = pass == 0 ? wm : rm; mk; mk &= mk - 1) {
           const int L = __ffsll((unsigned long long)mk) - 1;
           const int32_t row = pass == 0 ? sh.wrows[slot0 + s][L] : sh.rrows[s][L];
-          for (int a = a0; a <= D && u - a >= 0; ++a) {
-            const int sl = (slot0 + s - a + kBmSlots) % kBmSlots;
-            const uint64_t hit = __ballot(sh.wrows[sl][lane] == row);
+#pragma unroll
+          for (int a = 0; a <= D; ++a) {
+            if (a < 1 - pass || u - a < 0) continue;
+            const uint64_t hit = __ballot(win[a] == row);
             if (hit) {
               const int jj = __ffsll((unsigned long long)hit) - 1;
               const int64_t sw = u - a;
@@ -340,14 +353,13 @@ struct Producer {
           }
         }
       }
-      const bool any = __ballot(src != 0u) != 0ull;
-      if (any) {
+      if (__ballot(src != 0u) != 0ull) {
         StepPlan<COLS>& p = sh.plan[(u / kChunk) % kNBuf][u % kChunk];
         p.src[tslot] = src;
         if (lane == 0) p.sc[kScFwd] = 1u;
       }
-      wave_sync();
     }
+    wave_sync();
   }
 };
 

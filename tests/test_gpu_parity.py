@@ -286,12 +286,34 @@ def test_chunked_scan_bitwise_and_deterministic():
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_step_decode_parity(dtype):
+    cfg = S.CONFIGS["decode"].with_(B=3, H=2, n=64, T=12, W=16, R=24,
+                                    state="f32" if dtype == F32 else "bf16")
+    _decode_parity(cfg, dtype)
+
+
+@pytest.mark.parametrize("d_v", [128, 256])
+@pytest.mark.parametrize("overlap", ["all", "part"])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_step_decode_reads_rows_it_writes(dtype, overlap, d_v):
+    # Read sub-scores equal to the write ones ("all": every read row is a row
+    # this step writes) or sharing one half ("part": some are).  With d_v 128
+    # a step's rows fit one batch of loads and the read takes rows written in
+    # the same step from the block's LDS copy; with d_v 256 the write and the
+    # read run one after the other.
+    cfg = S.CONFIGS["decode"].with_(B=2, H=2, n=64, T=6, W=64, R=64, d_v=d_v,
+                                    state="f32" if dtype == F32 else "bf16", seed=405)
+    host = host_inputs(cfg)
+    host["q1"] = host["s1"].copy()
+    if overlap == "all":
+        host["q2"] = host["s2"].copy()
+    _decode_parity(cfg, dtype, host)
+
+
+def _decode_parity(cfg, dtype, host=None):
     torch = _torch()
     import sparse_memory_linear_sdm_amd as sdm
 
-    cfg = S.CONFIGS["decode"].with_(B=3, H=2, n=64, T=12, W=16, R=24,
-                                    state="f32" if dtype == F32 else "bf16")
-    host = host_inputs(cfg)
+    host = host or host_inputs(cfg)
     dev = to_dev(host)
     M0 = S.host_block(cfg, "M0")
     tdt = torch.float32 if dtype == F32 else torch.bfloat16

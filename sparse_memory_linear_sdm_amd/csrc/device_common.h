@@ -49,6 +49,12 @@ __device__ __forceinline__ void wave_sync() {
 //              of lane i | 16}; take the one that is not the lane's own
 //   o = 32     v_permlane32_swap likewise with bit 5.
 // The o argument must fold to a constant at the call site.
+//
+// Two forms of each DPP move: dpp_* (an "old" operand of 0) lets the compiler
+// fold the move into the DPP source of the arithmetic that consumes it (as
+// in the reductions below); dpp_mov<> takes no old operand -- every lane of
+// these permutations has a source lane -- so a plain exchange costs no
+// register initialisation.
 __device__ __forceinline__ uint32_t dpp_qp_xor1(uint32_t v) {
   return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);
 }
@@ -64,17 +70,21 @@ __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
 __device__ __forceinline__ uint32_t dpp_row_ror12(uint32_t v) {
   return __builtin_amdgcn_update_dpp(0u, v, 0x12C, 0xF, 0xF, false);
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
 
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int o) {
   const int lane = lane_id();
   switch (o) {
-    case 1: return dpp_qp_xor1(v);
-    case 2: return dpp_qp_xor2(v);
+    case 1: return dpp_mov<0xB1>(v);
+    case 2: return dpp_mov<0x4E>(v);
     case 4: {
-      uint32_t up = dpp_row_ror12(v), down = dpp_row_ror4(v);
+      uint32_t up = dpp_mov<0x12C>(v), down = dpp_mov<0x124>(v);
       return (lane & 4) ? down : up;
     }
-    case 8: return dpp_row_ror8(v);
+    case 8: return dpp_mov<0x128>(v);
     case 16: {
       auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
       return (lane & 16) ? r[0] : r[1];
@@ -133,10 +143,11 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 __device__ __forceinline__ int wave_excl_scan_i32(int v) {
   const int lane = lane_id();
   uint32_t x = (uint32_t)v;
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);
+  // bound_ctrl: lanes whose source is outside the row read 0
+  x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x111, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x112, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x118, 0xF, 0xF, true);
   const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
   const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
   const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
@@ -157,17 +168,18 @@ __device__ __forceinline__ float lane0_f32(float v) {
 }
 
 // Bitonic sort of one 64-bit key per lane, descending across lanes 0..63.
+// A compare-exchange keeps the partner's key y when (y > x) equals "this lane
+// keeps the larger key"; on y == x either choice leaves the same key.  One
+// 64-bit compare and two selects per key and stage.
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t x) {
   int lane = lane_id();
 #pragma unroll
   for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t y = shfl_xor_u64(x, j);
-      bool lower = (lane & j) == 0;
-      bool desc = (lane & k) == 0 || k == 64;
-      bool keep_max = (lower == desc);
-      x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+      const uint64_t y = shfl_xor_u64(x, j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0 || k == 64);
+      x = ((y > x) == keep_max) ? y : x;
     }
   }
   return x;
@@ -183,11 +195,9 @@ __device__ __forceinline__ void wave_sort2_desc_u64(uint64_t& x, uint64_t& z) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       const uint64_t y = shfl_xor_u64(x, j);
       const uint64_t w = shfl_xor_u64(z, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc = (lane & k) == 0 || k == 64;
-      const bool keep_max = (lower == desc);
-      x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
-      z = keep_max ? (z > w ? z : w) : (z < w ? z : w);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0 || k == 64);
+      x = ((y > x) == keep_max) ? y : x;
+      z = ((w > z) == keep_max) ? w : z;
     }
   }
 }

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   {
     const float* x = w == 0 ? s1 : w == 1 ? s2 : w == 2 ? q1 : q2;
     SelectLds& S = sl[w >> 1];
-    stage1_half<P>(x + (int64_t)mem * n, n, w < 2 ? W : R, (w & 1) ? S.s1.bkey : S.s1.akey,
-                   (w & 1) ? S.s1.bidx : S.s1.aidx, S.trash);
+    stage1_half<P>(x + (int64_t)mem * n, n, w < 2 ? W : R, (w & 1) ? S.sorted.b : S.sorted.a,
+                   S.trash);
   }
   if (tid < d_v) s_v[tid] = vreg;
   __syncthreads();

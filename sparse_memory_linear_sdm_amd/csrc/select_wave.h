@@ -71,22 +71,14 @@ static_assert(list_len(kMaxK) <= kSlots * 64, "slot count");
 static __constant__ const pairtab::Table kPairTab = pairtab::make();
 
 struct SelectLds {
-  // Stage 1 writes the survivors here (key, index); after sorting, the same
-  // bytes hold the sorted lists as 64-bit words (key << 32) | ~index.
-  union {
-    struct {
-      uint32_t akey[64];
-      int32_t aidx[64];
-      uint32_t bkey[64];
-      int32_t bidx[64];
-    } s1;
-    struct {
-      uint64_t a[64];
-      uint64_t b[64];
-    } sorted;
-  };
-  uint64_t cand[64];  // the K selected: (key << 32) | ~f
-  uint32_t trash[64];  // per-lane sink of stage 1's branch-free compaction
+  // The survivors of each half as 64-bit words (key << 32) | ~index: stage 1
+  // writes them in no particular order, select_finish sorts them in place.
+  struct {
+    uint64_t a[64];
+    uint64_t b[64];
+  } sorted;
+  uint64_t cand[64];   // the K selected: (key << 32) | ~f
+  uint64_t trash[64];  // per-lane sink of stage 1's branch-free compaction
 };
 
 // Index of register slot p of a lane: groups of 4 consecutive elements per
@@ -161,12 +153,12 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&u)[P], int K, uint6
   return (uint32_t)lo;
 }
 
-// Stage 1 for one half: writes the K survivors (key, index) to LDS, in no
-// particular order.  Every slot is stored; a slot that is not selected goes
-// to the lane's own trash word, so the compaction has no branches.
+// Stage 1 for one half: writes the K survivors to LDS as (key << 32) | ~index,
+// in no particular order.  Every slot is stored; a slot that is not selected
+// goes to the lane's own trash word, so the compaction has no branches.
 template <int P>
 __device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int lane,
-                                       uint32_t* out_key, int32_t* out_idx, uint32_t* trash) {
+                                       uint64_t* out, uint64_t* trash) {
   uint32_t lmax = 0, lmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -195,20 +187,21 @@ __device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int
     }
     ibound = ilo;
   }
+  bool sel[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p)  // exactly K keys >= tau (the usual case), else ties cut at ibound
+    sel[p] = exact ? u[p] >= tau
+                   : (u[p] > tau || (u[p] == tau && elem_index<P>(p, lane) < ibound));
   int cnt = 0;
 #pragma unroll
-  for (int p = 0; p < P; ++p)
-    cnt += (u[p] > tau || (u[p] == tau && elem_index<P>(p, lane) < ibound)) ? 1 : 0;
+  for (int p = 0; p < P; ++p) cnt += sel[p] ? 1 : 0;
   int pos = wave_excl_scan_i32(cnt);
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const int i = elem_index<P>(p, lane);
-    const bool sel = u[p] > tau || (u[p] == tau && i < ibound);
-    uint32_t* const kd = sel ? out_key + pos : trash + lane;
-    int32_t* const id = sel ? out_idx + pos : reinterpret_cast<int32_t*>(trash + lane);
-    *kd = u[p];
-    *id = i;
-    pos += sel ? 1 : 0;
+    const uint32_t i = (uint32_t)elem_index<P>(p, lane);
+    uint64_t* const d = sel[p] ? out + pos : trash + lane;
+    *d = ((uint64_t)u[p] << 32) | (uint32_t)~i;
+    pos += sel[p] ? 1 : 0;
   }
 }
 
@@ -242,10 +235,10 @@ __device__ __forceinline__ void pair_slots(int K, uint32_t (&rc)[pairtab::kSlots
 // Stage 1 of one half, from its n values in memory to its K survivors in LDS.
 template <int P>
 __device__ __forceinline__ void stage1_half(const float* __restrict__ x, int n, int K,
-                                            uint32_t* out_key, int32_t* out_idx, uint32_t* trash) {
+                                            uint64_t* out, uint64_t* trash) {
   uint32_t u[P];
   load_keys<P>(x, n, lane_id(), u);
-  stage1<P>(u, n, K, lane_id(), out_key, out_idx, trash);
+  stage1<P>(u, n, K, lane_id(), out, trash);
 }
 
 // Everything after stage 1: both halves' survivors are in s.s1 (written by
@@ -258,11 +251,7 @@ __device__ inline void select_finish(int n, int K, SelectLds& s, const uint32_t 
   const int lane = lane_id();
 
   // ---- sort both survivor lists by (key desc, index asc)
-  uint64_t ka = 0, kb = 0;
-  if (lane < K) {
-    ka = ((uint64_t)s.s1.akey[lane] << 32) | (uint32_t)(~(uint32_t)s.s1.aidx[lane]);
-    kb = ((uint64_t)s.s1.bkey[lane] << 32) | (uint32_t)(~(uint32_t)s.s1.bidx[lane]);
-  }
+  uint64_t ka = lane < K ? s.sorted.a[lane] : 0ull, kb = lane < K ? s.sorted.b[lane] : 0ull;
   wave_sort2_desc_u64(ka, kb);
   wave_sync();
   s.sorted.a[lane] = ka;
@@ -373,8 +362,8 @@ __device__ void select_unit(const float* __restrict__ x1, const float* __restric
                             float* __restrict__ score_out, float* __restrict__ weight_out) {
   uint32_t rc[pairtab::kSlots];
   pair_slots(K, rc);
-  stage1_half<P>(x1, n, K, s.s1.akey, s.s1.aidx, s.trash);
-  stage1_half<P>(x2, n, K, s.s1.bkey, s.s1.bidx, s.trash);
+  stage1_half<P>(x1, n, K, s.sorted.a, s.trash);
+  stage1_half<P>(x2, n, K, s.sorted.b, s.trash);
   wave_sync();
   select_finish(n, K, s, rc, idx_out, score_out, weight_out);
 }

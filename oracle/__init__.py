@@ -45,12 +45,15 @@ def _L():
         lib.oracle_scan.argtypes = [p, i32, i64, i32, i64, i32, i32, p, p, p, p, p, p, p, p,
                                     i32, i32]
         lib.oracle_step_decode.argtypes = [p, i32, i32, i32, i32, i32, i32, i32] + [p] * 10
+        lib.oracle_scan_backward.argtypes = [p, i64, i32, i64, i32, i32] + [p] * 16
+        lib.oracle_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p]
         lib.oracle_last_error.restype = ctypes.c_char_p
         lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         lib.oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
-        for f in ("oracle_select", "oracle_state_init", "oracle_scan", "oracle_step_decode"):
+        for f in ("oracle_select", "oracle_state_init", "oracle_scan", "oracle_step_decode",
+                  "oracle_scan_backward", "oracle_select_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -159,6 +162,65 @@ def step_decode(M, dtype, s1, s2, q1, q2, v, alpha, beta, W: int, R: int):
                                    _ptr(q1), _ptr(q2), _ptr(v), _ptr(alpha), _ptr(beta),
                                    _ptr(out), _ptr(wi), _ptr(ri)))
     return out, wi, ri
+
+
+def scan_backward(M0, widx, wk, ridx, rw, v, alpha, beta, dout, dMT=None):
+    """Gradients of T steps on ONE fp32 memory with the selections fixed.
+
+    M0 [N,d_v]: the memory before step 0.  dout [T,d_v]: gradient of the loss
+    with respect to the read outputs; dMT [N,d_v] (default zero): with respect
+    to the memory after the last step.  Returns a dict with dM0 [N,d_v],
+    dv [T,d_v], dwk [T,W], drw [T,R], dalpha [T], dbeta [T] (all float64),
+    tape [T,W,d_v] (the pre-write rows, float32) and MT (the final memory)."""
+    M0 = _c(M0, np.float32)
+    N, d_v = M0.shape
+    widx, ridx = _c(widx, np.int32), _c(ridx, np.int32)
+    wk, rw = _c(wk, np.float64), _c(rw, np.float64)
+    v, dout = _c(v, np.float32), _c(dout, np.float32)
+    alpha, beta = _c(alpha, np.float32), _c(beta, np.float32)
+    T, W = widx.shape
+    R = ridx.shape[1]
+    assert v.shape == (T, d_v) and dout.shape == (T, d_v)
+    G = np.zeros((N, d_v), np.float64) if dMT is None else np.array(dMT, np.float64, order="C")
+    dv = np.empty((T, d_v), np.float64)
+    dwk = np.empty((T, W), np.float64)
+    drw = np.empty((T, R), np.float64)
+    da = np.empty((T,), np.float64)
+    db = np.empty((T,), np.float64)
+    tape = np.empty((T, W, d_v), np.float32)
+    MT = np.empty((N, d_v), np.float32)
+    _check(_L().oracle_scan_backward(_ptr(M0), N, d_v, T, W, R, _ptr(widx), _ptr(wk), _ptr(ridx),
+                                     _ptr(rw), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(dout),
+                                     _ptr(G), _ptr(dv), _ptr(dwk), _ptr(drw), _ptr(da), _ptr(db),
+                                     _ptr(tape), _ptr(MT)))
+    return {"dM0": G, "dv": dv, "dwk": dwk, "drw": drw, "dalpha": da, "dbeta": db,
+            "tape": tape, "MT": MT}
+
+
+def select_backward(idx, weight, dweight, n: int):
+    """Gradient of the selection weights with respect to the halves x1, x2,
+    with the selection held fixed.  idx, weight, dweight [..., K] ->
+    (dx1, dx2) [..., n], float64."""
+    idx = _c(idx, np.int32)
+    w, dw = _c(weight, np.float64), _c(dweight, np.float64)
+    K = idx.shape[-1]
+    lead = idx.shape[:-1]
+    units = int(np.prod(lead)) if lead else 1
+    dx1 = np.empty(lead + (n,), np.float64)
+    dx2 = np.empty(lead + (n,), np.float64)
+    _check(_L().oracle_select_backward(_ptr(idx), _ptr(w), _ptr(dw), units, n, K, _ptr(dx1),
+                                       _ptr(dx2)))
+    return dx1, dx2
+
+
+def state_init_backward(dM):
+    """Gradient of the per-sequence copy M[b,h] = M0[h]: dM0[h] = sum over b
+    of dM[b,h], summed in order b = 0, 1, ... in float64.  dM [B,H,N,d_v]."""
+    dM = np.asarray(dM)
+    acc = np.zeros(dM.shape[1:], np.float64)
+    for b in range(dM.shape[0]):
+        acc += dM[b]
+    return acc
 
 
 def bf16_from_double(x: float) -> int:

@@ -292,6 +292,153 @@ int oracle_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, 
   return rc;
 }
 
+/* ------------------------------------------------------------- backward
+ *
+ * Gradients of the step for training.  The pages train the whole layer end to
+ * end and learn M0 ("Stato Iniziale Appreso"; "学習された初期状態"), so the
+ * reverse pass below differentiates the write and read of "Meccanismo Core"
+ * items 3 and 4 with the selections held fixed (the chosen slot indices are
+ * piecewise constant in the scores; gradients reach the scores only through
+ * the selection weights).  fp32 state only.
+ *
+ * Forward of one step, per write row i = f_j with pre-write stored row P:
+ *   u = alpha*P + (beta*k_j)*(v - alpha*P)  = alpha*(1 - beta*k_j)*P + beta*k_j*v
+ * and the read o = sum_j r_j * M_t[g_j] of the stored rows after the write.
+ * With G the gradient of the loss with respect to the memory after step t,
+ * the chain rule gives, in reverse time order:
+ *   read:   dr_j = <do_t, M_t[g_j]>;  G[g_j] += r_j * do_t
+ *   write:  with g = G[f_j] (already holding this step's read part):
+ *           dv_t += beta*k_j * g
+ *           dalpha_t += <g, P> * (1 - beta*k_j)
+ *           d(beta k_j) = <g, v_t - alpha*P>;  dk_j = beta * d(beta k_j);
+ *           dbeta_t += k_j * d(beta k_j)
+ *           G[f_j] = alpha*(1 - beta*k_j) * g        (the row's own carry)
+ *   then the rows are restored to P, giving the memory after step t-1.
+ * Rows not written at step t carry G unchanged (the unselected rows are left
+ * as they were).  After t = 0, G is the gradient with respect to the memory's
+ * initial state.  All arithmetic in double; the forward replay stores fp32
+ * rows exactly as oracle_scan does. */
+
+/* One memory.  M0 [N,d_v] fp32: the memory before step 0.  G [N,d_v] double:
+ * in, the gradient with respect to the memory after step T-1; out, with
+ * respect to M0.  dout, dv [T,d_v]; dwk [T,W]; drw [T,R]; dalpha, dbeta [T].
+ * tape [T,W,d_v] (may be NULL): the pre-write rows of every step.  MT [N,d_v]
+ * (may be NULL): the memory after step T-1. */
+int oracle_scan_backward(const float* M0, int64_t N, int d_v, int64_t T, int W, int R,
+                         const int32_t* widx, const double* wk, const int32_t* ridx,
+                         const double* rw, const float* v, const float* alpha,
+                         const float* beta, const float* dout, double* G, double* dv,
+                         double* dwk, double* drw, double* dalpha, double* dbeta, float* tape,
+                         float* MT) {
+  if (!M0 || !widx || !wk || !ridx || !rw || !v || !alpha || !beta || !dout || !G || !dv ||
+      !dwk || !drw || !dalpha || !dbeta)
+    return fail("null pointer");
+  if (N < 1 || d_v < 1 || T < 0 || W < 1 || R < 1) return fail("bad sizes");
+  if (!all_finite(dout, T * d_v)) return fail("non-finite output gradient");
+  for (int64_t t = 0; t < T; ++t) {
+    for (int j = 0; j < W; ++j) {
+      int32_t r = widx[t * W + j];
+      if (r < 0 || r >= N) return fail("write index out of range");
+      for (int l = 0; l < j; ++l)
+        if (widx[t * W + l] == r) return fail("write indices of a step must be distinct");
+    }
+    for (int j = 0; j < R; ++j) {
+      int32_t r = ridx[t * R + j];
+      if (r < 0 || r >= N) return fail("read index out of range");
+      for (int l = 0; l < j; ++l)
+        if (ridx[t * R + l] == r) return fail("read indices of a step must be distinct");
+    }
+  }
+  float* M = (float*)malloc(sizeof(float) * (size_t)(N * d_v));
+  float* P = (float*)malloc(sizeof(float) * (size_t)(T * W * d_v + 1));
+  if (!M || !P) {
+    free(M); free(P);
+    return fail("out of memory");
+  }
+  memcpy(M, M0, sizeof(float) * (size_t)(N * d_v));
+  /* forward replay, keeping every step's pre-write rows */
+  for (int64_t t = 0; t < T; ++t) {
+    double a = (double)alpha[t], be = (double)beta[t];
+    for (int j = 0; j < W; ++j) {
+      float* row = M + (int64_t)widx[t * W + j] * d_v;
+      float* keep = P + (t * W + j) * d_v;
+      double k = wk[t * W + j];
+      for (int c = 0; c < d_v; ++c) {
+        keep[c] = row[c];
+        double mt = a * (double)row[c];
+        row[c] = (float)(mt + be * k * ((double)v[t * d_v + c] - mt));
+      }
+    }
+  }
+  if (MT) memcpy(MT, M, sizeof(float) * (size_t)(N * d_v));
+  if (tape) memcpy(tape, P, sizeof(float) * (size_t)(T * W * d_v));
+  /* reverse pass */
+  for (int64_t t = T - 1; t >= 0; --t) {
+    const float* dot = dout + t * d_v;
+    double a = (double)alpha[t], be = (double)beta[t];
+    for (int j = 0; j < R; ++j) {
+      const float* row = M + (int64_t)ridx[t * R + j] * d_v;
+      double s = 0.0;
+      for (int c = 0; c < d_v; ++c) s += (double)dot[c] * (double)row[c];
+      drw[t * R + j] = s;
+    }
+    for (int j = 0; j < R; ++j) {
+      double* g = G + (int64_t)ridx[t * R + j] * d_v;
+      for (int c = 0; c < d_v; ++c) g[c] += rw[t * R + j] * (double)dot[c];
+    }
+    for (int c = 0; c < d_v; ++c) dv[t * d_v + c] = 0.0;
+    double da = 0.0, db = 0.0;
+    for (int j = 0; j < W; ++j) {
+      double* g = G + (int64_t)widx[t * W + j] * d_v;
+      const float* keep = P + (t * W + j) * d_v;
+      double k = wk[t * W + j], bk = be * k;
+      double dbk = 0.0, gp = 0.0;
+      for (int c = 0; c < d_v; ++c) {
+        dv[t * d_v + c] += bk * g[c];
+        gp += g[c] * (double)keep[c];
+        dbk += g[c] * ((double)v[t * d_v + c] - a * (double)keep[c]);
+        g[c] = a * (1.0 - bk) * g[c];
+      }
+      da += gp * (1.0 - bk);
+      dwk[t * W + j] = be * dbk;
+      db += k * dbk;
+    }
+    dalpha[t] = da;
+    dbeta[t] = db;
+    for (int j = 0; j < W; ++j)
+      memcpy(M + (int64_t)widx[t * W + j] * d_v, P + (t * W + j) * d_v, sizeof(float) * (size_t)d_v);
+  }
+  free(M);
+  free(P);
+  return 0;
+}
+
+/* Gradient through the selection weights to the half scores, selections held
+ * fixed.  The weights are the softmax of the selected sums sigma_j, and
+ * sigma_j = x1[a_j] + x2[b_j] with f_j = a_j*n + b_j, so
+ *   dsigma_j = w_j * (dw_j - sum_l w_l dw_l),
+ *   dx1[a] = sum of dsigma_j over j with a_j = a, dx2[b] likewise,
+ * and zero for every half index that no selected slot uses.
+ * idx, w, dw [units, K]; dx1, dx2 [units, n]. */
+int oracle_select_backward(const int32_t* idx, const double* w, const double* dw, int64_t units,
+                           int n, int K, double* dx1, double* dx2) {
+  if (!idx || !w || !dw || !dx1 || !dx2) return fail("null pointer");
+  if (units < 0 || n < 1 || K < 1 || K > n) return fail("bad sizes");
+  for (int64_t u = 0; u < units; ++u) {
+    const int32_t* f = idx + u * K;
+    double s = 0.0;
+    for (int j = 0; j < K; ++j) s += w[u * K + j] * dw[u * K + j];
+    for (int i = 0; i < n; ++i) dx1[u * n + i] = dx2[u * n + i] = 0.0;
+    for (int j = 0; j < K; ++j) {
+      if (f[j] < 0 || f[j] >= n * n) return fail("slot index out of range");
+      double ds = w[u * K + j] * (dw[u * K + j] - s);
+      dx1[u * n + f[j] / n] += ds;
+      dx2[u * n + f[j] % n] += ds;
+    }
+  }
+  return 0;
+}
+
 /* bf16 helpers exposed for the tests of the oracle itself. */
 uint16_t oracle_bf16_from_double(double x) { return bf16_from_double(x); }
 double oracle_bf16_to_double(uint16_t h) { return bf16_to_double(h); }

@@ -50,6 +50,7 @@
 #ifndef SDM_H
 #define SDM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -118,6 +119,75 @@ int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int
                     const float* s1, const float* s2, const float* q1, const float* q2,
                     const float* v, const float* alpha, const float* beta, float* out,
                     int32_t* widx, int32_t* ridx, void* stream);
+
+/* ---- Training: the forward with a tape, and the reverse pass.
+ * The pages train the layer end to end and learn M0 ("Stato Iniziale
+ * Appreso"); these calls give the gradients of the write and read
+ * ("Meccanismo Core", items 3 and 4) with the selections held fixed (the
+ * chosen slots are piecewise constant in the scores; gradients reach the
+ * scores through the selection weights only).  fp32 state only. */
+
+/* sdm_scan (fp32 state) that also keeps every step's pre-write rows.
+ *   tape  [B, H, T, W, d_v] fp32 out: tape[b,h,t,j] = the stored row
+ *         widx[b,h,t,j] just before step t's write (rows outside [0, N) are
+ *         not written).  One memory's tape, T*W*d_v*4 bytes, must be below
+ *         2 GiB (split longer sequences into consecutive calls).
+ * Every other argument and output is as for sdm_scan, and the results are
+ * identical to it. */
+int sdm_scan_train(void* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                   const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+                   const float* v, const float* alpha, const float* beta, float* out,
+                   float* tape, void* stream);
+
+/* Bytes of workspace sdm_scan_backward needs for these sizes. */
+size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W, int R);
+
+/* Reverse pass over T steps, t = T-1 .. 0, for every (b,h) memory.
+ *   M      [B, H, N, d_v] fp32 in/out: the state after the forward's last
+ *          step; rolled back in place from the tape, it ends bit-identical to
+ *          the state before the forward's first step.
+ *   widx, wk, ridx, rw, v, alpha, beta: the forward's inputs (shapes as for
+ *          sdm_scan).  The rows of each step's widx must be distinct, and so
+ *          must those of each step's ridx (sdm_select guarantees both).
+ *   tape   [B, H, T, W, d_v] fp32 in: from sdm_scan_train on the same inputs.
+ *   dout   [B, H, T, d_v] fp32 in: dL/d out.
+ *   G      [B, H, N, d_v] fp32 in/out: in, dL/d(state after step T-1) (zeros
+ *          when the final state is not used); out, dL/d(state before step 0).
+ *   dv     [B, H, T, d_v] fp32 out: dL/dv.
+ *   dwk    [B, H, T, W] fp32 out: dL/dk (the write weights).
+ *   drw    [B, H, T, R] fp32 out: dL/dr (the read weights).
+ *   dalpha, dbeta [B, H, T] fp32 out.
+ *   workspace  device buffer of at least
+ *          sdm_scan_backward_workspace_size(B, H, d_v, T, W, R) bytes,
+ *          16-byte aligned; its contents on entry do not matter.
+ * Per step, with P the pre-write row of write row f_j and g = G[f_j] after
+ * the step's read contributions G[g_l] += r_l * dout_t:
+ *   dv_t += beta*k_j*g;  dalpha_t += (1 - beta*k_j)*<g, P>;
+ *   dk_j = beta*<g, v_t - alpha*P>;  dbeta_t += k_j*<g, v_t - alpha*P>;
+ *   G[f_j] = alpha*(1 - beta*k_j)*g;   dr_l = <dout_t, M_t[g_l]>.
+ * Arithmetic in fp32; the tile partial sums are added in a fixed order, so
+ * results are deterministic.  Sizes as for sdm_scan, plus T < 2^26. */
+int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                      const int32_t* widx, const float* wk, const int32_t* ridx,
+                      const float* rw, const float* v, const float* alpha, const float* beta,
+                      const float* tape, const float* dout, float* G, float* dv, float* dwk,
+                      float* drw, float* dalpha, float* dbeta, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Gradient of the selection weights back to the halves ("Meccanismo Core",
+ * item 2: slot f = a*n + b scores x1[a] + x2[b]), selections held fixed.
+ *   idx, weight  [units, K] from sdm_select;  dweight [units, K] fp32 in.
+ *   dx1, dx2     [units, n] fp32 out: with dsigma_j = w_j*(dw_j - sum_l w_l dw_l),
+ *                dx1[a] = sum of dsigma_j over the j with a_j = a (dx2 with
+ *                b_j), zero at every half index no selected slot uses. */
+int sdm_select_backward(const int32_t* idx, const float* weight, const float* dweight,
+                        int64_t units, int n, int K, float* dx1, float* dx2, void* stream);
+
+/* Gradient of the per-sequence copy M[b,h] = M0[h]:
+ *   dM0[h] = sum over b = 0, 1, ... of G[b,h].
+ *   G [B, H, N, d_v] fp32 in;  dM0 [H, N, d_v] fp32 out (16-byte aligned). */
+int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v, float* dM0,
+                            void* stream);
 
 /* Static text for a status code. */
 const char* sdm_status_string(int status);

@@ -22,6 +22,8 @@ Recipe (per element, all float32):
   v               N(0,1) of length d_v per (b,h,t)
   alpha           U(0.9, 1) per (b,h,t);  beta U(0, 1) per (b,h,t)
   M0              0.02 * N(0,1), one [N, d_v] table per head
+  dout            N(0,1) of length d_v per (b,h,t): the output gradient fed to
+                  the reverse pass (training)
   long: planted recall -- at t=1000 slot (i*, j*) gets s1[i*]=s2[j*]=16,
         v=e_0, alpha=beta=1; at t=T-1 the read halves get q1[i*]=q2[j*]=16.
 """
@@ -82,7 +84,7 @@ CONFIGS = {
 
 # Stream tags (the Philox key's second word).
 TAGS = {"s1": 0, "s2": 1, "q1": 2, "q2": 3, "v": 4, "alpha": 5, "beta": 6, "M0": 7,
-        "g1": 8, "g2": 9, "planted": 10}
+        "g1": 8, "g2": 9, "planted": 10, "dout": 11}
 
 PLANT_WRITE_T = 1000
 PLANT_SCORE = 16.0
@@ -103,6 +105,8 @@ def _recipe(cfg: Config, name: str):
         return TAGS["beta"], GEN_UNIFORM, 1.0, 0.0, 1.0, -1, 0.0, 1
     if name == "M0":
         return TAGS["M0"], GEN_NORMAL, 0.02, 0.0, 0.0, -1, 0.0, cfg.d_v
+    if name == "dout":  # training: gradient of the loss with respect to the outputs
+        return TAGS["dout"], GEN_NORMAL, 1.0, 0.0, 0.0, -1, 0.0, cfg.d_v
     raise KeyError(name)
 
 

@@ -12,6 +12,11 @@ Calls (same names as the C ABI without the "sdm_" prefix):
   state_init(M0, B, dtype)               -> M
   scan(M, widx, wk, ridx, rw, v, alpha, beta) -> out      (M updated in place)
   step_decode(M, s1, s2, q1, q2, v, alpha, beta, W, R) -> (out, widx, ridx)
+Training (fp32 state; selections held fixed):
+  scan_train(M, widx, wk, ridx, rw, v, alpha, beta) -> (out, tape)
+  scan_backward(M, widx, wk, ridx, rw, v, alpha, beta, tape, dout, G) -> dict
+  select_backward(idx, weight, dweight, n) -> (dx1, dx2)
+  state_init_backward(G) -> dM0
 """
 from __future__ import annotations
 
@@ -26,8 +31,9 @@ SDM_BF16 = 1
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_INVALID", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_HIP"}
 
 # Every symbol include/sdm.h declares.
-EXPORTS = ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_status_string",
-           "sdm_last_error", "sdm_abi_version")
+EXPORTS = ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_scan_train",
+           "sdm_scan_backward_workspace_size", "sdm_scan_backward", "sdm_select_backward",
+           "sdm_state_init_backward", "sdm_status_string", "sdm_last_error", "sdm_abi_version")
 
 _lib = None
 
@@ -51,8 +57,16 @@ def lib():
         L.sdm_state_init.argtypes = [p, i32, p, i32, i32, i64, i32, p]
         L.sdm_scan.argtypes = [p, i32, i32, i32, i64, i32, i64, i32, i32] + [p] * 9
         L.sdm_step_decode.argtypes = [p, i32, i32, i32, i32, i32, i32, i32] + [p] * 11
+        L.sdm_scan_train.argtypes = [p, i32, i32, i64, i32, i64, i32, i32] + [p] * 10
+        L.sdm_scan_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32, i32]
+        L.sdm_scan_backward_workspace_size.restype = ctypes.c_size_t
+        L.sdm_scan_backward.argtypes = ([p, i32, i32, i64, i32, i64, i32, i32] + [p] * 16 +
+                                        [ctypes.c_size_t, p])
+        L.sdm_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p, p]
+        L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p]
         for f in ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode",
-                  "sdm_abi_version"):
+                  "sdm_abi_version", "sdm_scan_train", "sdm_scan_backward",
+                  "sdm_select_backward", "sdm_state_init_backward"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i32]
         L.sdm_status_string.restype = ctypes.c_char_p
@@ -193,3 +207,103 @@ def step_decode(M, s1, s2, q1, q2, v, alpha, beta, W: int, R: int, out=None, wan
                                  ridx.data_ptr() if ridx is not None else None,
                                  _stream(stream)))
     return out, widx, ridx
+
+
+def _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta):
+    B, H, N, d_v = M.shape
+    T, W = widx.shape[2], widx.shape[3]
+    R = ridx.shape[3]
+    for name, t, shp in (("widx", widx, (B, H, T, W)), ("wk", wk, (B, H, T, W)),
+                         ("ridx", ridx, (B, H, T, R)), ("rw", rw, (B, H, T, R)),
+                         ("v", v, (B, H, T, d_v)), ("alpha", alpha, (B, H, T)),
+                         ("beta", beta, (B, H, T))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be {shp}, got {tuple(t.shape)}")
+    return B, H, N, d_v, T, W, R
+
+
+def _scan_ptrs(widx, wk, ridx, rw, v, alpha, beta):
+    import torch
+
+    return (_dev(widx, torch.int32, "widx"), _dev(wk, torch.float32, "wk"),
+            _dev(ridx, torch.int32, "ridx"), _dev(rw, torch.float32, "rw"),
+            _dev(v, torch.float32, "v"), _dev(alpha, torch.float32, "alpha"),
+            _dev(beta, torch.float32, "beta"))
+
+
+def scan_train(M, widx, wk, ridx, rw, v, alpha, beta, out=None, tape=None, stream=None):
+    """scan() on an fp32 state that also keeps every step's pre-write rows:
+    returns (out [B,H,T,d_v], tape [B,H,T,W,d_v])."""
+    import torch
+
+    B, H, N, d_v, T, W, R = _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta)
+    if out is None:
+        out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
+    if tape is None:
+        tape = torch.empty((B, H, T, W, d_v), dtype=torch.float32, device=M.device)
+    _check(lib().sdm_scan_train(_dev(M, torch.float32, "M", 4), B, H, N, d_v, T, W, R,
+                                *_scan_ptrs(widx, wk, ridx, rw, v, alpha, beta),
+                                _dev(out, torch.float32, "out"),
+                                _dev(tape, torch.float32, "tape"), _stream(stream)))
+    return out, tape
+
+
+def scan_backward(M, widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=None,
+                  stream=None):
+    """Reverse pass: M (state after the forward) is rolled back in place to
+    the state before it; G (dL/d final state) becomes dL/d initial state.
+    Returns dict dv [B,H,T,d_v], dwk [B,H,T,W], drw [B,H,T,R], dalpha,
+    dbeta [B,H,T]."""
+    import torch
+
+    B, H, N, d_v, T, W, R = _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta)
+    dev = M.device
+    f32 = torch.float32
+    o = {"dv": torch.empty((B, H, T, d_v), dtype=f32, device=dev),
+         "dwk": torch.empty((B, H, T, W), dtype=f32, device=dev),
+         "drw": torch.empty((B, H, T, R), dtype=f32, device=dev),
+         "dalpha": torch.empty((B, H, T), dtype=f32, device=dev),
+         "dbeta": torch.empty((B, H, T), dtype=f32, device=dev)}
+    need = int(lib().sdm_scan_backward_workspace_size(B, H, d_v, T, W, R))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=f32, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().sdm_scan_backward(_dev(M, f32, "M", 4), B, H, N, d_v, T, W, R,
+                                   *_scan_ptrs(widx, wk, ridx, rw, v, alpha, beta),
+                                   _dev(tape, f32, "tape"), _dev(dout, f32, "dout"),
+                                   _dev(G, f32, "G", 4), o["dv"].data_ptr(), o["dwk"].data_ptr(),
+                                   o["drw"].data_ptr(), o["dalpha"].data_ptr(),
+                                   o["dbeta"].data_ptr(), _dev(workspace, workspace.dtype,
+                                                               "workspace"),
+                                   nbytes, _stream(stream)))
+    return o
+
+
+def select_backward(idx, weight, dweight, n: int, stream=None):
+    """Gradient of the selection weights back to the halves: idx, weight,
+    dweight [..., K] -> (dx1, dx2) [..., n] fp32."""
+    import torch
+
+    K = idx.shape[-1]
+    lead = tuple(idx.shape[:-1])
+    units = 1
+    for s in lead:
+        units *= s
+    dx1 = torch.empty(lead + (n,), dtype=torch.float32, device=idx.device)
+    dx2 = torch.empty(lead + (n,), dtype=torch.float32, device=idx.device)
+    _check(lib().sdm_select_backward(_dev(idx, torch.int32, "idx"),
+                                     _dev(weight, torch.float32, "weight"),
+                                     _dev(dweight, torch.float32, "dweight"), units, n, K,
+                                     dx1.data_ptr(), dx2.data_ptr(), _stream(stream)))
+    return dx1, dx2
+
+
+def state_init_backward(G, out=None, stream=None):
+    """dM0 [H,N,d_v] = sum over b of G [B,H,N,d_v]."""
+    import torch
+
+    B, H, N, d_v = G.shape
+    dM0 = torch.empty((H, N, d_v), dtype=torch.float32, device=G.device) if out is None else out
+    _check(lib().sdm_state_init_backward(_dev(G, torch.float32, "G", 4), B, H, N, d_v,
+                                         _dev(dM0, torch.float32, "dM0", 3), _stream(stream)))
+    return dM0

@@ -119,9 +119,14 @@ int sdm_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N,
   return finish("sdm_state_init", sdm::launch_state_init(M, dtype, M0, B, H, N, d_v, s), s);
 }
 
-int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
-             const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
-             const float* v, const float* alpha, const float* beta, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int check_scan_args(const void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W,
+                    int R, const int32_t* widx, const float* wk, const int32_t* ridx,
+                    const float* rw, const float* v, const float* alpha, const float* beta,
+                    const float* out) {
   int rc;
   if ((rc = check_state(M, dtype, N, d_v))) return rc;
   if (!widx || !wk || !ridx || !rw || !v || !alpha || !beta || !out)
@@ -139,11 +144,110 @@ int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, in
   if (W > N || R > N) return fail(SDM_ERR_INVALID, "W and R must not exceed N");
   if (N * d_v * (dtype == SDM_F32 ? 4 : 2) >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's table must be below 2 GiB for sdm_scan");
+  return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+             const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+             const float* v, const float* alpha, const float* beta, float* out, void* stream) {
+  int rc;
+  if ((rc = check_scan_args(M, dtype, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta,
+                            out)))
+    return rc;
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_scan",
                 sdm::launch_scan(M, dtype, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
-                                 beta, out, s),
+                                 beta, out, nullptr, s),
                 s);
+}
+
+int sdm_scan_train(void* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                   const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+                   const float* v, const float* alpha, const float* beta, float* out,
+                   float* tape, void* stream) {
+  int rc;
+  if ((rc = check_scan_args(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                            beta, out)))
+    return rc;
+  if (!tape) return fail(SDM_ERR_INVALID, "tape is NULL");
+  if (!aligned(tape, 16)) return fail(SDM_ERR_INVALID, "tape must be 16-byte aligned");
+  if (T * W * d_v * 4 >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*W*d_v*4 bytes) must be below 2 GiB; "
+                "split the sequence into consecutive calls");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_scan_train",
+                sdm::launch_scan(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                                 beta, out, tape, s),
+                s);
+}
+
+size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W, int R) {
+  if (B < 1 || H < 1 || T < 0 || W < 1 || R < 1 || !dv_supported(d_v)) return 0;
+  return sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
+}
+
+int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                      const int32_t* widx, const float* wk, const int32_t* ridx,
+                      const float* rw, const float* v, const float* alpha, const float* beta,
+                      const float* tape, const float* dout, float* G, float* dv, float* dwk,
+                      float* drw, float* dalpha, float* dbeta, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_scan_args(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                            beta, dv)))
+    return rc;
+  if (!tape || !dout || !G || !dwk || !drw || !dalpha || !dbeta || !workspace)
+    return fail(SDM_ERR_INVALID, "a backward input or output pointer is NULL");
+  if (!aligned(tape, 16) || !aligned(dout, 16) || !aligned(G, 16) || !aligned(workspace, 16))
+    return fail(SDM_ERR_INVALID, "tape, dout, G and workspace must be 16-byte aligned");
+  if (!aligned(dwk, 4) || !aligned(drw, 4) || !aligned(dalpha, 4) || !aligned(dbeta, 4))
+    return fail(SDM_ERR_INVALID, "dwk, drw, dalpha and dbeta must be 4-byte aligned");
+  if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
+  if (T * W * d_v * 4 >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*W*d_v*4 bytes) must be below 2 GiB; "
+                "split the sequence into consecutive calls");
+  const size_t need = sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
+  if (workspace_bytes < need)
+    return fail(SDM_ERR_INVALID, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_scan_backward",
+                sdm::launch_scan_backward(M, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                                          beta, tape, dout, G, dv, dwk, drw, dalpha, dbeta,
+                                          reinterpret_cast<float*>(workspace), s),
+                s);
+}
+
+int sdm_select_backward(const int32_t* idx, const float* weight, const float* dweight,
+                        int64_t units, int n, int K, float* dx1, float* dx2, void* stream) {
+  int rc;
+  if (!idx || !weight || !dweight || !dx1 || !dx2)
+    return fail(SDM_ERR_INVALID, "a selection-gradient pointer is NULL");
+  if (!aligned(idx, 4) || !aligned(weight, 4) || !aligned(dweight, 4) || !aligned(dx1, 4) ||
+      !aligned(dx2, 4))
+    return fail(SDM_ERR_INVALID, "selection-gradient arrays must be 4-byte aligned");
+  if (units < 0) return fail(SDM_ERR_INVALID, "units must be >= 0");
+  if ((rc = check_n_k(n, K, "K"))) return rc;
+  if (units > ((int64_t)1 << 32)) return fail(SDM_ERR_INVALID, "units above 2^32");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_select_backward",
+                sdm::launch_select_backward(idx, weight, dweight, units, n, K, dx1, dx2, s), s);
+}
+
+int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v, float* dM0,
+                            void* stream) {
+  int rc;
+  if ((rc = check_state(G, SDM_F32, N, d_v))) return rc;
+  if (!dM0) return fail(SDM_ERR_INVALID, "dM0 is NULL");
+  if (!aligned(dM0, 16)) return fail(SDM_ERR_INVALID, "dM0 must be 16-byte aligned");
+  if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_state_init_backward",
+                sdm::launch_state_init_backward(G, B, H, N, d_v, dM0, s), s);
 }
 
 int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,

@@ -1,0 +1,439 @@
+// Reverse pass of the SDM step for training: gradients of the gated delta
+// write and the sparse read (page "Riepilogo Tecnico: Sparse Delta Memory
+// (SDM)", section "Meccanismo Core", items 3 and 4) with the selections held
+// fixed, the selection weights' gradient taken back to the key halves
+// (item 2: slot a*n + b scores x1[a] + x2[b]), and the gradient of the
+// learned initial state (section "Stato Iniziale Appreso").
+//
+// Per step, for write row i = f_j with pre-write stored row P and
+// g = dL/dM_t[i] (this step's read part included):
+//   u = alpha*(1 - beta*k_j)*P + beta*k_j*v          (the forward write)
+//   dv += beta*k_j*g;  dalpha += (1 - beta*k_j)*<g, P>;
+//   d(beta*k_j) = <g, v - alpha*P>;  dM_{t-1}[i] = alpha*(1 - beta*k_j)*g
+// and for read row g_j: dr_j = <do, M_t[g_j]>, dM_t[g_j] += r_j*do.
+// Rows that a step does not write carry their gradient unchanged.
+//
+// scan_bwd_kernel walks t = T-1 .. 0 with one wavefront per (memory,
+// 32-column tile).  The state M (after the forward) is rolled back one step
+// at a time from the tape of pre-write rows that the training forward kept,
+// so a step's read sees exactly the stored values the forward read, and the
+// memory ends as it started.  The gradient table G (caller-owned, the shape
+// of M) starts as dL/dM_T and ends as dL/dM_0.  Each step gathers the read
+// rows of M and G and the write rows of G and of the tape (all 16-byte
+// buffer loads of one tile row per lane group), matches write rows against
+// this step's read rows through a hashed LDS table, and stores G's read
+// rows, then G's write rows, then M's restored rows -- in that order, so a
+// row that is both read and written ends with its write-side value.  All
+// accesses to a (row, tile) come from one wavefront, and the next step's
+// loads are issued after this step's stores, so program order keeps every
+// step's view current.  Per-tile partial sums of d(beta*k), dr and dalpha go
+// to a caller-provided workspace; a finishing kernel adds the tiles in a
+// fixed order (deterministic) and applies beta and the k weights.  Nothing
+// here is a dense contraction: no MFMA.
+#include "device_common.h"
+#include "internal.h"
+
+namespace sdm {
+namespace {
+
+constexpr int kBufWord3 = 0x00020000;  // raw buffer access, gfx9 family
+constexpr uint32_t kOffNone = 0x80000000u;  // outside every range: loads 0, stores dropped
+constexpr int kHashBits = 12;
+
+struct BwdArgs {
+  int n_mem;
+  int64_t N;
+  int d_v;
+  int64_t T;
+  int W, R;
+  const int32_t* widx;
+  const float* wk;
+  const int32_t* ridx;
+  const float* rw;
+  const float* v;
+  const float* alpha;
+  const float* beta;
+  const float* dout;
+  const float* tape;
+  float* G;
+  float* dv;
+  float* ws;
+  int ntiles;
+};
+
+__device__ __forceinline__ uint32_t hash_slot(uint32_t row) {
+  return (row * 2654435761u) >> (32 - kHashBits);
+}
+
+__device__ __forceinline__ f32x4 as_f4(const u32x4& q) {
+  return f32x4{__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
+               __uint_as_float(q.w)};
+}
+__device__ __forceinline__ u32x4 as_u4(const f32x4& f) {
+  return u32x4{__float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(f.z),
+               __float_as_uint(f.w)};
+}
+
+template <int O>
+__device__ __forceinline__ float xor_add(float x) {
+  return x + __uint_as_float(lane_xor(__float_as_uint(x), O));
+}
+
+// Sum over the LPR lanes that hold one row (lanes differ in the low bits).
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (LPR >= 2) x = xor_add<1>(x);
+  if constexpr (LPR >= 4) x = xor_add<2>(x);
+  if constexpr (LPR >= 8) x = xor_add<4>(x);
+  return x;
+}
+
+// Sum over the lanes that hold the same columns (lanes differ in the high bits).
+template <int LPR>
+__device__ __forceinline__ float col_sum(float x) {
+  if constexpr (LPR <= 4) x = xor_add<4>(x);
+  if constexpr (LPR <= 8) x = xor_add<8>(x);
+  x = xor_add<16>(x);
+  x = xor_add<32>(x);
+  return x;
+}
+
+template <int COLS>
+__global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, BwdArgs A) {
+  constexpr int LPR = COLS / 4;      // lanes per tile row (16 bytes each)
+  constexpr int RPI = kWave / LPR;   // rows per wave instruction
+  constexpr int NI = 64 / RPI;       // instructions for 64 row slots
+  __shared__ uint64_t tab[1 << kHashBits];  // (row << 32) | (t << 6 | slot)
+  __shared__ float rws[64];
+
+  // XCD-aware numbering as in the forward: every tile of a memory on one XCD.
+  const int bid = blockIdx.x;
+  const int x = bid & 7;
+  const int rest = bid >> 3;
+  const int tile = rest % A.ntiles;
+  const int mem = (rest / A.ntiles) * 8 + x;
+  if (mem >= A.n_mem) return;
+
+  const int lane = lane_id();
+  const int lr = lane / LPR, lc = lane % LPR;
+  const int d_v = A.d_v, W = A.W, R = A.R;
+  const int64_t T = A.T, N = A.N;
+  for (int i = lane; i < (1 << kHashBits); i += kWave) tab[i] = ~0ull;
+
+  const int64_t mem_elems = N * d_v;
+  const int tile_bytes = tile * COLS * 4;
+  const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
+      M + (int64_t)mem * mem_elems + tile * COLS, 0, (int)(mem_elems * 4 - tile_bytes),
+      kBufWord3);
+  const __amdgpu_buffer_rsrc_t gres = __builtin_amdgcn_make_buffer_rsrc(
+      A.G + (int64_t)mem * mem_elems + tile * COLS, 0, (int)(mem_elems * 4 - tile_bytes),
+      kBufWord3);
+  const int64_t tape_elems = T * W * d_v;
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(A.tape) + (int64_t)mem * tape_elems + tile * COLS, 0,
+      (int)(tape_elems * 4 - tile_bytes), kBufWord3);
+  const uint32_t row_bytes = (uint32_t)d_v * 4u;
+  const uint32_t lane_off = (uint32_t)lc * 16u;
+
+  const int32_t* widx = A.widx + (int64_t)mem * T * W;
+  const float* wk = A.wk + (int64_t)mem * T * W;
+  const int32_t* ridx = A.ridx + (int64_t)mem * T * R;
+  const float* rw = A.rw + (int64_t)mem * T * R;
+  const float* vm = A.v + (int64_t)mem * T * d_v + tile * COLS + lc * 4;
+  const float* dom = A.dout + (int64_t)mem * T * d_v + tile * COLS + lc * 4;
+  float* dvm = A.dv + (int64_t)mem * T * d_v + tile * COLS + lc * 4;
+  const float* am = A.alpha + (int64_t)mem * T;
+  const float* bm = A.beta + (int64_t)mem * T;
+  const int ws_row = W + R + 1;
+  float* wsm = A.ws + ((int64_t)mem * T * A.ntiles + tile) * ws_row;
+  wave_sync();
+
+  for (int64_t t = T - 1; t >= 0; --t) {
+    // ---- this step's plan
+    uint32_t wrow[NI], wo[NI], ro[NI], to[NI];
+    float wkk[NI], rwk[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int j = k * RPI + lr;
+      const int32_t fw = j < W ? widx[t * W + j] : -1;
+      const int32_t fr = j < R ? ridx[t * R + j] : -1;
+      const bool wv = (uint32_t)fw < (uint32_t)N, rv = (uint32_t)fr < (uint32_t)N;
+      wrow[k] = wv ? (uint32_t)fw : 0xFFFFFFFFu;
+      wo[k] = wv ? (uint32_t)fw * row_bytes + lane_off : kOffNone;
+      ro[k] = rv ? (uint32_t)fr * row_bytes + lane_off : kOffNone;
+      to[k] = wv ? ((uint32_t)t * (uint32_t)W + (uint32_t)j) * row_bytes + lane_off : kOffNone;
+      wkk[k] = j < W ? wk[t * W + j] : 0.0f;
+      rwk[k] = j < R ? rw[t * R + j] : 0.0f;
+    }
+    const f32x4 vv = *reinterpret_cast<const f32x4*>(vm + t * d_v);
+    const f32x4 dd = *reinterpret_cast<const f32x4*>(dom + t * d_v);
+    const float a = am[t], b = bm[t];
+
+    // ---- gathers (all issued before any is used)
+    u32x4 Mg[NI], Gg[NI], Gf[NI], P[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) Mg[k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ro[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) Gg[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, ro[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) Gf[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, wo[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) P[k] = __builtin_amdgcn_raw_buffer_load_b128(tres, to[k], 0, 0);
+
+    // ---- match write rows to this step's read rows while the gathers fly.
+    // Lane j inserts read slot j; a read row whose table entry was taken by
+    // another read row of the step (hash collision) is matched by a
+    // wave-uniform loop instead.  Entries of other steps carry another stamp.
+    const int32_t my_r = lane < R ? ridx[t * R + lane] : -1;
+    const bool my_valid = (uint32_t)my_r < (uint32_t)N;
+    const uint32_t stamp = ((uint32_t)t << 6) | (uint32_t)lane;
+    const uint64_t entry = ((uint64_t)(uint32_t)my_r << 32) | stamp;
+    rws[lane] = lane < R ? rw[t * R + lane] : 0.0f;
+    if (my_valid) tab[hash_slot((uint32_t)my_r)] = entry;
+    wave_sync();
+    const bool lost = my_valid && tab[hash_slot((uint32_t)my_r)] != entry;
+    uint64_t lostmask = __ballot(lost);
+    int match[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const uint64_t e = tab[hash_slot(wrow[k])];
+      const bool hit = wrow[k] != 0xFFFFFFFFu && (uint32_t)(e >> 32) == wrow[k] &&
+                       ((uint32_t)e >> 6) == (uint32_t)t;
+      match[k] = hit ? (int)(e & 63u) : -1;
+    }
+    while (lostmask) {
+      const int j = __builtin_ctzll(lostmask);
+      lostmask &= lostmask - 1;
+      const uint32_t s = (uint32_t)__builtin_amdgcn_readlane(my_r, j);
+#pragma unroll
+      for (int k = 0; k < NI; ++k)
+        if (wrow[k] == s) match[k] = j;
+    }
+    float mw[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) mw[k] = match[k] >= 0 ? rws[match[k]] : 0.0f;
+
+    // ---- read part: dr_j and G[g_j] += r_j * do
+    float drp[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const f32x4 m = as_f4(Mg[k]);
+      drp[k] = dd.x * m.x + dd.y * m.y + dd.z * m.z + dd.w * m.w;
+      f32x4 g = as_f4(Gg[k]);
+      g.x = fmaf(rwk[k], dd.x, g.x);
+      g.y = fmaf(rwk[k], dd.y, g.y);
+      g.z = fmaf(rwk[k], dd.z, g.z);
+      g.w = fmaf(rwk[k], dd.w, g.w);
+      Gg[k] = as_u4(g);
+    }
+    // ---- write part
+    f32x4 dva = {0.f, 0.f, 0.f, 0.f};
+    float dap = 0.0f;
+    float dbk[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      f32x4 g = as_f4(Gf[k]);
+      g.x = fmaf(mw[k], dd.x, g.x);
+      g.y = fmaf(mw[k], dd.y, g.y);
+      g.z = fmaf(mw[k], dd.z, g.z);
+      g.w = fmaf(mw[k], dd.w, g.w);
+      const f32x4 p = as_f4(P[k]);
+      const float bk = b * wkk[k];
+      dva.x = fmaf(bk, g.x, dva.x);
+      dva.y = fmaf(bk, g.y, dva.y);
+      dva.z = fmaf(bk, g.z, dva.z);
+      dva.w = fmaf(bk, g.w, dva.w);
+      const float gp = g.x * p.x + g.y * p.y + g.z * p.z + g.w * p.w;
+      dap = fmaf(1.0f - bk, gp, dap);
+      dbk[k] = g.x * (vv.x - a * p.x) + g.y * (vv.y - a * p.y) + g.z * (vv.z - a * p.z) +
+               g.w * (vv.w - a * p.w);
+      const float c = a * (1.0f - bk);
+      Gf[k] = as_u4(f32x4{c * g.x, c * g.y, c * g.z, c * g.w});
+    }
+    // ---- stores: G read rows, then G write rows, then the restored M rows
+#pragma unroll
+    for (int k = 0; k < NI; ++k) __builtin_amdgcn_raw_buffer_store_b128(Gg[k], gres, ro[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) __builtin_amdgcn_raw_buffer_store_b128(Gf[k], gres, wo[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) __builtin_amdgcn_raw_buffer_store_b128(P[k], mres, wo[k], 0, 0);
+
+    // ---- reductions and the step's partial sums
+    float* wst = wsm + t * (int64_t)A.ntiles * ws_row;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const float s_bk = row_sum<LPR>(dbk[k]);
+      const float s_dr = row_sum<LPR>(drp[k]);
+      const int j = k * RPI + lr;
+      if (lc == 0) {
+        if (j < W) wst[j] = s_bk;
+        if (j < R) wst[W + j] = s_dr;
+      }
+    }
+    dva.x = col_sum<LPR>(dva.x);
+    dva.y = col_sum<LPR>(dva.y);
+    dva.z = col_sum<LPR>(dva.z);
+    dva.w = col_sum<LPR>(dva.w);
+    if (lr == 0) *reinterpret_cast<f32x4*>(dvm + t * d_v) = dva;
+    const float da = wave_sum_f32(dap);
+    if (lane == 0) wst[W + R] = da;
+    wave_sync();  // rws and tab are rewritten by the next step
+  }
+}
+
+// dwk = beta * sum over tiles of d(beta k); drw = sum of dr; dalpha = sum;
+// dbeta = sum_j k_j * d(beta k_j).  One wavefront per (memory, step).
+__global__ __launch_bounds__(256) void scan_bwd_finish(BwdArgs A, float* __restrict__ dwk,
+                                                       float* __restrict__ drw,
+                                                       float* __restrict__ dalpha,
+                                                       float* __restrict__ dbeta) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int64_t units = (int64_t)A.n_mem * A.T;
+  if (u >= units) return;  // whole wavefront leaves together
+  const int lane = lane_id();
+  const int W = A.W, R = A.R, ws_row = W + R + 1;
+  const float* p = A.ws + u * A.ntiles * ws_row;
+  float sbk = 0.0f, sdr = 0.0f, sda = 0.0f;
+  for (int tl = 0; tl < A.ntiles; ++tl) {
+    const float* q = p + tl * ws_row;
+    if (lane < W) sbk += q[lane];
+    if (lane < R) sdr += q[W + lane];
+    sda += q[W + R];
+  }
+  const float b = A.beta[u];
+  const float kj = lane < W ? A.wk[u * W + lane] : 0.0f;
+  if (lane < W) dwk[u * W + lane] = b * sbk;
+  if (lane < R) drw[u * R + lane] = sdr;
+  const float db = wave_sum_f32(lane < W ? kj * sbk : 0.0f);
+  if (lane == 0) {
+    dalpha[u] = sda;
+    dbeta[u] = db;
+  }
+}
+
+// Selection weights back to the halves.  One wavefront per unit: the two
+// half-gradient rows are zeroed, then lane j (< K) computes
+// dsigma_j = w_j (dw_j - sum_l w_l dw_l) and, for its half indices a_j and
+// b_j, the sum of dsigma_l over every l with the same half index (in order
+// l = 0, 1, ...); the lowest such l stores it.
+__global__ __launch_bounds__(256) void select_bwd_kernel(const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ dw,
+                                                         int64_t units, int n, int K,
+                                                         float* __restrict__ dx1,
+                                                         float* __restrict__ dx2) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (u >= units) return;  // whole wavefront leaves together
+  const int lane = lane_id();
+  float* r1 = dx1 + u * n;
+  float* r2 = dx2 + u * n;
+  for (int i = lane; i < n; i += kWave) {
+    r1[i] = 0.0f;
+    r2[i] = 0.0f;
+  }
+  const bool on = lane < K;
+  const int32_t f = on ? idx[u * K + lane] : 0;
+  const float wj = on ? w[u * K + lane] : 0.0f;
+  const float dwj = on ? dw[u * K + lane] : 0.0f;
+  const float s = wave_sum_f32(wj * dwj);
+  const float ds = wj * (dwj - s);
+  const int ia = on ? f / n : -1, ib = on ? f % n : -1;
+  float sa = 0.0f, sb = 0.0f;
+  bool own_a = on, own_b = on;
+  for (int l = 0; l < K; ++l) {
+    const int al = __builtin_amdgcn_readlane(ia, l);
+    const int bl = __builtin_amdgcn_readlane(ib, l);
+    const float dl = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(ds), l));
+    if (al == ia) {
+      sa += dl;
+      if (l < lane) own_a = false;
+    }
+    if (bl == ib) {
+      sb += dl;
+      if (l < lane) own_b = false;
+    }
+  }
+  wave_sync();
+  if (on && (uint32_t)ia < (uint32_t)n && own_a) r1[ia] = sa;
+  if (on && (uint32_t)ib < (uint32_t)n && own_b) r2[ib] = sb;
+}
+
+// dM0[h] = sum over b of G[b, h], in order b = 0, 1, ...
+__global__ __launch_bounds__(256) void init_bwd_kernel(const float4* __restrict__ G,
+                                                       float4* __restrict__ dM0, int B,
+                                                       int64_t per_seq4, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    float4 acc = G[i];
+    for (int b = 1; b < B; ++b) {
+      const float4 x = G[(int64_t)b * per_seq4 + i];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    dM0[i] = acc;
+  }
+}
+
+int cu_count() {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+    cu = 256;
+  return cu;
+}
+
+}  // namespace
+
+size_t scan_backward_workspace_bytes(int n_mem, int d_v, int64_t T, int W, int R) {
+  const int cols = d_v < 32 ? d_v : 32;
+  return (size_t)n_mem * (size_t)T * (size_t)(d_v / cols) * (size_t)(W + R + 1) * sizeof(float);
+}
+
+hipError_t launch_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W,
+                                int R, const int32_t* widx, const float* wk,
+                                const int32_t* ridx, const float* rw, const float* v,
+                                const float* alpha, const float* beta, const float* tape,
+                                const float* dout, float* G, float* dv, float* dwk, float* drw,
+                                float* dalpha, float* dbeta, float* ws, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int cols = d_v < 32 ? d_v : 32;
+  BwdArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, dout, tape, G, dv, ws,
+            d_v / cols};
+  const int groups = (A.n_mem + 7) / 8;
+  const int64_t blocks = (int64_t)groups * A.ntiles * 8;
+  if (cols == 32)
+    hipLaunchKernelGGL((scan_bwd_kernel<32>), dim3((unsigned)blocks), dim3(kWave), 0, stream, M, A);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<16>), dim3((unsigned)blocks), dim3(kWave), 0, stream, M, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)A.n_mem * T;
+  hipLaunchKernelGGL(scan_bwd_finish, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, A,
+                     dwk, drw, dalpha, dbeta);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_backward(const int32_t* idx, const float* w, const float* dw,
+                                  int64_t units, int n, int K, float* dx1, float* dx2,
+                                  hipStream_t stream) {
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_bwd_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
+                     idx, w, dw, units, n, K, dx1, dx2);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
+                                      float* dM0, hipStream_t stream) {
+  const int64_t n4 = (int64_t)H * N * d_v / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(init_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(G), reinterpret_cast<float4*>(dM0), B, n4,
+                     n4);
+  return hipGetLastError();
+}
+
+}  // namespace sdm

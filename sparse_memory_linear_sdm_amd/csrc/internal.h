@@ -15,12 +15,28 @@ hipError_t launch_state_init(void* M, int dtype, const float* M0, int B, int H, 
 hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W,
                        int R, const int32_t* widx, const float* wk, const int32_t* ridx,
                        const float* rw, const float* v, const float* alpha, const float* beta,
-                       float* out, hipStream_t stream);
+                       float* out, void* tape, hipStream_t stream);
 
 hipError_t launch_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,
                               const float* s1, const float* s2, const float* q1,
                               const float* q2, const float* v, const float* alpha,
                               const float* beta, float* out, int32_t* widx, int32_t* ridx,
                               hipStream_t stream);
+
+size_t scan_backward_workspace_bytes(int n_mem, int d_v, int64_t T, int W, int R);
+
+hipError_t launch_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W,
+                                int R, const int32_t* widx, const float* wk,
+                                const int32_t* ridx, const float* rw, const float* v,
+                                const float* alpha, const float* beta, const float* tape,
+                                const float* dout, float* G, float* dv, float* dwk, float* drw,
+                                float* dalpha, float* dbeta, float* ws, hipStream_t stream);
+
+hipError_t launch_select_backward(const int32_t* idx, const float* w, const float* dw,
+                                  int64_t units, int n, int K, float* dx1, float* dx2,
+                                  hipStream_t stream);
+
+hipError_t launch_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
+                                      float* dM0, hipStream_t stream);
 
 }  // namespace sdm

@@ -129,6 +129,7 @@ struct ScanArgs {
   const float* alpha;
   const float* beta;
   float* out;
+  void* tape;  // training forward: pre-write rows [n_mem, T, W, d_v] in the state type
   int ntiles;
   int shards;  // 1, or 2: rows split between two workgroups by row_shard()
 };
@@ -365,7 +366,7 @@ struct Producer {
 
 // ---------------------------------------------------------------- consumer
 
-template <typename DT, int COLS, int D>
+template <typename DT, int COLS, int D, bool SAVE>
 struct Consumer {
   using TL = Tile<DT, COLS>;
   static constexpr int NI = TL::NI, EPL = TL::EPL, LPR = TL::LPR, RPI = TL::RPI;
@@ -373,6 +374,9 @@ struct Consumer {
   u32x4v wv[D + 1][NI];
   u32x4v rv[D + 1][NI];
   __amdgpu_buffer_rsrc_t mres;  // this memory's tile column, range = the memory slice
+  __amdgpu_buffer_rsrc_t tres;  // SAVE: this memory's tape slice, shifted to the tile column
+  uint32_t tape_step;            // SAVE: bytes of one step's W tape rows
+  uint32_t row_bytes;            // SAVE: bytes of one full row
   uint32_t lane_off;             // lc * 16
   bool accumulate;               // rows split over two workgroups: add into out
 
@@ -464,6 +468,16 @@ struct Consumer {
         if (src) wv[SLOT][k] = lds_u4(sh.upd[(src - 1) >> 6][((src - 1) & 63) * LPR + lc]);
       }
     }
+    if constexpr (SAVE) {  // the pre-write rows, as stored, for the reverse pass
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const uint32_t to = p.wofs[lr * NI + k] == kOffNone
+                                ? kOffNone
+                                : (uint32_t)u * tape_step + (uint32_t)(k * RPI + lr) * row_bytes +
+                                      lane_off;
+        __builtin_amdgcn_raw_buffer_store_b128(wv[SLOT][k], tres, to, 0, 0);
+      }
+    }
     // gated delta write
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
@@ -532,8 +546,8 @@ struct Consumer {
       issue<S>(sh, lr, S, T);
       const u32x4v zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < NI; ++k)  // distinct offsets: identical stores would be merged
-        __builtin_amdgcn_raw_buffer_store_b128(zero, mres, kOffNone + (uint32_t)(S * NI + k) * 16u,
+      for (int k = 0; k < (SAVE ? 2 : 1) * NI; ++k)  // distinct offsets: identical stores would be merged
+        __builtin_amdgcn_raw_buffer_store_b128(zero, mres, kOffNone + (uint32_t)(S * 2 * NI + k) * 16u,
                                                0, 0);
       prologue<S + 1>(sh, lr, T);
     }
@@ -562,7 +576,7 @@ struct Consumer {
   }
 };
 
-template <typename DT, int COLS, int D>
+template <typename DT, int COLS, int D, bool SAVE>
 __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, ScanArgs A) {
   using TL = Tile<DT, COLS>;
   __shared__ ScanShared<DT, COLS, D> sh;
@@ -614,9 +628,18 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   const int d_v = A.d_v;
   DT* const Mm = M + (int64_t)mem * A.N * d_v;
   float* const out_mem = A.out + (int64_t)mem * T * d_v;
-  Consumer<DT, COLS, D> cs;
+  Consumer<DT, COLS, D, SAVE> cs;
   cs.lane_off = (uint32_t)(lc * 16);
   cs.accumulate = A.shards > 1;
+  if constexpr (SAVE) {
+    const int64_t tape_mem = T * A.W * d_v;  // elements of one memory's tape
+    cs.tape_step = (uint32_t)(A.W * d_v * (int)sizeof(DT));
+    cs.row_bytes = (uint32_t)(d_v * (int)sizeof(DT));
+    cs.tres = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<DT*>(A.tape) + (int64_t)mem * tape_mem + (int64_t)tile * COLS, 0,
+        (int)(tape_mem * (int64_t)sizeof(DT) - (int64_t)tile * COLS * (int64_t)sizeof(DT)),
+        kBufWord3);
+  }
   cs.mres = __builtin_amdgcn_make_buffer_rsrc(
       Mm + (int64_t)tile * COLS, 0,
       (int)(A.N * d_v * (int64_t)sizeof(DT) - (int64_t)tile * COLS * (int64_t)sizeof(DT)),
@@ -633,10 +656,11 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <typename DT, int COLS, int D>
+template <typename DT, int COLS, int D, bool SAVE>
 hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
   static_assert(D >= 1 && D <= kChunk, "prefetch depth");
-  static_assert(3 * Tile<DT, COLS>::NI * D <= 63, "outstanding vector memory operations");
+  static_assert((SAVE ? 4 : 3) * Tile<DT, COLS>::NI * D <= 63,
+                "outstanding vector memory operations");
   A.ntiles = A.d_v / COLS;
   const int groups = (A.n_mem + 7) / 8;
   const int64_t blocks = (int64_t)groups * A.shards * A.ntiles * 8;
@@ -646,7 +670,7 @@ hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream,
                        reinterpret_cast<float4*>(A.out), n4);
   }
-  hipLaunchKernelGGL((scan_kernel<DT, COLS, D>), dim3((unsigned)blocks), dim3(2 * kWave), 0,
+  hipLaunchKernelGGL((scan_kernel<DT, COLS, D, SAVE>), dim3((unsigned)blocks), dim3(2 * kWave), 0,
                      stream, reinterpret_cast<DT*>(M), A);
   return hipGetLastError();
 }
@@ -670,9 +694,9 @@ int compute_units() {
 hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W,
                        int R, const int32_t* widx, const float* wk, const int32_t* ridx,
                        const float* rw, const float* v, const float* alpha, const float* beta,
-                       float* out, hipStream_t stream) {
+                       float* out, void* tape, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, 0, 1};
+  ScanArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, out, tape, 0, 1};
   // Tile width and prefetch depth, measured on the mid (64 memories) and
   // long-stream (16 memories) workloads.  Each workgroup walks its steps at a
   // rate set by the latency of a step's gathers, so with few memories the
@@ -688,13 +712,18 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
   const int cus = compute_units();
   const bool narrow = d_v == 16 || (int64_t)A.n_mem * (d_v / 16) <= cus;
   if (narrow && 2 * (int64_t)A.n_mem * (d_v / 16) <= cus) A.shards = 2;
-  if (dtype == 0) {
-    if (!narrow) return launch<float, 32, 1>(M, A, stream);
-    if (A.shards == 2) return launch<float, 16, 3>(M, A, stream);
-    return launch<float, 16, 2>(M, A, stream);
+  if (tape) {  // training forward (fp32 state): also keep the pre-write rows
+    if (!narrow) return launch<float, 32, 1, true>(M, A, stream);
+    if (A.shards == 2) return launch<float, 16, 3, true>(M, A, stream);
+    return launch<float, 16, 2, true>(M, A, stream);
   }
-  if (!narrow) return launch<uint16_t, 32, 1>(M, A, stream);
-  return launch<uint16_t, 16, 3>(M, A, stream);
+  if (dtype == 0) {
+    if (!narrow) return launch<float, 32, 1, false>(M, A, stream);
+    if (A.shards == 2) return launch<float, 16, 3, false>(M, A, stream);
+    return launch<float, 16, 2, false>(M, A, stream);
+  }
+  if (!narrow) return launch<uint16_t, 32, 1, false>(M, A, stream);
+  return launch<uint16_t, 16, 3, false>(M, A, stream);
 }
 
 }  // namespace sdm

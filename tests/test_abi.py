@@ -116,3 +116,43 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sdm, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         sdm.lib()
+
+
+def test_training_calls_validation():
+    L = sdm.lib()
+    # sdm_scan_train: M, B, H, N, d_v, T, W, R, 7 inputs, out, tape, stream
+    ok = [FAKE, 1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 9 + [None]
+    assert L.sdm_scan_train(*ok[:16] + [None, None]) == 1  # tape NULL
+    a = list(ok); a[16] = FAKE + 4
+    assert L.sdm_scan_train(*a) == 1  # tape misaligned
+    a = list(ok); a[5] = 1 << 22; a[4] = 256; a[6] = 64
+    assert L.sdm_scan_train(*a) == 2 and "tape" in _err()  # one memory's tape above 2 GiB
+    need = L.sdm_scan_backward_workspace_size(2, 4, 128, 100, 64, 32)
+    assert need == 2 * 4 * 100 * 4 * (64 + 32 + 1) * 4  # 4 column tiles of 32
+    assert L.sdm_scan_backward_workspace_size(1, 1, 16, 10, 8, 8) == 10 * 1 * 17 * 4
+    assert L.sdm_scan_backward_workspace_size(1, 1, 48, 10, 8, 8) == 0
+    # sdm_scan_backward: M, B, H, N, d_v, T, W, R, 7 inputs, tape, dout, G, dv, dwk, drw,
+    # dalpha, dbeta, workspace, bytes, stream
+    wsb = L.sdm_scan_backward_workspace_size(1, 1, 16, 8, 8, 8)
+    ok = [FAKE, 1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 16 + [wsb, None]
+    assert len(ok) == 26
+    a = list(ok); a[24] = wsb - 4
+    assert L.sdm_scan_backward(*a) == 1 and "workspace" in _err()
+    a = list(ok); a[17] = None  # G
+    assert L.sdm_scan_backward(*a) == 1
+    a = list(ok); a[5] = 1 << 26
+    assert L.sdm_scan_backward(*a) == 2
+    a = list(ok); a[4] = 24
+    assert L.sdm_scan_backward(*a) == 2
+    # sdm_select_backward: idx, w, dw, units, n, K, dx1, dx2, stream
+    ok = [FAKE, FAKE, FAKE, 10, 64, 8, FAKE, FAKE, None]
+    a = list(ok); a[6] = None
+    assert L.sdm_select_backward(*a) == 1
+    a = list(ok); a[5] = 65
+    assert L.sdm_select_backward(*a) == 1
+    a = list(ok); a[4] = 100
+    assert L.sdm_select_backward(*a) == 2
+    # sdm_state_init_backward: G, B, H, N, d_v, dM0, stream
+    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 16, None, None) == 1
+    assert L.sdm_state_init_backward(FAKE, 0, 1, 16, 16, FAKE, None) == 1
+    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 20, FAKE, None) == 2

@@ -1,0 +1,149 @@
+"""GPU parity of the training calls (sdm_scan_train, sdm_scan_backward,
+sdm_select_backward, sdm_state_init_backward) against the CPU oracle.
+
+Bars.  Indices: bit-exact (checked by the forward tests and again here).
+Forward with tape: out and M bitwise equal to sdm_scan; tape within the fp32
+bar of the oracle's pre-write rows.  Rolled-back state: bitwise equal to the
+initial state.  Gradients (fp32 on the GPU, float64 in the oracle):
+normwise per memory, max|x - y| <= 1e-5 * max(1, max|y|).  Each gradient
+element is a sum of at most a few hundred fp32 products per step, carried
+over the steps by factors alpha*(1 - beta*k) <= 1, so its fp32 error stays
+within a few hundred ulps of the tensor's largest element (~1e-5 relative);
+the selection weights themselves differ by ~1e-7 between the sides.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sdm_inputs as S
+from tests.gpu_util import check_selection, host_inputs, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL = 1e-5
+
+
+def _close(g, o, what):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    scale = max(1.0, float(np.abs(o).max()) if o.size else 1.0)
+    err = float(np.abs(g - o).max()) if o.size else 0.0
+    assert err <= GRAD_REL * scale, f"{what}: error {err} vs scale {scale}"
+    return err / scale
+
+
+def _train_case(cfg, seed_g=None, check_mems=None):
+    """Forward with tape, then the reverse pass, on the GPU; every checked
+    memory against the oracle's backward on the oracle's own selections."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    host = host_inputs(cfg)
+    dout = S.host_block(cfg, "dout")
+    M0 = S.host_block(cfg, "M0")
+    dev = to_dev(host)
+    M = sdm.state_init(torch.from_numpy(M0).cuda(), cfg.B)
+    M_start = M.clone()
+    widx, wsc, wk = sdm.select(dev["s1"], dev["s2"], cfg.W)
+    ridx, rsc, rw = sdm.select(dev["q1"], dev["q2"], cfg.R)
+    out, tape = sdm.scan_train(M, widx, wk, ridx, rw, dev["v"], dev["alpha"], dev["beta"])
+    # the same forward without a tape gives the same bits
+    M2 = M_start.clone()
+    out2 = sdm.scan(M2, widx, wk, ridx, rw, dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(M, M2)
+    del M2, out2
+    if seed_g is None:
+        dMT = np.zeros((cfg.B, cfg.H, cfg.N, cfg.d_v), np.float32)
+    else:
+        dMT = np.random.default_rng(seed_g).standard_normal(
+            (cfg.B, cfg.H, cfg.N, cfg.d_v)).astype(np.float32)
+    G = torch.from_numpy(dMT).cuda()
+    gr = sdm.scan_backward(M, widx, wk, ridx, rw, dev["v"], dev["alpha"], dev["beta"], tape,
+                           torch.from_numpy(dout).cuda(), G)
+    dM0 = sdm.state_init_backward(G)
+    torch.cuda.synchronize()
+    assert torch.equal(M, M_start), "the reverse pass must restore the initial state bitwise"
+    gr = {k: v.cpu().numpy() for k, v in gr.items()}
+    Gh = G.cpu().numpy()
+    tape_h = tape.cpu().numpy()
+    gi, gw = widx.cpu().numpy(), wk.cpu().numpy()
+    ri, rwh = ridx.cpu().numpy(), rw.cpu().numpy()
+    mems = check_mems or [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    worst = 0.0
+    for b, h in mems:
+        tag = f"{cfg.name} b={b} h={h}"
+        o_wi, o_ws, o_wk = oracle.select(host["s1"][b, h], host["s2"][b, h], cfg.W, threads=8)
+        o_ri, o_rs, o_rw = oracle.select(host["q1"][b, h], host["q2"][b, h], cfg.R, threads=8)
+        check_selection(gi[b, h], wsc[b, h].cpu().numpy(), gw[b, h], o_wi, o_ws, o_wk, tag + " w")
+        check_selection(ri[b, h], rsc[b, h].cpu().numpy(), rwh[b, h], o_ri, o_rs, o_rw, tag + " r")
+        o = oracle.scan_backward(M0[h], o_wi, o_wk, o_ri, o_rw, host["v"][b, h],
+                                 host["alpha"][b, h], host["beta"][b, h], dout[b, h], dMT[b, h])
+        worst = max(worst, _close(tape_h[b, h], o["tape"], tag + " tape"))
+        for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
+            worst = max(worst, _close(gr[k][b, h], o[k], f"{tag} {k}"))
+        worst = max(worst, _close(Gh[b, h], o["dM0"], tag + " G"))
+    # dM0 = sum over b of G: against the oracle's plain sum of the GPU's G
+    want = oracle.state_init_backward(Gh)
+    _close(dM0.cpu().numpy(), want, "dM0")
+    return worst
+
+
+# (B, H, n, d_v, T, W, R): each picks a different forward variant and tile
+# shape -- 16-column tiles with two row shards (few memories), 16-column
+# tiles unsharded, 32-column tiles (many memories), d_v = 16 (one tile) --
+# with ragged T and W != R.
+CASES = [
+    (1, 2, 16, 16, 77, 8, 5),
+    (2, 2, 32, 64, 130, 32, 32),
+    (3, 7, 16, 128, 45, 16, 9),   # 21 memories: narrow tiles, one shard
+    (5, 8, 64, 128, 33, 13, 64),  # 40 memories: 32-column tiles
+    (1, 3, 64, 128, 60, 64, 64),  # two shards, full 64-row steps
+]
+
+
+@pytest.mark.parametrize("B,H,n,d_v,T,W,R", CASES)
+def test_scan_backward_parity(B, H, n, d_v, T, W, R):
+    cfg = S.CONFIGS["tiny"].with_(B=B, H=H, n=n, d_v=d_v, T=T, W=W, R=R,
+                                  seed=7000 + B * 100 + H * 10 + W)
+    _train_case(cfg, seed_g=B * 1000 + T)
+
+
+def test_scan_backward_dense_reuse():
+    """A tiny table (n = 8, 64 slots) with W = R = 8: rows are re-written and
+    re-read at almost every step, read rows coincide with write rows, and the
+    hashed match table sees collisions."""
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=3, n=8, d_v=32, T=200, W=8, R=8, seed=7777)
+    _train_case(cfg, seed_g=5)
+
+
+def test_scan_backward_small_config_subset():
+    """The small workload's shapes (n = 256, d_v = 64, W = R = 32), all 16
+    memories, first 512 steps, final-state gradient zero (loss on outputs)."""
+    cfg = S.CONFIGS["small"].with_(T=512)
+    _train_case(cfg, seed_g=None, check_mems=[(0, 0), (1, 2), (3, 3)])
+
+
+@pytest.mark.parametrize("n,K,units", [(8, 8, 33), (64, 5, 70), (256, 32, 129), (1024, 64, 300),
+                                       (37, 1, 20)])
+def test_select_backward_parity(n, K, units):
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(n=n, T=units, seed=9100 + n + K)
+    x1, x2 = S.host_block(cfg, "s1")[0, 0], S.host_block(cfg, "s2")[0, 0]
+    dw = np.random.default_rng(n + K).standard_normal((units, K)).astype(np.float32)
+    gi, _, gw = sdm.select(torch.from_numpy(x1).cuda(), torch.from_numpy(x2).cuda(), K)
+    d1, d2 = sdm.select_backward(gi, gw, torch.from_numpy(dw).cuda(), n)
+    torch.cuda.synchronize()
+    oi, _, ow = oracle.select(x1, x2, K, threads=8)
+    assert np.array_equal(gi.cpu().numpy(), oi)
+    o1, o2 = oracle.select_backward(oi, ow, dw, n)
+    _close(d1.cpu().numpy(), o1, "dx1")
+    _close(d2.cpu().numpy(), o2, "dx2")
+    # exact zeros at every half index no selected slot uses
+    used1 = np.zeros((units, n), bool)
+    np.put_along_axis(used1, oi // n, True, axis=1)
+    assert np.all(d1.cpu().numpy()[~used1] == 0.0)

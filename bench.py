@@ -2,7 +2,7 @@
 """Throughput of the Sparse Delta Memory step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config mid]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--train]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: the learned-state copy M[b,h] = M0[h] (sdm_state_init),
@@ -237,6 +237,149 @@ def run_prefill(cfg, args, torch, S, sdm):
     return rec
 
 
+def cpu_baseline_train(cfg, n_mem: int = 8):
+    """The oracle's training pass (selections, then the backward, which
+    replays the forward) on memories (b, 0) for b < n_mem; one per thread."""
+    import numpy as np
+
+    import oracle
+    import sdm_inputs as S
+
+    names = ("s1", "s2", "q1", "q2", "v", "alpha", "beta")
+    nb = min(n_mem, cfg.B)
+    host = {k: S.host_block(cfg, k, 0, nb, 0, 1) for k in names}
+    dout = S.host_block(cfg, "dout", 0, nb, 0, 1)
+    M0 = S.host_block(cfg, "M0", h0=0, nh=1)
+    P = min(workers(), nb)
+
+    def run(b):
+        wi, _, wk = oracle.select(host["s1"][b, 0], host["s2"][b, 0], cfg.W)
+        ri, _, rw = oracle.select(host["q1"][b, 0], host["q2"][b, 0], cfg.R)
+        g = oracle.scan_backward(M0[0], wi, wk, ri, rw, host["v"][b, 0], host["alpha"][b, 0],
+                                 host["beta"][b, 0], dout[b, 0])
+        oracle.select_backward(wi, wk, g["dwk"], cfg.n)
+        oracle.select_backward(ri, rw, g["drw"], cfg.n)
+        return cfg.T
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(P) as ex:
+        head_steps = sum(ex.map(run, range(nb)))
+    dt = time.perf_counter() - t0
+    return {"value": head_steps / cfg.H / dt, "unit": "tokens/s", "cores": P, "kind": "oracle",
+            "sample": f"{nb} of {cfg.B * cfg.H} memories (head 0, sequences 0..{nb - 1}), all "
+                      f"{cfg.T} steps: selections, forward replay, reverse pass and the "
+                      f"selection-weight gradients; {dt:.1f} s wall on {P} threads",
+            "seconds": dt}
+
+
+def run_train(cfg, args, torch, S, sdm):
+    """One training step over one batch: the forward (state init, two
+    selections beside it, the scan keeping its tape) and the reverse pass
+    (gradient table zeroed -- the loss reads the outputs only --, the reverse
+    scan, both selection-weight gradients to the halves, and the M0
+    gradient)."""
+    dev = torch.device("cuda:0")
+    B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
+    if args.state != "f32":
+        raise SystemExit("--train runs on fp32 state only")
+    print(f"[bench] {cfg.name} training step: B{B} H{H} n{n} N={N} d_v{d_v} T{T} W{W} R{R}; "
+          f"generating inputs on the GPU", file=sys.stderr, flush=True)
+    f32 = torch.float32
+    inp = {k: torch.empty((B, H, T, n), dtype=f32, device=dev) for k in ("s1", "s2", "q1", "q2")}
+    inp["v"] = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
+    inp["dout"] = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
+    inp["alpha"] = torch.empty((B, H, T), dtype=f32, device=dev)
+    inp["beta"] = torch.empty((B, H, T), dtype=f32, device=dev)
+    for k, t in inp.items():
+        S.device_block(cfg, k, t)
+    M0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
+    S.device_block(cfg, "M0", M0)
+    M = torch.empty((B, H, N, d_v), dtype=f32, device=dev)
+    G = torch.empty((B, H, N, d_v), dtype=f32, device=dev)
+    dM0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
+    tape = torch.empty((B, H, T, W, d_v), dtype=f32, device=dev)
+    widx = torch.empty((B, H, T, W), dtype=torch.int32, device=dev)
+    wk = torch.empty((B, H, T, W), dtype=f32, device=dev)
+    ridx = torch.empty((B, H, T, R), dtype=torch.int32, device=dev)
+    rw = torch.empty((B, H, T, R), dtype=f32, device=dev)
+    out = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
+    wsb = int(sdm.lib().sdm_scan_backward_workspace_size(B, H, d_v, T, W, R))
+    ws = torch.empty((wsb + 3) // 4, dtype=f32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    x = {"v": inp["v"], "alpha": inp["alpha"], "beta": inp["beta"]}
+
+    def step(record=None):
+        e = [ev() for _ in range(12)]
+        e[0].record(stream)
+        side.wait_event(e[0])
+        sdm.state_init(M0, B, out=M, stream=stream)
+        e[1].record(stream)
+        e[2].record(side)
+        sdm.select(inp["s1"], inp["s2"], W, out=(widx, None, wk), stream=side)
+        sdm.select(inp["q1"], inp["q2"], R, out=(ridx, None, rw), stream=side)
+        e[3].record(side)
+        stream.wait_event(e[3])
+        e[4].record(stream)
+        sdm.scan_train(M, widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], out=out,
+                       tape=tape, stream=stream)
+        e[5].record(stream)
+        G.zero_()
+        e[6].record(stream)
+        g = sdm.scan_backward(M, widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], tape,
+                              inp["dout"], G, workspace=ws, stream=stream)
+        e[7].record(stream)
+        sdm.select_backward(widx, wk, g["dwk"], n, stream=stream)
+        sdm.select_backward(ridx, rw, g["drw"], n, stream=stream)
+        e[8].record(stream)
+        sdm.state_init_backward(G, out=dM0, stream=stream)
+        e[9].record(stream)
+        if record is not None:
+            record.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    g0, g1 = ev(), ev()
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(recs)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = g0.elapsed_time(g1) / args.steps
+    avg = lambda a, b: sum(r[a].elapsed_time(r[b]) for r in recs) / args.steps  # noqa: E731
+    bd = {"state_init": avg(0, 1), "select_write_read": avg(2, 3), "scan_train": avg(4, 5),
+          "zero_G": avg(5, 6), "scan_backward": avg(6, 7), "select_backward": avg(7, 8),
+          "state_init_backward": avg(8, 9), "overlap": "select || state_init"}
+    bwd_bytes = B * H * T * (4 * W + 3 * R) * d_v * 4
+    fwd_bytes = B * H * T * (3 * W + R) * d_v * 4
+    gbps = bwd_bytes / (bd["scan_backward"] * 1e-3) / 1e9
+    workload = (f"{cfg.name} training step: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
+                f"f32 state")
+    roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": "scan_bwd_kernel<32> + scan_bwd_finish",
+                "algorithmic_bytes_per_launch": bwd_bytes}
+    extra = {"breakdown_ms": bd, "wall_s": wall,
+             "scan_train_GBps": fwd_bytes / (bd["scan_train"] * 1e-3) / 1e9,
+             "backward_tokens_per_s": B * T / (bd["scan_backward"] * 1e-3)}
+    rec = _common_record(cfg, args, B * T / (ms_step * 1e-3), "tokens/s", ms_step, "f32",
+                         workload, roofline, extra)
+    rec["metric"] = METRIC + " (training step: forward + reverse pass)"
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle's training pass on a bounded sample",
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_train(cfg)
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
 def run_decode(cfg, args, torch, S, sdm):
     """One step = the T single-token calls of one batch of sequences
     (sdm_step_decode on every (b,h)); the state is initialised once before the
@@ -425,6 +568,8 @@ def main():
                     help="mid (default, the headline), small, decode or long")
     ap.add_argument("--state", default=None, help="f32 or bf16 (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step (forward with tape + reverse pass) instead")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the step's kernels back to back on one stream")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -450,7 +595,9 @@ def main():
     cfg = S.CONFIGS[args.config]
     if args.state is None:
         args.state = cfg.state
-    if cfg.decode:
+    if args.train:
+        rec = run_train(cfg, args, torch, S, sdm)
+    elif cfg.decode:
         rec = run_decode(cfg, args, torch, S, sdm)
     elif cfg.name == "long":
         rec = run_long(cfg, args, torch, S, sdm)

@@ -148,26 +148,49 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
   float* wsm = A.ws + ((int64_t)mem * T * A.ntiles + tile) * ws_row;
   wave_sync();
 
-  for (int64_t t = T - 1; t >= 0; --t) {
-    // ---- this step's plan
-    uint32_t wrow[NI], wo[NI], ro[NI], to[NI];
-    float wkk[NI], rwk[NI];
+  // Step metadata travels one step ahead: during step t the lanes load step
+  // t-1's indices, weights, values and gates in "lane j = slot j" layout;
+  // after step t they pass through LDS into the per-row layout the gathers
+  // use, so a step's gathers are issued without waiting on its metadata.
+  __shared__ int32_t sm_w[64], sm_r[64];
+  __shared__ float sm_wk[64], sm_rw[64];
+  __shared__ f32x4 sm_v[LPR], sm_d[LPR];
+  int32_t fw_[NI], fr_[NI];
+  float wkk[NI], rwk[NI];
+  f32x4 vv, dd;
+  float a, b;
+  int32_t my_r;
+  float my_rw;
+  {  // step T-1 directly
+    const int64_t t = T - 1;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int j = k * RPI + lr;
-      const int32_t fw = j < W ? widx[t * W + j] : -1;
-      const int32_t fr = j < R ? ridx[t * R + j] : -1;
-      const bool wv = (uint32_t)fw < (uint32_t)N, rv = (uint32_t)fr < (uint32_t)N;
-      wrow[k] = wv ? (uint32_t)fw : 0xFFFFFFFFu;
-      wo[k] = wv ? (uint32_t)fw * row_bytes + lane_off : kOffNone;
-      ro[k] = rv ? (uint32_t)fr * row_bytes + lane_off : kOffNone;
-      to[k] = wv ? ((uint32_t)t * (uint32_t)W + (uint32_t)j) * row_bytes + lane_off : kOffNone;
+      fw_[k] = j < W ? widx[t * W + j] : -1;
+      fr_[k] = j < R ? ridx[t * R + j] : -1;
       wkk[k] = j < W ? wk[t * W + j] : 0.0f;
       rwk[k] = j < R ? rw[t * R + j] : 0.0f;
     }
-    const f32x4 vv = *reinterpret_cast<const f32x4*>(vm + t * d_v);
-    const f32x4 dd = *reinterpret_cast<const f32x4*>(dom + t * d_v);
-    const float a = am[t], b = bm[t];
+    vv = *reinterpret_cast<const f32x4*>(vm + t * d_v);
+    dd = *reinterpret_cast<const f32x4*>(dom + t * d_v);
+    a = am[t];
+    b = bm[t];
+    my_r = lane < R ? ridx[t * R + lane] : -1;
+    my_rw = lane < R ? rw[t * R + lane] : 0.0f;
+  }
+
+  for (int64_t t = T - 1; t >= 0; --t) {
+    // ---- this step's offsets
+    uint32_t wrow[NI], wo[NI], ro[NI], to[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int j = k * RPI + lr;
+      const bool wv = (uint32_t)fw_[k] < (uint32_t)N, rv = (uint32_t)fr_[k] < (uint32_t)N;
+      wrow[k] = wv ? (uint32_t)fw_[k] : 0xFFFFFFFFu;
+      wo[k] = wv ? (uint32_t)fw_[k] * row_bytes + lane_off : kOffNone;
+      ro[k] = rv ? (uint32_t)fr_[k] * row_bytes + lane_off : kOffNone;
+      to[k] = wv ? ((uint32_t)t * (uint32_t)W + (uint32_t)j) * row_bytes + lane_off : kOffNone;
+    }
 
     // ---- gathers (all issued before any is used)
     u32x4 Mg[NI], Gg[NI], Gf[NI], P[NI];
@@ -180,15 +203,25 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
 #pragma unroll
     for (int k = 0; k < NI; ++k) P[k] = __builtin_amdgcn_raw_buffer_load_b128(tres, to[k], 0, 0);
 
+    // ---- step t-1's metadata, in flight with the gathers
+    const int64_t tn = t > 0 ? t - 1 : 0;
+    const int32_t n_w = lane < W ? widx[tn * W + lane] : -1;
+    const float n_wk = lane < W ? wk[tn * W + lane] : 0.0f;
+    const int32_t n_r = lane < R ? ridx[tn * R + lane] : -1;
+    const float n_rw = lane < R ? rw[tn * R + lane] : 0.0f;
+    const int lv = lane < LPR ? lane : 0;
+    const f32x4 n_v = *reinterpret_cast<const f32x4*>(vm - lc * 4 + lv * 4 + tn * d_v);
+    const f32x4 n_d = *reinterpret_cast<const f32x4*>(dom - lc * 4 + lv * 4 + tn * d_v);
+    const float n_a = am[tn], n_b = bm[tn];
+
     // ---- match write rows to this step's read rows while the gathers fly.
     // Lane j inserts read slot j; a read row whose table entry was taken by
     // another read row of the step (hash collision) is matched by a
     // wave-uniform loop instead.  Entries of other steps carry another stamp.
-    const int32_t my_r = lane < R ? ridx[t * R + lane] : -1;
     const bool my_valid = (uint32_t)my_r < (uint32_t)N;
     const uint32_t stamp = ((uint32_t)t << 6) | (uint32_t)lane;
     const uint64_t entry = ((uint64_t)(uint32_t)my_r << 32) | stamp;
-    rws[lane] = lane < R ? rw[t * R + lane] : 0.0f;
+    rws[lane] = my_rw;
     if (my_valid) tab[hash_slot((uint32_t)my_r)] = entry;
     wave_sync();
     const bool lost = my_valid && tab[hash_slot((uint32_t)my_r)] != entry;
@@ -277,7 +310,32 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
     if (lr == 0) *reinterpret_cast<f32x4*>(dvm + t * d_v) = dva;
     const float da = wave_sum_f32(dap);
     if (lane == 0) wst[W + R] = da;
-    wave_sync();  // rws and tab are rewritten by the next step
+
+    // ---- step t-1's metadata into the per-row layout
+    sm_w[lane] = n_w;
+    sm_r[lane] = n_r;
+    sm_wk[lane] = n_wk;
+    sm_rw[lane] = n_rw;
+    if (lane < LPR) {
+      sm_v[lane] = n_v;
+      sm_d[lane] = n_d;
+    }
+    wave_sync();
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int j = k * RPI + lr;
+      fw_[k] = sm_w[j];
+      fr_[k] = sm_r[j];
+      wkk[k] = sm_wk[j];
+      rwk[k] = sm_rw[j];
+    }
+    vv = sm_v[lc];
+    dd = sm_d[lc];
+    a = n_a;
+    b = n_b;
+    my_r = n_r;
+    my_rw = n_rw;
+    wave_sync();  // the LDS staging, rws and tab are rewritten by the next step
   }
 }
 

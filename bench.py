@@ -36,27 +36,29 @@ sys.path.insert(0, ROOT)
 METRIC = "SDM scan tokens/sec + slot-traffic HBM GB/s (% of peak), N=2^20, d_v=128"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_traffic.json")
-SCAN_SOURCES = [os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc", f)
-                for f in ("scan.hip", "device_common.h")]
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_bwd_mid_traffic.json")
+_CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
+SCAN_SOURCES = [os.path.join(_CSRC, f) for f in ("scan.hip", "device_common.h")]
+BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "device_common.h")]
 
 
-def scan_source_sha() -> str:
+def scan_source_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for f in SCAN_SOURCES:
+    for f in sources or SCAN_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(n_launch_bytes: float):
-    """HBM bytes per scan launch from the committed counter summary, or None
-    when there is none or the scan kernel has changed since it was taken."""
+def measured_traffic(n_launch_bytes: float, path=TRAFFIC_FILE, sources=None):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none or the kernel's sources have changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha") != scan_source_sha():
+    if rec.get("source_sha") != scan_source_sha(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -123,6 +125,19 @@ def _common_record(cfg, args, value, unit, ms_step, dtype, workload, roofline, e
     return rec
 
 
+def calibration_copy(args, torch, dev):
+    """One plain device copy of --calib-copy-mib MiB: a kernel of known
+    traffic for scaling the HBM byte counters of the same run."""
+    if args.calib_copy_mib > 0:
+        nelem = args.calib_copy_mib * (1 << 20) // 4
+        csrc = torch.ones(nelem, dtype=torch.float32, device=dev)
+        cdst = torch.empty_like(csrc)
+        torch.cuda.synchronize()
+        cdst.copy_(csrc)
+        torch.cuda.synchronize()
+        del csrc, cdst
+
+
 def run_prefill(cfg, args, torch, S, sdm):
     """One step = state init + two selections + the T-step scan over the whole
     [B, H, T] batch (the headline workload)."""
@@ -151,14 +166,7 @@ def run_prefill(cfg, args, torch, S, sdm):
     out = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
     torch.cuda.synchronize()
 
-    if args.calib_copy_mib > 0:
-        nelem = args.calib_copy_mib * (1 << 20) // 4
-        csrc = torch.ones(nelem, dtype=f32, device=dev)
-        cdst = torch.empty_like(csrc)
-        torch.cuda.synchronize()
-        cdst.copy_(csrc)
-        torch.cuda.synchronize()
-        del csrc, cdst
+    calibration_copy(args, torch, dev)
 
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()  # default priority
@@ -306,6 +314,7 @@ def run_train(cfg, args, torch, S, sdm):
     wsb = int(sdm.lib().sdm_scan_backward_workspace_size(B, H, d_v, T, W, R))
     ws = torch.empty((wsb + 3) // 4, dtype=f32, device=dev)
     torch.cuda.synchronize()
+    calibration_copy(args, torch, dev)
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()  # default priority
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -361,8 +370,10 @@ def run_train(cfg, args, torch, S, sdm):
     gbps = bwd_bytes / (bd["scan_backward"] * 1e-3) / 1e9
     workload = (f"{cfg.name} training step: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
                 f"f32 state")
+    traffic = (measured_traffic(bwd_bytes, BWD_TRAFFIC_FILE, BWD_SOURCES)
+               if cfg.name == "mid" else None)
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": "scan_bwd_kernel<32> + scan_bwd_finish",
                 "algorithmic_bytes_per_launch": bwd_bytes}
     extra = {"breakdown_ms": bd, "wall_s": wall,

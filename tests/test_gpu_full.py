@@ -149,6 +149,68 @@ def test_mid_config_full_size():
     _free()
 
 
+def test_mid_config_training_full_size():
+    """The training step of the mid workload in the benchmark's launch
+    configuration (64 memories of 2^20 x 128, T = 4096, gradient table
+    zeroed, loss on the outputs): two memories' gradients checked in full
+    against the oracle's reverse pass, the state rolled back bitwise to M0
+    for every memory, and dM0 against the plain sum of the GPU's G."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["mid"]
+    B, H, T = cfg.B, cfg.H, cfg.T
+    d = _dev_inputs(cfg)
+    dout = torch.empty((B, H, T, cfg.d_v), dtype=torch.float32, device="cuda")
+    S.device_block(cfg, "dout", dout)
+    M0 = torch.empty((H, cfg.N, cfg.d_v), dtype=torch.float32, device="cuda")
+    S.device_block(cfg, "M0", M0)
+    M = sdm.state_init(M0, B)
+    widx, _, wk = sdm.select(d["s1"], d["s2"], cfg.W)
+    ridx, _, rw = sdm.select(d["q1"], d["q2"], cfg.R)
+    out, tape = sdm.scan_train(M, widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"])
+    G = torch.zeros_like(M)
+    gr = sdm.scan_backward(M, widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"], tape, dout, G)
+    del tape
+    dM0 = sdm.state_init_backward(G)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            assert torch.equal(M[b, h], M0[h]), f"state of b={b} h={h} not restored"
+    for b, h in ((0, 0), (6, 3)):
+        host = host_inputs(cfg, b, 1, h, 1)
+        M0h = S.host_block(cfg, "M0", h0=h, nh=1)[0]
+        wi, _, wkk = oracle.select(host["s1"][0, 0], host["s2"][0, 0], cfg.W, threads=16)
+        ri, _, rww = oracle.select(host["q1"][0, 0], host["q2"][0, 0], cfg.R, threads=16)
+        assert np.array_equal(widx[b, h].cpu().numpy(), wi)
+        assert np.array_equal(ridx[b, h].cpu().numpy(), ri)
+        o = oracle.scan_backward(M0h, wi, wkk, ri, rww, host["v"][0, 0], host["alpha"][0, 0],
+                                 host["beta"][0, 0], S.host_block(cfg, "dout", b, 1, h, 1)[0, 0])
+        tag = f"mid training b={b} h={h}"
+        check_values(out[b, h].cpu().numpy(), oracle.scan(
+            M0h.copy(), F32, wi, wkk, ri, rww, host["v"][0, 0], host["alpha"][0, 0],
+            host["beta"][0, 0]), F32, tag + " out")
+        for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
+            _grad_close(gr[k][b, h].cpu().numpy(), o[k], f"{tag} {k}")
+        _grad_close(G[b, h].cpu().numpy(), o["dM0"], tag + " G")
+        del o
+    for h in (0, 5):
+        want = oracle.state_init_backward(G[:, h:h + 1].cpu().numpy())[0]
+        _grad_close(dM0[h].cpu().numpy(), want, f"dM0 h={h}")
+    del d, dout, M0, M, G, gr, dM0, widx, wk, ridx, rw, out
+    _free()
+
+
+def _grad_close(g, o, what):
+    """Gradient bar: normwise per tensor, max|x - y| <= 1e-5 * max(1, max|y|)."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    scale = max(1.0, float(np.abs(o).max()))
+    err = float(np.abs(g - o).max())
+    assert err <= 1e-5 * scale, f"{what}: error {err} vs scale {scale}"
+
+
 def test_decode_config_full_size():
     """64 x 4 memories of 2^20 x 128 bf16 (64 GiB), 512 single-token calls;
     two memories checked against the oracle over all 512 steps."""

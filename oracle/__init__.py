@@ -17,7 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(_HERE, "liboracle.so")
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 _lib = None
 
 
@@ -52,6 +52,10 @@ def _L():
         lib.oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_fp8_from_float.argtypes = [ctypes.c_float]
+        lib.oracle_fp8_from_float.restype = ctypes.c_uint8
+        lib.oracle_fp8_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_to_double.restype = ctypes.c_double
         for f in ("oracle_select", "oracle_state_init", "oracle_scan", "oracle_step_decode",
                   "oracle_scan_backward", "oracle_select_backward"):
             getattr(lib, f).restype = ctypes.c_int
@@ -118,11 +122,15 @@ def select(x1, x2, K: int, threads: int = 1):
     return idx, score, weight
 
 
+_STATE_NP = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
+
+
 def state_init(M0, B: int, dtype: int = F32):
-    """M [B,H,N,d_v] (float32, or uint16 bf16 bits) from M0 [H,N,d_v]."""
+    """M [B,H,N,d_v] (float32, uint16 bf16 bits or uint8 fp8 codes) from
+    M0 [H,N,d_v]."""
     M0 = _c(M0, np.float32)
     H, N, d_v = M0.shape
-    M = np.empty((B, H, N, d_v), np.float32 if dtype == F32 else np.uint16)
+    M = np.empty((B, H, N, d_v), _STATE_NP[dtype])
     _check(_L().oracle_state_init(_ptr(M), dtype, _ptr(M0), B, H, N, d_v))
     return M
 
@@ -132,7 +140,7 @@ def scan(M, dtype, widx, wk, ridx, rw, v, alpha, beta, cols=None, out=None):
     cols = (c0, c1) restricts the computed columns."""
     N, d_v = M.shape
     assert M.flags.c_contiguous
-    assert M.dtype == (np.float32 if dtype == F32 else np.uint16)
+    assert M.dtype == _STATE_NP[dtype]
     widx, ridx = _c(widx, np.int32), _c(ridx, np.int32)
     wk, rw = _c(wk, np.float64), _c(rw, np.float64)
     v = _c(v, np.float32)
@@ -229,6 +237,21 @@ def bf16_from_double(x: float) -> int:
 
 def bf16_to_double(h: int) -> float:
     return float(_L().oracle_bf16_to_double(int(h)))
+
+
+def fp8_from_float(x: float) -> int:
+    return int(_L().oracle_fp8_from_float(float(x)))
+
+
+def fp8_to_double(c: int) -> float:
+    return float(_L().oracle_fp8_to_double(int(c)))
+
+
+def fp8_codes_to_f32(a) -> np.ndarray:
+    """Decode uint8 E4M3 codes to float32 (exact) with the oracle's decoder."""
+    a = np.asarray(a, np.uint8)
+    table = np.array([fp8_to_double(c) for c in range(256)], np.float64).astype(np.float32)
+    return table[a]
 
 
 def bf16_bits_to_f32(a) -> np.ndarray:

@@ -35,7 +35,11 @@
  *    rows, taken from the stored memory after this step's write.
  *    Accumulated in double, rounded once to fp32.
  *  - Learned initial state: every sequence's memory starts as a copy of M0
- *    (fp32; rounded to bf16 with round-to-nearest-even for bf16 state).
+ *    (fp32; rounded to bf16 with round-to-nearest-even for bf16 state, to
+ *    fp8 E4M3 likewise for fp8 state).
+ *  - fp8 E4M3 state: the stored code is decided by the binary32 update, so
+ *    for that state type the write is taken in binary32 in a fixed order
+ *    (see oracle_scan) and then rounded to E4M3.
  *
  * All inputs must be finite; the functions return a non-zero status and set
  * a message otherwise.  Plain, slow and single-threaded on purpose.
@@ -80,6 +84,38 @@ static uint16_t bf16_from_double(double x) {
   uint32_t b;
   memcpy(&b, &f, 4);
   return (uint16_t)(b >> 16);
+}
+
+/* ------------------------------------------------------------------ fp8
+ * OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities; codes 0x7F and 0xFF are NaN; largest finite
+ * value 448 = 1.75 * 2^8; normal values from 2^-6, subnormals m * 2^-9 for
+ * m = 1..7.  Encoding rounds to the nearest representable value, ties to the
+ * even code, and clamps magnitudes beyond 448 to 448 (a finite state never
+ * needs more: every write is a convex combination of alpha*M and v). */
+
+static double fp8_to_double(uint8_t c) {
+  int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return sgn ? -mag : mag;
+}
+
+static uint8_t fp8_from_float(float x) {
+  uint8_t sgn = signbit(x) ? 0x80u : 0x00u;
+  double a = fabs((double)x);
+  if (a == 0.0) return sgn;
+  int e;
+  (void)frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int q = e - 4;      /* spacing of 3-mantissa-bit values in that binade */
+  if (q < -9) q = -9; /* subnormal spacing */
+  double r = ldexp(nearbyint(ldexp(a, -q)), q); /* exact scaling; rint is ties-to-even */
+  if (r > 448.0) r = 448.0;
+  if (r < ldexp(1.0, -6)) return (uint8_t)(sgn | (uint8_t)ldexp(r, 9));
+  int er;
+  double fr = frexp(r, &er); /* r = fr * 2^er, fr in [0.5, 1) */
+  int E = er - 1 + 7;
+  int M = (int)ldexp(fr * 2.0 - 1.0, 3);
+  return (uint8_t)(sgn | (uint8_t)(E << 3) | (uint8_t)M);
 }
 
 /* ------------------------------------------------------------- selection */
@@ -181,11 +217,12 @@ int oracle_select(const float* x1, const float* x2, int64_t units, int n, int K,
 
 /* ----------------------------------------------------------------- state */
 
-/* M[b,h] = M0[h] for all b.  dtype 0: fp32 copy; 1: bf16, nearest even.
- * M [B,H,N,d_v] (float or uint16), M0 [H,N,d_v] float. */
+/* M[b,h] = M0[h] for all b.  dtype 0: fp32 copy; 1: bf16, nearest even;
+ * 2: fp8 E4M3, nearest even.  M [B,H,N,d_v] (float, uint16 or uint8),
+ * M0 [H,N,d_v] float. */
 int oracle_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N, int d_v) {
   if (!M || !M0) return fail("null pointer");
-  if (B < 1 || H < 1 || N < 1 || d_v < 1 || (dtype != 0 && dtype != 1)) return fail("bad sizes");
+  if (B < 1 || H < 1 || N < 1 || d_v < 1 || dtype < 0 || dtype > 2) return fail("bad sizes");
   int64_t per = N * d_v;
   if (!all_finite(M0, per * H)) return fail("non-finite M0");
   for (int b = 0; b < B; ++b)
@@ -194,9 +231,12 @@ int oracle_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t
       int64_t off = ((int64_t)b * H + h) * per;
       if (dtype == 0) {
         memcpy((float*)M + off, src, sizeof(float) * (size_t)per);
-      } else {
+      } else if (dtype == 1) {
         uint16_t* dst = (uint16_t*)M + off;
         for (int64_t i = 0; i < per; ++i) dst[i] = bf16_from_double((double)src[i]);
+      } else {
+        uint8_t* dst = (uint8_t*)M + off;
+        for (int64_t i = 0; i < per; ++i) dst[i] = fp8_from_float(src[i]);
       }
     }
   return 0;
@@ -204,7 +244,8 @@ int oracle_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t
 
 static double load_elem(const void* M, int dtype, int64_t pos) {
   if (dtype == 0) return (double)((const float*)M)[pos];
-  return bf16_to_double(((const uint16_t*)M)[pos]);
+  if (dtype == 1) return bf16_to_double(((const uint16_t*)M)[pos]);
+  return fp8_to_double(((const uint8_t*)M)[pos]);
 }
 
 static void store_elem(void* M, int dtype, int64_t pos, double val) {
@@ -223,7 +264,7 @@ int oracle_scan(void* M, int dtype, int64_t N, int d_v, int64_t T, int W, int R,
                 int c1) {
   if (!M || !widx || !wk || !ridx || !rw || !v || !alpha || !beta || !out)
     return fail("null pointer");
-  if (N < 1 || d_v < 1 || T < 0 || W < 1 || R < 1 || (dtype != 0 && dtype != 1))
+  if (N < 1 || d_v < 1 || T < 0 || W < 1 || R < 1 || dtype < 0 || dtype > 2)
     return fail("bad sizes");
   if (c0 < 0 || c1 > d_v || c0 > c1) return fail("bad column range");
   for (int64_t t = 0; t < T; ++t) {
@@ -246,6 +287,19 @@ int oracle_scan(void* M, int dtype, int64_t N, int d_v, int64_t T, int W, int R,
       double k = wk[t * W + j];
       for (int c = c0; c < c1; ++c) {
         double m = load_elem(M, dtype, row + c);
+        if (dtype == 2) {
+          /* fp8 state: the stored code is decided by the binary32 update,
+           * taken in this order -- Mt = alpha*m; d = v - Mt;
+           * u = fma(beta*k, d, Mt) -- with each operation rounded to
+           * binary32, then rounded once more to E4M3.  The weight k must be
+           * a binary32 value for this to be the same computation on any
+           * implementation. */
+          float mt = (float)alpha[t] * (float)m;
+          float d = vt[c] - mt;
+          float g = beta[t] * (float)k;
+          ((uint8_t*)M)[row + c] = fp8_from_float(fmaf(g, d, mt));
+          continue;
+        }
         double mt = a * m;
         double u = mt + be * k * ((double)vt[c] - mt);
         store_elem(M, dtype, row + c, u);
@@ -439,6 +493,8 @@ int oracle_select_backward(const int32_t* idx, const double* w, const double* dw
   return 0;
 }
 
-/* bf16 helpers exposed for the tests of the oracle itself. */
+/* bf16 and fp8 helpers exposed for the tests of the oracle itself. */
 uint16_t oracle_bf16_from_double(double x) { return bf16_from_double(x); }
 double oracle_bf16_to_double(uint16_t h) { return bf16_to_double(h); }
+uint8_t oracle_fp8_from_float(float x) { return fp8_from_float(x); }
+double oracle_fp8_to_double(uint8_t c) { return fp8_to_double(c); }

@@ -143,8 +143,8 @@ def run_prefill(cfg, args, torch, S, sdm):
     [B, H, T] batch (the headline workload)."""
     dev = torch.device("cuda:0")
     B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
-    sdt = torch.float32 if args.state == "f32" else torch.bfloat16
-    es = 4 if args.state == "f32" else 2
+    sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[args.state]
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[args.state]
     print(f"[bench] {cfg.name}: B{B} H{H} n{n} N={N} d_v{d_v} T{T} W{W} R{R} {args.state} "
           f"state; generating inputs on the GPU", file=sys.stderr, flush=True)
     f32 = torch.float32
@@ -221,7 +221,8 @@ def run_prefill(cfg, args, torch, S, sdm):
     tokens_per_step = B * T
     slot_bytes = B * H * T * (2 * W + R) * d_v * es  # algorithmic, one scan launch
     scan_gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
-    kname = "scan_kernel<float,32,1>" if es == 4 else "scan_kernel<uint16_t(bf16),32,1>"
+    kname = {4: "scan_kernel<float,32,1>", 2: "scan_kernel<uint16_t(bf16),32,1>",
+             1: "scan_kernel<fp8e4m3,32,1>"}[es]
     traffic = measured_traffic(slot_bytes) if (cfg.name == "mid" and es == 4) else None
     workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
                 f"{args.state} state")
@@ -235,8 +236,8 @@ def run_prefill(cfg, args, torch, S, sdm):
              "scan_tokens_per_s": tokens_per_step / (scan_ms * 1e-3),
              "wall_s": wall}
     rec = _common_record(cfg, args, tokens_per_step / (ms_step * 1e-3), "tokens/s", ms_step,
-                         "f32" if es == 4 else "f32 math, bf16 state", workload, roofline,
-                         extra)
+                         {4: "f32", 2: "f32 math, bf16 state", 1: "f32 math, fp8 e4m3 state"}[es],
+                         workload, roofline, extra)
     if not args.no_cpu_baseline and es == 4:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg)
@@ -577,7 +578,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="mid",
                     help="mid (default, the headline), small, decode or long")
-    ap.add_argument("--state", default=None, help="f32 or bf16 (default: the config's)")
+    ap.add_argument("--state", default=None,
+                    help="f32, bf16 or fp8 (E4M3) (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (forward with tape + reverse pass) instead")

@@ -41,7 +41,12 @@
  *   - Supported shapes: n in 1..64 or n in {128, 256, 512, 1024, 2048};
  *     1 <= K, W, R <= min(n, 64); d_v in {16, 32, 64, 128, 256};
  *     state dtype SDM_F32 or SDM_BF16 (bf16 state uses fp32 arithmetic and
- *     rounds to nearest even on store).  Pointers to M, M0 and v must be
+ *     rounds to nearest even on store), or SDM_FP8 for sdm_state_init and
+ *     sdm_scan with d_v >= 32: OCP FP8 E4M3 codes ("e4m3fn", bias 7, largest
+ *     finite 448), fp32 arithmetic, rounded to nearest even on store; the
+ *     write is then evaluated in a fixed binary32 order with no contraction
+ *     -- Mt = alpha*M, d = v - Mt, M = fma(beta*k, d, Mt) -- so the stored
+ *     codes are a function of the binary32 inputs alone.  Pointers to M, M0 and v must be
  *     16-byte aligned; sub-score pointers must be 16-byte aligned when
  *     n >= 256 and 4-byte aligned otherwise.
  *   - Calls on different streams are independent as long as they do not
@@ -58,7 +63,7 @@ extern "C" {
 #endif
 
 enum { SDM_OK = 0, SDM_ERR_INVALID = 1, SDM_ERR_UNSUPPORTED = 2, SDM_ERR_HIP = 3 };
-enum { SDM_F32 = 0, SDM_BF16 = 1 };
+enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8 = 2 };
 
 /* Product-key top-K selection with softmax weights ("Meccanismo Core",
  * item 2), for `units` independent (key or query) half pairs.
@@ -77,15 +82,16 @@ int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, in
 
 /* Learned initial state ("Stato Iniziale Appreso"): M[b,h] = M0[h] for every
  * batch row b.
- *   M   [B, H, N, d_v] out, fp32 (dtype SDM_F32) or bf16 bits (SDM_BF16,
- *       rounded to nearest even).
+ *   M   [B, H, N, d_v] out, fp32 (dtype SDM_F32), bf16 bits (SDM_BF16) or
+ *       E4M3 codes (SDM_FP8), the last two rounded to nearest even.
  *   M0  [H, N, d_v] fp32 in. */
 int sdm_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N, int d_v,
                    void* stream);
 
 /* T sequential steps of the gated delta write and the sparse read
  * ("Meccanismo Core", items 3 and 4) on every (b,h) memory, in place.
- *   M       [B, H, N, d_v] state (fp32 or bf16 bits), updated in place.
+ *   M       [B, H, N, d_v] state (fp32, bf16 bits or fp8 E4M3 codes),
+ *           updated in place.
  *   widx    [B, H, T, W] int32 write rows of each step (as sdm_select
  *           returns them); the W rows of one step must be distinct.
  *   wk      [B, H, T, W] fp32 write weights k.
@@ -93,7 +99,7 @@ int sdm_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N,
  *   v       [B, H, T, d_v] fp32 values;  alpha, beta [B, H, T] fp32 gates.
  *   out     [B, H, T, d_v] fp32 out: o_t = sum_j rw_j * M_t[ridx_j], read
  *           from the state after step t's write (as stored, i.e. after the
- *           bf16 rounding for bf16 state).
+ *           bf16 or fp8 rounding).
  * Per step and row: Mt = alpha*M; M = Mt + (beta*k)*(v - Mt), in fp32.
  * Rows not selected for writing are never touched.  Row indices outside
  * [0, N) are skipped (no access; a skipped read row contributes 0); repeated

@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(HERE, "libsdm.so")
 
 SDM_F32 = 0
 SDM_BF16 = 1
+SDM_FP8 = 2
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_INVALID", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_HIP"}
 
 # Every symbol include/sdm.h declares.
@@ -114,7 +115,9 @@ def _state_dtype(M):
         return SDM_F32
     if M.dtype == torch.bfloat16:
         return SDM_BF16
-    raise ValueError(f"state must be float32 or bfloat16, got {M.dtype}")
+    if M.dtype == torch.float8_e4m3fn:
+        return SDM_FP8
+    raise ValueError(f"state must be float32, bfloat16 or float8_e4m3fn, got {M.dtype}")
 
 
 def select(x1, x2, K: int, out=None, stream=None):
@@ -143,7 +146,7 @@ def select(x1, x2, K: int, out=None, stream=None):
 
 
 def state_init(M0, B: int, dtype=None, out=None, stream=None):
-    """M [B,H,N,d_v] = M0 [H,N,d_v] for every b (fp32 or bf16 state)."""
+    """M [B,H,N,d_v] = M0 [H,N,d_v] for every b (fp32, bf16 or fp8 E4M3 state)."""
     import torch
 
     dtype = torch.float32 if dtype is None else dtype

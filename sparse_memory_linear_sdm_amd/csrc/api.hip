@@ -68,15 +68,19 @@ int check_scores(const float* p, int n, const char* name) {
 int check_state(const void* M, int dtype, int64_t N, int d_v) {
   if (!M) return fail(SDM_ERR_INVALID, "M is NULL");
   if (!aligned(M, 16)) return fail(SDM_ERR_INVALID, "M must be 16-byte aligned");
-  if (dtype != SDM_F32 && dtype != SDM_BF16)
-    return fail(SDM_ERR_INVALID, "dtype must be SDM_F32 or SDM_BF16 (got %d)", dtype);
+  if (dtype != SDM_F32 && dtype != SDM_BF16 && dtype != SDM_FP8)
+    return fail(SDM_ERR_INVALID, "dtype must be SDM_F32, SDM_BF16 or SDM_FP8 (got %d)", dtype);
   if (N < 1 || N >= ((int64_t)1 << 31))
     return fail(SDM_ERR_INVALID, "N must be in [1, 2^31) (got %lld)", (long long)N);
   if (d_v < 1) return fail(SDM_ERR_INVALID, "d_v must be >= 1 (got %d)", d_v);
   if (!dv_supported(d_v))
     return fail(SDM_ERR_UNSUPPORTED, "d_v=%d not compiled (16, 32, 64, 128, 256)", d_v);
+  if (dtype == SDM_FP8 && d_v < 32)
+    return fail(SDM_ERR_UNSUPPORTED, "fp8 state needs d_v >= 32 (got %d)", d_v);
   return SDM_OK;
 }
+
+int64_t elem_bytes(int dtype) { return dtype == SDM_F32 ? 4 : (dtype == SDM_BF16 ? 2 : 1); }
 
 }  // namespace
 
@@ -142,7 +146,7 @@ int check_scan_args(const void* M, int dtype, int B, int H, int64_t N, int d_v, 
   if (W < 1 || R < 1) return fail(SDM_ERR_INVALID, "W and R must be >= 1");
   if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W and R above 64 are not compiled");
   if (W > N || R > N) return fail(SDM_ERR_INVALID, "W and R must not exceed N");
-  if (N * d_v * (dtype == SDM_F32 ? 4 : 2) >= ((int64_t)1 << 31))
+  if (N * d_v * elem_bytes(dtype) >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's table must be below 2 GiB for sdm_scan");
   return SDM_OK;
 }
@@ -257,6 +261,8 @@ int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int
   int rc;
   if ((rc = check_n_k(n, W, "W")) || (rc = check_n_k(n, R, "R"))) return rc;
   if ((rc = check_state(M, dtype, (int64_t)n * n, d_v))) return rc;
+  if (dtype == SDM_FP8)
+    return fail(SDM_ERR_UNSUPPORTED, "sdm_step_decode supports fp32 and bf16 state");
   if ((rc = check_scores(s1, n, "s1")) || (rc = check_scores(s2, n, "s2")) ||
       (rc = check_scores(q1, n, "q1")) || (rc = check_scores(q2, n, "q2")))
     return rc;

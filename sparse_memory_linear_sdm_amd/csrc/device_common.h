@@ -209,4 +209,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(b >> 16);
 }
 
+// fp8 E4M3 (OCP "e4m3fn") state element.  The gfx950 conversions round to
+// nearest even; the values the write produces stay within +-448, so the
+// saturation behaviour of the conversion never matters.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+
+// Four binary32 values -> four E4M3 codes, element i in byte i.
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 }  // namespace sdm

@@ -1,25 +1,26 @@
 // State-init kernel (page "Riepilogo Tecnico: Sparse Delta Memory (SDM)",
 // section "Stato Iniziale Appreso": each sequence starts from the learned
 // table M0).  M[b,h] = M0[h]; a streaming copy that reads each M0 element
-// once and writes it B times (bf16 state: rounded to nearest even).
+// once and writes it B times (bf16 and fp8 E4M3 state: rounded to nearest
+// even).
 #include "device_common.h"
 #include "internal.h"
 
 namespace sdm {
 namespace {
 
-// Each thread moves kU groups of 4 (fp32) or 8 (bf16) consecutive values of
+// Each thread moves kU groups of 4 (fp32), 8 (bf16) or 16 (fp8) consecutive values of
 // M0 -- one 16-byte store per group and sequence -- with a block covering
 // kU * 256 consecutive groups, so every load and store is coalesced.  M0 is
 // [H, N*d_v] and M is [B, H, N*d_v], so group i of M0 lands at group
 // b * (H * groups per head) + i of M: no per-element index arithmetic.
 constexpr int kU = 4;
 
-template <bool BF16>
+template <int DTYPE>  // 0 fp32, 1 bf16, 2 fp8
 __global__ __launch_bounds__(256) void init_kernel(void* __restrict__ M,
                                                    const f32x4* __restrict__ M0, int B, int H,
                                                    int64_t per4) {
-  constexpr int G = BF16 ? 2 : 1;  // float4 loads per group
+  constexpr int G = DTYPE == 2 ? 4 : (DTYPE == 1 ? 2 : 1);  // float4 loads per group
   const int64_t total = (int64_t)H * (per4 / G);  // groups of M0
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * kU;
   for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x * kU + threadIdx.x; i0 < total;
@@ -39,7 +40,14 @@ __global__ __launch_bounds__(256) void init_kernel(void* __restrict__ M,
         const int64_t i = i0 + (int64_t)u * 256;
         if (i >= total) continue;
         const int64_t o = (int64_t)b * total + i;
-        if constexpr (BF16) {
+        if constexpr (DTYPE == 2) {
+          u32x4 p;
+          p.x = f32x4_to_fp8x4(f[u][0].x, f[u][0].y, f[u][0].z, f[u][0].w);
+          p.y = f32x4_to_fp8x4(f[u][1].x, f[u][1].y, f[u][1].z, f[u][1].w);
+          p.z = f32x4_to_fp8x4(f[u][2].x, f[u][2].y, f[u][2].z, f[u][2].w);
+          p.w = f32x4_to_fp8x4(f[u][3].x, f[u][3].y, f[u][3].z, f[u][3].w);
+          reinterpret_cast<u32x4*>(M)[o] = p;
+        } else if constexpr (DTYPE == 1) {
           u32x4 p;
           p.x = (uint32_t)f32_to_bf16_rne(f[u][0].x) | ((uint32_t)f32_to_bf16_rne(f[u][0].y) << 16);
           p.y = (uint32_t)f32_to_bf16_rne(f[u][0].z) | ((uint32_t)f32_to_bf16_rne(f[u][0].w) << 16);
@@ -59,15 +67,18 @@ __global__ __launch_bounds__(256) void init_kernel(void* __restrict__ M,
 hipError_t launch_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N,
                              int d_v, hipStream_t stream) {
   const int64_t per4 = N * d_v / 4;
-  const int64_t total = (int64_t)H * per4 / (dtype == 1 ? 2 : 1);
+  const int64_t total = (int64_t)H * per4 / (dtype == 2 ? 4 : (dtype == 1 ? 2 : 1));
   int64_t blocks = (total + 256 * kU - 1) / (256 * kU);
   if (blocks > 256 * 4) blocks = 256 * 4;  // 4 blocks per CU: fastest alone, and leaves wave slots for
                                           // the selections that run beside it
-  if (dtype == 1)
-    hipLaunchKernelGGL(init_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
+  if (dtype == 2)
+    hipLaunchKernelGGL(init_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
+                       reinterpret_cast<const f32x4*>(M0), B, H, per4);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(init_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
                        reinterpret_cast<const f32x4*>(M0), B, H, per4);
   else
-    hipLaunchKernelGGL(init_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
+    hipLaunchKernelGGL(init_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
                        reinterpret_cast<const f32x4*>(M0), B, H, per4);
   return hipGetLastError();
 }

@@ -155,7 +155,18 @@ __device__ __forceinline__ RowKey row_key(uint32_t row) {
 
 template <typename DT>
 __device__ __forceinline__ void unpack(const u32x4v& q, float (&f)[16 / sizeof(DT)]) {
-  if constexpr (sizeof(DT) == 4) {
+  if constexpr (sizeof(DT) == 1) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  } else if constexpr (sizeof(DT) == 4) {
     f[0] = __uint_as_float(q.x);
     f[1] = __uint_as_float(q.y);
     f[2] = __uint_as_float(q.z);
@@ -172,7 +183,11 @@ __device__ __forceinline__ void unpack(const u32x4v& q, float (&f)[16 / sizeof(D
 
 template <typename DT>
 __device__ __forceinline__ u32x4v pack(const float (&f)[16 / sizeof(DT)]) {
-  if constexpr (sizeof(DT) == 4) {
+  if constexpr (sizeof(DT) == 1) {
+    return u32x4v{f32x4_to_fp8x4(f[0], f[1], f[2], f[3]), f32x4_to_fp8x4(f[4], f[5], f[6], f[7]),
+                  f32x4_to_fp8x4(f[8], f[9], f[10], f[11]),
+                  f32x4_to_fp8x4(f[12], f[13], f[14], f[15])};
+  } else if constexpr (sizeof(DT) == 4) {
     return u32x4v{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                   __float_as_uint(f[3])};
   } else {
@@ -185,6 +200,16 @@ __device__ __forceinline__ u32x4v pack(const float (&f)[16 / sizeof(DT)]) {
 }
 
 __device__ __forceinline__ u32x4v lds_u4(const uint4& x) { return u32x4v{x.x, x.y, x.z, x.w}; }
+
+// The gated delta write of one element.  For fp8 state the stored code is
+// decided by this binary32 result, so it is taken in a fixed order with no
+// contraction: Mt = alpha*m, d = v - Mt, u = fma(beta*k, d, Mt).
+__device__ __forceinline__ float write_elem_exact(float a, float g, float v, float m) {
+#pragma clang fp contract(off)
+  const float mt = a * m;
+  const float d = v - mt;
+  return __builtin_fmaf(g, d, mt);
+}
 
 // ---------------------------------------------------------------- producer
 
@@ -486,8 +511,12 @@ struct Consumer {
       const float g = b * wkk[k];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float mt = a * m[e];
-        m[e] = fmaf(g, vv[e] - mt, mt);
+        if constexpr (sizeof(DT) == 1) {
+          m[e] = write_elem_exact(a, g, vv[e], m[e]);
+        } else {
+          const float mt = a * m[e];
+          m[e] = fmaf(g, vv[e] - mt, mt);
+        }
       }
       wv[SLOT][k] = pack<DT>(m);
       __builtin_amdgcn_raw_buffer_store_b128(wv[SLOT][k], mres, wo[k], 0, 0);
@@ -711,7 +740,7 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
   // scan 2.27 -> 2.82 TB/s; three steps in flight are then best for fp32 too).
   const int cus = compute_units();
   const bool narrow = d_v == 16 || (int64_t)A.n_mem * (d_v / 16) <= cus;
-  if (narrow && 2 * (int64_t)A.n_mem * (d_v / 16) <= cus) A.shards = 2;
+  if (dtype != 2 && narrow && 2 * (int64_t)A.n_mem * (d_v / 16) <= cus) A.shards = 2;
   if (tape) {  // training forward (fp32 state): also keep the pre-write rows
     if (!narrow) return launch<float, 32, 1, true>(M, A, stream);
     if (A.shards == 2) return launch<float, 16, 3, true>(M, A, stream);
@@ -721,6 +750,12 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
     if (!narrow) return launch<float, 32, 1, false>(M, A, stream);
     if (A.shards == 2) return launch<float, 16, 3, false>(M, A, stream);
     return launch<float, 16, 2, false>(M, A, stream);
+  }
+  if (dtype == 2) {  // fp8 E4M3: 32-column tiles (32-byte rows)
+    const bool few = (int64_t)A.n_mem * (d_v / 32) < cus;
+    if (!few) return launch<fp8e4m3, 32, 1, false>(M, A, stream);
+    if (2 * (int64_t)A.n_mem * (d_v / 32) <= cus) A.shards = 2;
+    return launch<fp8e4m3, 32, 3, false>(M, A, stream);
   }
   if (!narrow) return launch<uint16_t, 32, 1, false>(M, A, stream);
   return launch<uint16_t, 16, 3, false>(M, A, stream);

@@ -82,7 +82,8 @@ def test_scan_validation():
         return L.sdm_scan(*a)
 
     assert call(M=None) == 1
-    assert call(dtype=2) == 1
+    assert call(dtype=3) == 1
+    assert call(dtype=2) == 2  # fp8 state needs d_v >= 32
     assert call(B=0) == 1
     assert call(T=-1) == 1
     assert call(W=0) == 1
@@ -156,3 +157,12 @@ def test_training_calls_validation():
     assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 16, None, None) == 1
     assert L.sdm_state_init_backward(FAKE, 0, 1, 16, 16, FAKE, None) == 1
     assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 20, FAKE, None) == 2
+
+
+def test_fp8_state_validation():
+    L = sdm.lib()
+    assert L.sdm_state_init(FAKE, 2, FAKE, 1, 1, 16, 16, None) == 2  # fp8 needs d_v >= 32
+    assert L.sdm_state_init(FAKE, 3, FAKE, 1, 1, 16, 32, None) == 1
+    ok = [FAKE, 1, 1, 1, 64, 128, 8, 8] + [FAKE] * 8 + [None, None, None]
+    ok[1] = 2
+    assert L.sdm_step_decode(*ok) == 2 and "decode" in _err()

@@ -202,6 +202,51 @@ def test_mid_config_training_full_size():
     _free()
 
 
+def test_mid_config_fp8_full_size():
+    """The mid workload with fp8 E4M3 state, all 64 memories in the
+    benchmark's launch configuration.  Memories are independent, so two
+    sampled memories run on the oracle's own selections (weights rounded to
+    binary32) while the rest keep the GPU's; the sampled memories' state codes
+    must equal the oracle's bit for bit, and their outputs meet the fp32 bar."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["mid"]
+    d = _dev_inputs(cfg)
+    M0 = torch.empty((cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device="cuda")
+    S.device_block(cfg, "M0", M0)
+    M = sdm.state_init(M0, cfg.B, torch.float8_e4m3fn)
+    widx, _, wk = sdm.select(d["s1"], d["s2"], cfg.W)
+    ridx, _, rw = sdm.select(d["q1"], d["q2"], cfg.R)
+    torch.cuda.synchronize()
+    picks = ((1, 2), (7, 7))
+    ref = {}
+    for b, h in picks:
+        host = host_inputs(cfg, b, 1, h, 1)
+        wi, _, wkk = oracle.select(host["s1"][0, 0], host["s2"][0, 0], cfg.W, threads=16)
+        ri, _, rww = oracle.select(host["q1"][0, 0], host["q2"][0, 0], cfg.R, threads=16)
+        wkk, rww = wkk.astype(np.float32), rww.astype(np.float32)
+        widx[b, h] = torch.from_numpy(wi).cuda()
+        wk[b, h] = torch.from_numpy(wkk).cuda()
+        ridx[b, h] = torch.from_numpy(ri).cuda()
+        rw[b, h] = torch.from_numpy(rww).cuda()
+        ref[b, h] = (host, wi, wkk, ri, rww)
+    out = sdm.scan(M, widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"])
+    torch.cuda.synchronize()
+    for (b, h), (host, wi, wkk, ri, rww) in ref.items():
+        M0h = S.host_block(cfg, "M0", h0=h, nh=1)
+        Mo = oracle.state_init(M0h, 1, oracle.FP8)[0, 0].copy()
+        oo = oracle.scan(Mo, oracle.FP8, wi, wkk.astype(np.float64), ri, rww.astype(np.float64),
+                         host["v"][0, 0], host["alpha"][0, 0], host["beta"][0, 0])
+        got = M[b, h].contiguous().view(torch.uint8).cpu().numpy()
+        nbad = int((got != Mo).sum())
+        assert nbad == 0, f"mid fp8 b={b} h={h}: {nbad} state codes differ"
+        check_values(out[b, h].cpu().numpy(), oo, F32, f"mid fp8 b={b} h={h} out")
+    del d, M0, M, widx, wk, ridx, rw, out
+    _free()
+
+
 def _grad_close(g, o, what):
     """Gradient bar: normwise per tensor, max|x - y| <= 1e-5 * max(1, max|y|)."""
     g = np.asarray(g, np.float64)

@@ -425,3 +425,88 @@ def test_step_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(Mg, Me), f"replay {rep}: state differs"
         assert torch.equal(out_g, out_e), f"replay {rep}: output differs"
+
+
+# ---------------------------------------------------------------- fp8 E4M3 state
+
+def _fp8_codes(t):
+    return t.contiguous().view(_torch().uint8).cpu().numpy()
+
+
+def test_state_init_fp8_bitwise_rounding():
+    """Every finite E4M3 value, every midpoint between neighbours (exact ties),
+    the binary32 neighbours of each midpoint, and random values at several
+    scales: the GPU's E4M3 codes equal the oracle's, bit for bit."""
+    import sparse_memory_linear_sdm_amd as sdm
+
+    torch = _torch()
+    t = np.array([oracle.fp8_to_double(c) for c in range(0x7F)])
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(5)
+    vals = [t.astype(np.float32), mids, np.nextafter(mids, np.float32(1e9)),
+            np.nextafter(mids, np.float32(-1e9))]
+    vals += [(rng.standard_normal(4096) * s).astype(np.float32) for s in (1e-3, 0.02, 1.0, 50.0)]
+    x = np.concatenate(vals)
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) <= 448.0]
+    d_v = 64
+    x = np.concatenate([x, np.zeros((-x.size) % (2 * d_v), np.float32)]).reshape(2, -1, d_v)
+    M = sdm.state_init(torch.from_numpy(x).cuda(), 3, torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    ref = oracle.state_init(x, 3, oracle.FP8)
+    got = _fp8_codes(M)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, [(float(x[tuple(i[1:])]), int(got[tuple(i)]), int(ref[tuple(i)]))
+                           for i in bad[:5]]
+
+
+def _fp8_scan_case(cfg):
+    """fp8 state: the GPU scan and the oracle scan on the same binary32
+    selection weights (the oracle's, rounded to binary32), so the stored codes
+    must agree bit for bit; outputs within the fp32 bar."""
+    import sparse_memory_linear_sdm_amd as sdm
+
+    torch = _torch()
+    host = host_inputs(cfg)
+    M0 = S.host_block(cfg, "M0")
+    sel = {}
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            wi, _, wk = oracle.select(host["s1"][b, h], host["s2"][b, h], cfg.W)
+            ri, _, rw = oracle.select(host["q1"][b, h], host["q2"][b, h], cfg.R)
+            sel[b, h] = (wi, wk.astype(np.float32), ri, rw.astype(np.float32))
+
+    def stack(i, dt):
+        return np.stack([np.stack([sel[b, h][i] for h in range(cfg.H)]) for b in range(cfg.B)]
+                        ).astype(dt)
+
+    widx, wk, ridx, rw = stack(0, np.int32), stack(1, np.float32), stack(2, np.int32), \
+        stack(3, np.float32)
+    dev = to_dev({k: host[k] for k in ("v", "alpha", "beta")})
+    M = sdm.state_init(torch.from_numpy(M0).cuda(), cfg.B, torch.float8_e4m3fn)
+    out = sdm.scan(M, *(torch.from_numpy(a).cuda() for a in (widx, wk, ridx, rw)), dev["v"],
+                   dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    Mg, og = _fp8_codes(M), out.cpu().numpy()
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            Mo = oracle.state_init(M0[h][None], 1, oracle.FP8)[0, 0].copy()
+            oo = oracle.scan(Mo, oracle.FP8, widx[b, h], wk[b, h].astype(np.float64), ridx[b, h],
+                             rw[b, h].astype(np.float64), host["v"][b, h], host["alpha"][b, h],
+                             host["beta"][b, h])
+            tag = f"fp8 {cfg.name} b={b} h={h}"
+            nbad = int((Mg[b, h] != Mo).sum())
+            assert nbad == 0, f"{tag}: {nbad} state codes differ"
+            check_values(og[b, h], oo, F32, tag + " out")
+
+
+@pytest.mark.parametrize("B,H,n,d_v,T,W,R", [
+    (8, 36, 16, 32, 40, 8, 8),     # 288 memories x 1 tile: one step in flight
+    (5, 16, 64, 128, 70, 64, 64),  # 80 memories x 4 tiles: one step in flight
+    (1, 3, 32, 64, 101, 32, 17),   # few memories: three steps in flight, two row shards
+    (2, 2, 8, 256, 150, 8, 8),     # 64-slot tables, W = R = 8: heavy reuse, forwarded rows
+])
+def test_scan_fp8_codes_bitwise(B, H, n, d_v, T, W, R):
+    cfg = S.CONFIGS["tiny"].with_(B=B, H=H, n=n, d_v=d_v, T=T, W=W, R=R,
+                                  seed=8100 + B + H + n + d_v)
+    _fp8_scan_case(cfg)

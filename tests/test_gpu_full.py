@@ -149,6 +149,39 @@ def test_mid_config_full_size():
     _free()
 
 
+def test_mid_config_bf16_full_size():
+    """The mid workload with bf16 state (bench.py --state bf16), all 64
+    memories in that launch configuration; two memories checked in full
+    against the oracle (indices bit-exact, state and outputs normwise 2e-2)."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["mid"]
+    d = _dev_inputs(cfg)
+    M0 = torch.empty((cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device="cuda")
+    S.device_block(cfg, "M0", M0)
+    M = sdm.state_init(M0, cfg.B, torch.bfloat16)
+    widx, wsc, wk = sdm.select(d["s1"], d["s2"], cfg.W)
+    ridx, rsc, rw = sdm.select(d["q1"], d["q2"], cfg.R)
+    out = sdm.scan(M, widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"])
+    torch.cuda.synchronize()
+    for b, h in ((3, 1), (5, 6)):
+        host = host_inputs(cfg, b, 1, h, 1)
+        M0h = S.host_block(cfg, "M0", h0=h, nh=1)[0]
+        o = oracle_memory(cfg, host, 0, 0, M0h, BF16, threads=16)
+        tag = f"mid bf16 b={b} h={h}"
+        check_selection(widx[b, h].cpu().numpy(), wsc[b, h].cpu().numpy(), wk[b, h].cpu().numpy(),
+                        o["widx"], o["wscore"], o["wk"], tag + " write")
+        check_selection(ridx[b, h].cpu().numpy(), rsc[b, h].cpu().numpy(), rw[b, h].cpu().numpy(),
+                        o["ridx"], o["rscore"], o["rw"], tag + " read")
+        gm = oracle.bf16_bits_to_f32(state_to_host(M[b, h]))
+        check_values(gm, oracle.bf16_bits_to_f32(o["M"]), BF16, tag + " M")
+        check_values(out[b, h].cpu().numpy(), o["out"], BF16, tag + " out")
+    del d, M0, M, widx, wsc, wk, ridx, rsc, rw, out
+    _free()
+
+
 def test_mid_config_training_full_size():
     """The training step of the mid workload in the benchmark's launch
     configuration (64 memories of 2^20 x 128, T = 4096, gradient table

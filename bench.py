@@ -172,10 +172,58 @@ def run_prefill(cfg, args, torch, S, sdm):
     side = torch.cuda.Stream()  # default priority
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    # --pipeline: the selections of the next batch run on the side stream
+    # beside this batch's scan (ALU-bound beside HBM-bound), into the other
+    # of two selection buffers; each step still runs one batch's state init,
+    # selections and scan.
+    sel = [(widx, wk, ridx, rw)]
+    if args.pipeline:
+        sel.append(tuple(torch.empty_like(x) for x in (widx, wk, ridx, rw)))
+    pipe = {"i": 0, "scan_done": [None, None]}
+
+    def select_into(buf, s):
+        wi, wkk, ri, rww = sel[buf]
+        sdm.select(inp["s1"], inp["s2"], W, out=(wi, None, wkk), stream=s)
+        sdm.select(inp["q1"], inp["q2"], R, out=(ri, None, rww), stream=s)
+
+    if args.pipeline:  # batch 0's selections, before the first step
+        select_into(0, stream)
+        pipe["ready"] = torch.cuda.Event()
+        pipe["ready"].record(stream)
+
+    def step_pipelined(record=None):
+        i = pipe["i"]
+        cur, nxt = i % 2, (i + 1) % 2
+        e = [ev() for _ in range(6)]
+        e[0].record(stream)
+        sdm.state_init(M0, B, out=M, stream=stream)
+        e[1].record(stream)
+        # next batch's selections: after this init (so they sit beside the
+        # scan), and after the scan that last read buffer nxt
+        side.wait_event(e[1])
+        if pipe["scan_done"][nxt] is not None:
+            side.wait_event(pipe["scan_done"][nxt])
+        e[2].record(side)
+        select_into(nxt, side)
+        e[3].record(side)
+        stream.wait_event(pipe["ready"])
+        e[4].record(stream)
+        wi, wkk, ri, rww = sel[cur]
+        sdm.scan(M, wi, wkk, ri, rww, inp["v"], inp["alpha"], inp["beta"], out=out,
+                 stream=stream)
+        e[5].record(stream)
+        pipe["scan_done"][cur] = e[5]
+        pipe["ready"] = e[3]
+        pipe["i"] = i + 1
+        if record is not None:
+            record.append(e)
+
     def step(record=None):
         """init on the main stream; the two selections on the side stream (they
         are independent of the init, and ALU-bound while the init is
         HBM-bound); the scan on the main stream after both."""
+        if args.pipeline:
+            return step_pipelined(record)
         e = [ev() for _ in range(6)]
         e[0].record(stream)
         if args.no_overlap:
@@ -210,6 +258,8 @@ def run_prefill(cfg, args, torch, S, sdm):
     g0.record(stream)
     for _ in range(args.steps):
         step(recs)
+    if args.pipeline:
+        stream.wait_event(pipe["ready"])  # the last step's selections are inside the span
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -231,9 +281,13 @@ def run_prefill(cfg, args, torch, S, sdm):
                 "algorithmic_bytes_per_launch": slot_bytes}
     extra = {"breakdown_ms": {"state_init": init_ms, "select_write_read": sel_ms,
                               "scan": scan_ms,
-                              "overlap": "select || state_init" if not args.no_overlap
-                              else "none"},
+                              "overlap": ("select(k+1) || scan(k)" if args.pipeline else
+                                          "select || state_init" if not args.no_overlap
+                                          else "none")},
              "scan_tokens_per_s": tokens_per_step / (scan_ms * 1e-3),
+             "schedule": ("pipelined: selections of batch k+1 beside the scan of batch k"
+                          if args.pipeline else ("serial" if args.no_overlap else
+                                                 "selections beside the state init")),
              "wall_s": wall}
     rec = _common_record(cfg, args, tokens_per_step / (ms_step * 1e-3), "tokens/s", ms_step,
                          {4: "f32", 2: "f32 math, bf16 state", 1: "f32 math, fp8 e4m3 state"}[es],
@@ -585,6 +639,8 @@ def main():
                     help="time a training step (forward with tape + reverse pass) instead")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the step's kernels back to back on one stream")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="prefill: run the next batch's selections beside this batch's scan")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")

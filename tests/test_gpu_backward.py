@@ -147,3 +147,52 @@ def test_select_backward_parity(n, K, units):
     used1 = np.zeros((units, n), bool)
     np.put_along_axis(used1, oi // n, True, axis=1)
     assert np.all(d1.cpu().numpy()[~used1] == 0.0)
+
+
+def test_chunked_training_bitwise():
+    """Forward in two chunks (one tape each), then the reverse pass chunk by
+    chunk in reverse order carrying G: every gradient is bitwise equal to the
+    single-call forward and reverse pass, and the state ends restored."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(B=2, H=3, n=32, d_v=64, T=150, W=32, R=16, seed=9300)
+    host = host_inputs(cfg)
+    dev = to_dev(host)
+    dout = torch.from_numpy(S.host_block(cfg, "dout")).cuda()
+    M0 = torch.from_numpy(S.host_block(cfg, "M0")).cuda()
+    widx, _, wk = sdm.select(dev["s1"], dev["s2"], cfg.W)
+    ridx, _, rw = sdm.select(dev["q1"], dev["q2"], cfg.R)
+    names = ("v", "alpha", "beta")
+
+    def sl(x, a, b):
+        return x[:, :, a:b].contiguous()
+
+    # whole
+    M = sdm.state_init(M0, cfg.B)
+    out, tape = sdm.scan_train(M, widx, wk, ridx, rw, *(dev[k] for k in names))
+    G = torch.zeros_like(M)
+    whole = sdm.scan_backward(M, widx, wk, ridx, rw, *(dev[k] for k in names), tape, dout, G)
+    # two chunks
+    T1 = 61
+    spans = ((0, T1), (T1, cfg.T))
+    M2 = sdm.state_init(M0, cfg.B)
+    outs, tapes = [], []
+    for a, b in spans:
+        o, tp = sdm.scan_train(M2, sl(widx, a, b), sl(wk, a, b), sl(ridx, a, b), sl(rw, a, b),
+                               *(sl(dev[k], a, b) for k in names))
+        outs.append(o)
+        tapes.append(tp)
+    G2 = torch.zeros_like(M2)
+    parts = {}
+    for (a, b), tp in reversed(list(zip(spans, tapes))):
+        parts[a] = sdm.scan_backward(M2, sl(widx, a, b), sl(wk, a, b), sl(ridx, a, b),
+                                     sl(rw, a, b), *(sl(dev[k], a, b) for k in names), tp,
+                                     sl(dout, a, b), G2)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2), out)
+    assert torch.equal(G2, G)
+    assert torch.equal(M2, M) and torch.equal(M, sdm.state_init(M0, cfg.B))
+    for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
+        assert torch.equal(torch.cat([parts[0][k], parts[T1][k]], dim=2), whole[k]), k

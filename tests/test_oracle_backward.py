@@ -21,7 +21,7 @@ def _case(rng, N=8, d_v=3, T=6, W=3, R=2, reuse=True):
     summing to one, gates in the workload ranges."""
     widx = np.stack([rng.choice(N, W, replace=False) for _ in range(T)]).astype(np.int32)
     ridx = np.stack([rng.choice(N, R, replace=False) for _ in range(T)]).astype(np.int32)
-    if reuse and T > 1 and R > 0:
+    if reuse and T > 1 and R > 0 and widx[1, 0] not in ridx[1]:
         ridx[1, 0] = widx[1, 0]  # a read of a row written in the same step
     wk = rng.random((T, W)) + 0.1
     wk /= wk.sum(1, keepdims=True)
@@ -236,3 +236,27 @@ def test_state_init_backward_sums_sequences():
     got = oracle.state_init_backward(dM)
     assert np.array_equal(oracle.state_init_backward(dM[:1]), dM[0].astype(np.float64))
     assert np.allclose(got, dM.astype(np.float64).sum(0), rtol=0, atol=1e-12)
+
+
+def test_chunked_backward_equals_whole():
+    """Training a sequence in two chunks -- the second chunk's reverse pass
+    starting from the final gradient, the first's from the gradient the second
+    returns, each from its own starting state -- gives the whole-sequence
+    gradients (the reverse recurrence carries only G between steps)."""
+    rng = np.random.default_rng(11)
+    case = _case(rng, N=32, d_v=6, T=30, W=4, R=3)
+    T, d_v = case["v"].shape
+    dout = rng.standard_normal((T, d_v)).astype(np.float32)
+    dMT = rng.standard_normal((32, d_v))
+    whole = _bwd(case, dout, dMT)
+    T1 = 13
+    first = {k: (v[:T1] if k not in ("M0",) else v) for k, v in case.items()}
+    M1 = case["M0"].copy()
+    oracle.scan(M1, oracle.F32, case["widx"][:T1], case["wk"][:T1], case["ridx"][:T1],
+                case["rw"][:T1], case["v"][:T1], case["alpha"][:T1], case["beta"][:T1])
+    second = {k: (v[T1:] if k not in ("M0",) else M1) for k, v in case.items()}
+    g2 = _bwd(second, dout[T1:], dMT)
+    g1 = _bwd(first, dout[:T1], g2["dM0"])
+    assert np.allclose(g1["dM0"], whole["dM0"], rtol=0, atol=1e-12)
+    for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
+        assert np.allclose(np.concatenate([g1[k], g2[k]]), whole[k], rtol=0, atol=1e-12), k

@@ -172,7 +172,8 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  *   dk_j = beta*<g, v_t - alpha*P>;  dbeta_t += k_j*<g, v_t - alpha*P>;
  *   G[f_j] = alpha*(1 - beta*k_j)*g;   dr_l = <dout_t, M_t[g_l]>.
  * Arithmetic in fp32; the tile partial sums are added in a fixed order, so
- * results are deterministic.  Sizes as for sdm_scan, plus T < 2^26. */
+ * results are deterministic.  Sizes as for sdm_scan, plus T < 2^26 and
+ * B*H*T < 2^33. */
 int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,
                       const float* rw, const float* v, const float* alpha, const float* beta,

@@ -211,6 +211,8 @@ int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int
   if (!aligned(dwk, 4) || !aligned(drw, 4) || !aligned(dalpha, 4) || !aligned(dbeta, 4))
     return fail(SDM_ERR_INVALID, "dwk, drw, dalpha and dbeta must be 4-byte aligned");
   if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
+  if ((int64_t)B * H * T >= ((int64_t)1 << 33))
+    return fail(SDM_ERR_UNSUPPORTED, "B*H*T must be below 2^33 (one finishing wave per step)");
   if (T * W * d_v * 4 >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*W*d_v*4 bytes) must be below 2 GiB; "
                 "split the sequence into consecutive calls");

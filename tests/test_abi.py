@@ -143,6 +143,8 @@ def test_training_calls_validation():
     assert L.sdm_scan_backward(*a) == 1
     a = list(ok); a[5] = 1 << 26
     assert L.sdm_scan_backward(*a) == 2
+    a = list(ok); a[1] = 1 << 12; a[2] = 1 << 12; a[5] = 1 << 10
+    assert L.sdm_scan_backward(*a) == 2 and "2^33" in _err()
     a = list(ok); a[4] = 24
     assert L.sdm_scan_backward(*a) == 2
     # sdm_select_backward: idx, w, dw, units, n, K, dx1, dx2, stream

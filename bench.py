@@ -37,6 +37,7 @@ METRIC = "SDM scan tokens/sec + slot-traffic HBM GB/s (% of peak), N=2^20, d_v=1
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_traffic.json")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_bwd_mid_traffic.json")
+LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_traffic.json")
 _CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
 SCAN_SOURCES = [os.path.join(_CSRC, f) for f in ("scan.hip", "device_common.h")]
 BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "device_common.h")]
@@ -545,6 +546,8 @@ def run_long(cfg, args, torch, S, sdm):
                     torch.empty((B, H, C, R), dtype=torch.int32, device=dev),
                     torch.empty((B, H, C, R), dtype=f32, device=dev)))
     out = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
+    torch.cuda.synchronize()
+    calibration_copy(args, torch, dev)
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()  # default priority
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -613,8 +616,9 @@ def run_long(cfg, args, torch, S, sdm):
     gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": "scan_kernel<float,16,3>, two row shards (duration includes the "
+                "frac": gbps / HBM_PEAK_GBPS,
+                "traffic": measured_traffic(slot_bytes // nch, LONG_TRAFFIC_FILE),
+                "kernel": "scan_kernel<float,16,3,false>, two row shards (duration includes the "
                           "output zero fill of the same call)", "algorithmic_bytes_per_launch":
                 slot_bytes // nch}
     bd = ({"select_write_read": sel_ms, "scan": scan_ms} if args.no_overlap else

@@ -2,7 +2,8 @@
 // Tecnico: Sparse Delta Memory (SDM)", "Meccanismo Core" items 2-4):
 //   1. each of the four waves runs stage 1 of one half (s1, s2, q1, q2) of the
 //      product-key top-K; waves 0 and 1 then finish the write and the read
-//      selection (item 2);
+//      selection (item 2); both stages find their K-th key by the radix
+//      search, which has the shorter dependent chain;
 //   2. the whole block applies the gated delta write to the W rows (item 3);
 //   3. it reads the R rows and forms o = sum_j r_j M[g_j] (item 4).
 // When a step's rows fit one batch of loads per thread (the decode workload
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   __shared__ float s_red[4096 / ES];
   __shared__ uint4 s_stage[kStage];  // updated rows by write slot (one-batch path)
   __shared__ int32_t s_match[64];    // read slot -> write slot of the same row, or -1
+  __shared__ __align__(16) uint32_t s_hist[4][256];  // stage 1's radix-search histogram, one per wave
 
   const int mem = blockIdx.x;
   const int tid = threadIdx.x;
@@ -86,13 +88,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   {
     const float* x = w == 0 ? s1 : w == 1 ? s2 : w == 2 ? q1 : q2;
     SelectLds& S = sl[w >> 1];
-    stage1_half<P>(x + (int64_t)mem * n, n, w < 2 ? W : R, (w & 1) ? S.sorted.b : S.sorted.a,
-                   S.trash);
+    stage1_half<P, true>(x + (int64_t)mem * n, n, w < 2 ? W : R,
+                         (w & 1) ? S.sorted.b : S.sorted.a, S.trash, s_hist[w]);
   }
   if (tid < d_v) s_v[tid] = vreg;
   __syncthreads();
-  if (w == 0) select_finish(n, W, sl[0], rc, s_widx, nullptr, s_wk);
-  else if (w == 1) select_finish(n, R, sl[1], rc, s_ridx, nullptr, s_rw);
+  if (w == 0) select_finish<true>(n, W, sl[0], rc, s_widx, nullptr, s_wk);
+  else if (w == 1) select_finish<true>(n, R, sl[1], rc, s_ridx, nullptr, s_rw);
   __syncthreads();
   if (widx_out && tid < W) widx_out[(int64_t)mem * W + tid] = s_widx[tid];
   if (ridx_out && tid < R) ridx_out[(int64_t)mem * R + tid] = s_ridx[tid];

@@ -8,10 +8,16 @@
 //
 // Method, per unit, on one wave of 64 lanes and no sorting of the inputs:
 //   stage 1  each lane holds P = n/64 order-preserving uint32 keys.  The K-th
-//            largest key is found by bisection on the key value; each probe
-//            counts in registers and sums over the wave with DPP.  The search
-//            stops as soon as a probe has exactly K keys at or above it.  Ties
-//            at the final threshold are resolved by bisection on the index.
+//            largest key is found either by bisection on the key value (each
+//            probe counts in registers and sums over the wave; the search
+//            stops as soon as a probe has exactly K keys at or above it), or
+//            by a radix search over the key range [lo, hi): the keys in range
+//            are counted into a 256-bin LDS histogram by the top 8 bits of
+//            key - lo, one suffix scan over the bins finds the bin holding
+//            the K-th largest, and the range shrinks to that bin (at most four
+//            passes; it stops as soon as a bin holds exactly the keys still
+//            needed).  Ties at the final threshold are resolved by bisection
+//            on the index.
 //   stage 2  both survivor lists are sorted (rank r for x1, c for x2).  With
 //            both sorted, key(r, c) = key(fl(A_r + B_c)) does not increase
 //            along a row or a column (binary32 addition is monotone), so the
@@ -23,8 +29,8 @@
 //            leaves P+ contains a row prefix reaching past the bound, which
 //            already holds K pairs of P+, plus that row's boundary pair).
 //            P+ has at most 343 pairs for K <= 64, so every lane keeps <= 6
-//            of their keys in registers and the bisection of stage 1 applies
-//            to P+ unchanged.  Ties at the K-th key are broken by bisection
+//            of their keys in registers and the search of stage 1 applies to
+//            P+ unchanged.  Ties at the K-th key are broken by bisection
 //            on f.  Ties only extend past P+ through a boundary pair; in that
 //            rare case the affected rows' tied runs are added from LDS.
 //   weights  softmax of the K selected sums in fp32 (expf).
@@ -79,6 +85,7 @@ struct SelectLds {
   } sorted;
   uint64_t cand[64];   // the K selected: (key << 32) | ~f
   uint64_t trash[64];  // per-lane sink of stage 1's branch-free compaction
+  alignas(16) uint32_t hist[256];  // radix-search histogram of the wave that owns this
 };
 
 // Index of register slot p of a lane: groups of 4 consecutive elements per
@@ -136,7 +143,7 @@ __device__ __forceinline__ int count_ge(const uint32_t (&u)[P], uint32_t t) {
 // *exact tells whether exactly K keys are >= it (else it is the K-th key
 // itself, held by more than one key, and ties at it must be broken).
 template <int P>
-__device__ __forceinline__ uint32_t kth_key(const uint32_t (&u)[P], int K, uint64_t lo, uint64_t hi,
+__device__ __forceinline__ uint32_t kth_key_bisect(const uint32_t (&u)[P], int K, uint64_t lo, uint64_t hi,
                                             bool* exact_out) {
   bool exact = count_ge<P>(u, (uint32_t)lo) == K;
   while (!exact && hi - lo > 1) {
@@ -153,12 +160,74 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&u)[P], int K, uint6
   return (uint32_t)lo;
 }
 
+// The same result by a radix search, in [lo, hi) where
+// count(>= lo) >= K and count(>= hi) < K.  Each pass counts the keys in
+// range into a 256-bin histogram (LDS, one per wave) by the top 8 bits of
+// key - lo, finds the bin d* holding the K-th largest with one suffix scan
+// over the bins (lane l holds bins 4l .. 4l+3), and continues inside that
+// bin.  Returns the threshold; *exact tells whether exactly K keys are >= it
+// (else it is the K-th key itself, held by more than one key, and ties at it
+// must be broken).  Fewer dependent steps than the bisection (at most four
+// passes of a few LDS round trips, against 15-30 probes) but more
+// instructions: the fused decode step, one unit per wave and latency-bound,
+// takes this one; the batched selection, throughput-bound, the bisection.
+template <int P>
+__device__ __forceinline__ uint32_t kth_key_radix(const uint32_t (&u)[P], int K, uint64_t lo,
+                                                  uint64_t hi, bool* exact_out, uint32_t* hist) {
+  const int lane = lane_id();
+  int krem = K - (hi > 0xFFFFFFFFull ? 0 : count_ge<P>(u, (uint32_t)hi));  // still needed in range
+  for (;;) {
+    const uint64_t range = hi - lo;  // >= 1
+    const int bits = range > 1 ? 64 - __builtin_clzll(range - 1) : 0;
+    const int shift = bits > 8 ? bits - 8 : 0;
+    const uint32_t lo32 = (uint32_t)lo;
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_sync();
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (u[p] >= lo && (uint64_t)u[p] < hi) atomicAdd(&hist[(u[p] - lo32) >> shift], 1u);
+    wave_sync();
+    const uint4 b = reinterpret_cast<const uint4*>(hist)[lane];
+    const int local = (int)(b.x + b.y + b.z + b.w);
+    const int excl = wave_excl_scan_i32(local);
+    const int total = __builtin_amdgcn_readlane(excl + local, 63);
+    const int g4 = total - excl - local;  // keys in the bins of higher lanes
+    const int g3 = g4 + (int)b.w, g2 = g3 + (int)b.z, g1 = g2 + (int)b.y, g0 = g1 + (int)b.x;
+    // d* = 4l + j with count(digit >= d*) >= krem > count(digit > d*): one lane, one j
+    int j = -1, gt = 0, bc = 0;
+    if (g3 >= krem && g4 < krem) { j = 3; gt = g4; bc = (int)b.w; }
+    else if (g2 >= krem && g3 < krem) { j = 2; gt = g3; bc = (int)b.z; }
+    else if (g1 >= krem && g2 < krem) { j = 1; gt = g2; bc = (int)b.y; }
+    else if (g0 >= krem && g1 < krem) { j = 0; gt = g1; bc = (int)b.x; }
+    const int L = __ffsll((unsigned long long)__ballot(j >= 0)) - 1;
+    const int dstar = 4 * L + __builtin_amdgcn_readlane(j, L);
+    krem -= __builtin_amdgcn_readlane(gt, L);
+    const int bcount = __builtin_amdgcn_readlane(bc, L);
+    const uint64_t nlo = lo + ((uint64_t)dstar << shift);
+    const uint64_t nhi = nlo + (1ull << shift) < hi ? nlo + (1ull << shift) : hi;
+    wave_sync();  // the histogram is cleared again by the next pass
+    if (bcount == krem) {  // every key of the bin goes in: the bin's smallest key is the threshold
+      uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+      for (int p = 0; p < P; ++p) mn = (u[p] >= nlo && (uint64_t)u[p] < nhi && u[p] < mn) ? u[p] : mn;
+      *exact_out = true;
+      return wave_min_u32(mn);
+    }
+    if (shift == 0) {  // the bin is one key value, held by more keys than still needed
+      *exact_out = false;
+      return (uint32_t)nlo;
+    }
+    lo = nlo;
+    hi = nhi;
+  }
+}
+
 // Stage 1 for one half: writes the K survivors to LDS as (key << 32) | ~index,
 // in no particular order.  Every slot is stored; a slot that is not selected
 // goes to the lane's own trash word, so the compaction has no branches.
-template <int P>
+template <int P, bool RADIX>
 __device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int lane,
-                                       uint64_t* out, uint64_t* trash) {
+                                       uint64_t* out, uint64_t* trash, uint32_t* hist) {
   uint32_t lmax = 0, lmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -170,7 +239,8 @@ __device__ __forceinline__ void stage1(const uint32_t (&u)[P], int n, int K, int
   // >= 64 >= K keys at or above it; otherwise start from the smallest key.
   const uint64_t lo = (n >= 64) ? (uint64_t)wave_min_u32(lmax) : (uint64_t)wave_min_u32(lmin);
   bool exact;
-  const uint32_t tau = kth_key<P>(u, K, lo, hi, &exact);
+  const uint32_t tau = RADIX ? kth_key_radix<P>(u, K, lo, hi, &exact, hist)
+                             : kth_key_bisect<P>(u, K, lo, hi, &exact);
   // Tie handling: keys > tau all go in; m = K - #(> tau) of the keys == tau
   // with the lowest indices go in.  ibound = first index NOT taken.
   int ibound = 0x7FFFFFFF;
@@ -233,17 +303,18 @@ __device__ __forceinline__ void pair_slots(int K, uint32_t (&rc)[pairtab::kSlots
 }
 
 // Stage 1 of one half, from its n values in memory to its K survivors in LDS.
-template <int P>
+template <int P, bool RADIX>
 __device__ __forceinline__ void stage1_half(const float* __restrict__ x, int n, int K,
-                                            uint64_t* out, uint64_t* trash) {
+                                            uint64_t* out, uint64_t* trash, uint32_t* hist) {
   uint32_t u[P];
   load_keys<P>(x, n, lane_id(), u);
-  stage1<P>(u, n, K, lane_id(), out, trash);
+  stage1<P, RADIX>(u, n, K, lane_id(), out, trash, hist);
 }
 
 // Everything after stage 1: both halves' survivors are in s.s1 (written by
 // this wave, or by others before a barrier).  Writes K outputs per unit
 // (lanes j < K write slot j).
+template <bool RADIX>
 __device__ inline void select_finish(int n, int K, SelectLds& s, const uint32_t (&rc)[pairtab::kSlots],
                               int32_t* __restrict__ idx_out, float* __restrict__ score_out,
                               float* __restrict__ weight_out) {
@@ -280,7 +351,8 @@ __device__ inline void select_finish(int n, int K, SelectLds& s, const uint32_t 
   const uint64_t lo0 = okey(a0 + sorted_val(s.sorted.b[K - 1]));
   const uint64_t hi0 = (uint64_t)okey(a0 + sorted_val(s.sorted.b[0])) + 1;
   bool exact;
-  const uint32_t tau = kth_key<S>(sk, K, lo0, hi0, &exact);
+  const uint32_t tau = RADIX ? kth_key_radix<S>(sk, K, lo0, hi0, &exact, s.hist)
+                             : kth_key_bisect<S>(sk, K, lo0, hi0, &exact);
 
   // Ties at tau (not exact): m of them go in, lowest f first.  Tied pairs
   // outside P+ exist only in rows whose boundary pair ties; lane r then adds
@@ -362,10 +434,10 @@ __device__ void select_unit(const float* __restrict__ x1, const float* __restric
                             float* __restrict__ score_out, float* __restrict__ weight_out) {
   uint32_t rc[pairtab::kSlots];
   pair_slots(K, rc);
-  stage1_half<P>(x1, n, K, s.sorted.a, s.trash);
-  stage1_half<P>(x2, n, K, s.sorted.b, s.trash);
+  stage1_half<P, false>(x1, n, K, s.sorted.a, s.trash, s.hist);
+  stage1_half<P, false>(x2, n, K, s.sorted.b, s.trash, s.hist);
   wave_sync();
-  select_finish(n, K, s, rc, idx_out, score_out, weight_out);
+  select_finish<false>(n, K, s, rc, idx_out, score_out, weight_out);
 }
 
 }  // namespace sdm

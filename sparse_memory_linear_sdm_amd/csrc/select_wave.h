@@ -168,9 +168,12 @@ __device__ __forceinline__ uint32_t kth_key_bisect(const uint32_t (&u)[P], int K
 // bin.  Returns the threshold; *exact tells whether exactly K keys are >= it
 // (else it is the K-th key itself, held by more than one key, and ties at it
 // must be broken).  Fewer dependent steps than the bisection (at most four
-// passes of a few LDS round trips, against 15-30 probes) but more
-// instructions: the fused decode step, one unit per wave and latency-bound,
-// takes this one; the batched selection, throughput-bound, the bisection.
+// passes of a few LDS round trips, against 15-30 probes) but, over the n/64
+// keys per lane of stage 1, more instructions: the fused decode step (one
+// unit per wave, latency-bound) uses it in both stages; the batched
+// selection (throughput-bound) in stage 2 only, where each lane holds at most
+// six candidate keys (measured: stage 1 by bisection and stage 2 by this
+// search is the fastest of the four combinations there).
 template <int P>
 __device__ __forceinline__ uint32_t kth_key_radix(const uint32_t (&u)[P], int K, uint64_t lo,
                                                   uint64_t hi, bool* exact_out, uint32_t* hist) {
@@ -437,7 +440,7 @@ __device__ void select_unit(const float* __restrict__ x1, const float* __restric
   stage1_half<P, false>(x1, n, K, s.sorted.a, s.trash, s.hist);
   stage1_half<P, false>(x2, n, K, s.sorted.b, s.trash, s.hist);
   wave_sync();
-  select_finish<false>(n, K, s, rc, idx_out, score_out, weight_out);
+  select_finish<true>(n, K, s, rc, idx_out, score_out, weight_out);
 }
 
 }  // namespace sdm

@@ -4,10 +4,10 @@
 //
 // Layout and parallelism.  The update is independent per column, so each
 // memory's d_v columns are split into tiles of 32 columns (128 bytes of an
-// fp32 row = one cache line; 64 bytes of a bf16 row, which keeps the same
-// number of workgroups as fp32 -- measured faster than 128-byte bf16 tiles
-// at half the workgroups); one workgroup owns one (b,h,tile) and walks
-// t = 0..T-1.  With few memories (narrow 16-column tiles and still room on
+// fp32 row = one cache line; 64 bytes of a bf16 row and 32 bytes of an fp8
+// E4M3 row, which keep the same number of workgroups as fp32 -- measured
+// faster than line-sized bf16 or fp8 tiles at a half or a quarter of the
+// workgroups); one workgroup owns one (b,h,tile) and walks t = 0..T-1.  With few memories (narrow 16-column tiles and still room on
 // the chip) the rows of a memory are further split between two workgroups by
 // a hash of the row index; each adds its part of the read into the zeroed
 // output.  Blocks are numbered so that all tiles and shards of one memory
@@ -38,10 +38,13 @@
 //   consumer  keeps the row gathers of D steps in flight in a register ring:
 //             at step u it issues the 16-byte buffer loads of step u + D, then
 //             updates step u's W rows (Mt = alpha*M; M = Mt + (beta*k)(v - Mt)
-//             in fp32, rounded to the state type) and stores them, and
-//             accumulates the R read rows.  Rows the plan forwards come from a
-//             small LDS ring of saved updated rows instead of the (possibly
-//             stale) loaded values.  Loads of step u + D are issued after the
+//             in fp32, rounded to the state type; for fp8 in a fixed
+//             binary32 order with no contraction) and stores them, and
+//             accumulates the R read rows.  The training variant (SAVE)
+//             also stores each write row's current value, before the update,
+//             to the tape the reverse pass reads.  Rows the plan forwards come
+//             from a small LDS ring of saved updated rows instead of the
+//             (possibly stale) loaded values.  Loads of step u + D are issued after the
 //             stores of every step before u by the same wavefront, so the
 //             only rows they can miss are those written in [u, u + D - 1] --
 //             exactly the window the producer checks.  The read's cross-lane

@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -43,11 +44,19 @@ SCAN_SOURCES = [os.path.join(_CSRC, f) for f in ("scan.hip", "device_common.h")]
 BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "device_common.h")]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace, so that counter records
+    stay tied to the code itself and not to its commentary."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def scan_source_sha(sources=None) -> str:
     h = hashlib.sha256()
     for f in sources or SCAN_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -31,8 +31,15 @@ __global__ __launch_bounds__(256) void init_kernel(void* __restrict__ M,
       const int64_t i = i0 + (int64_t)u * 256;
 #pragma unroll
       for (int g = 0; g < G; ++g)
-        f[u][g] = i < total ? __builtin_nontemporal_load(M0 + i * G + g)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        // fp32: one 16-byte load per group, streamed past the caches.  bf16
+        // and fp8: G loads of one 64- or 32-byte group that share cache
+        // lines, so they are plain loads -- streamed, each went to memory on
+        // its own (fp8: 6.05 GB read for 4.29 GB of M0, 2.92 -> 2.48 ms at mid).
+        if constexpr (G == 1)
+          f[u][g] = i < total ? __builtin_nontemporal_load(M0 + i * G + g)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+        else
+          f[u][g] = i < total ? M0[i * G + g] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     for (int b = 0; b < B; ++b) {
 #pragma unroll

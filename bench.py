@@ -281,8 +281,8 @@ def run_prefill(cfg, args, torch, S, sdm):
     tokens_per_step = B * T
     slot_bytes = B * H * T * (2 * W + R) * d_v * es  # algorithmic, one scan launch
     scan_gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
-    kname = {4: "scan_kernel<float,32,1>", 2: "scan_kernel<uint16_t(bf16),32,1>",
-             1: "scan_kernel<fp8e4m3,32,1>"}[es]
+    kname = {4: "scan_kernel<float,32,1,false>", 2: "scan_kernel<uint16_t(bf16),32,1,false>",
+             1: "scan_kernel<fp8e4m3,32,1,false>"}[es]
     traffic = measured_traffic(slot_bytes) if (cfg.name == "mid" and es == 4) else None
     workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
                 f"{args.state} state")

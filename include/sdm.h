@@ -76,7 +76,7 @@ enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8 = 2 };
  *           -0.0 compares equal to +0.0.
  *   score   [units, K] fp32 out: the selected sums, or NULL.
  *   weight  [units, K] fp32 out: exp(score_j - score_0) / sum_l exp(...).
- * units = 0 is a valid no-op. */
+ * units = 0 is a valid no-op (x1, x2, idx, score and weight may then be NULL). */
 int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, int32_t* idx,
                float* score, float* weight, void* stream);
 
@@ -104,7 +104,7 @@ int sdm_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N,
  * Rows not selected for writing are never touched.  Row indices outside
  * [0, N) are skipped (no access; a skipped read row contributes 0); repeated
  * write rows within one step leave those rows unspecified.  T = 0 is a
- * valid no-op.  The caller may split a sequence into consecutive calls over
+ * valid no-op (the per-step arrays may then be NULL).  The caller may split a sequence into consecutive calls over
  * consecutive time ranges; the result is identical. */
 int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
              const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
@@ -173,7 +173,8 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  *   G[f_j] = alpha*(1 - beta*k_j)*g;   dr_l = <dout_t, M_t[g_l]>.
  * Arithmetic in fp32; the tile partial sums are added in a fixed order, so
  * results are deterministic.  Sizes as for sdm_scan, plus T < 2^26 and
- * B*H*T < 2^33. */
+ * B*H*T < 2^33.  T = 0 is a valid no-op (M and G unchanged; every per-step
+ * array and the workspace may then be NULL). */
 int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,
                       const float* rw, const float* v, const float* alpha, const float* beta,
@@ -186,7 +187,8 @@ int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int
  *   idx, weight  [units, K] from sdm_select;  dweight [units, K] fp32 in.
  *   dx1, dx2     [units, n] fp32 out: with dsigma_j = w_j*(dw_j - sum_l w_l dw_l),
  *                dx1[a] = sum of dsigma_j over the j with a_j = a (dx2 with
- *                b_j), zero at every half index no selected slot uses. */
+ *                b_j), zero at every half index no selected slot uses.
+ * units = 0 is a valid no-op (the arrays may then be NULL). */
 int sdm_select_backward(const int32_t* idx, const float* weight, const float* dweight,
                         int64_t units, int n, int K, float* dx1, float* dx2, void* stream);
 

@@ -103,10 +103,11 @@ const char* sdm_last_error(void) { return g_err; }
 int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, int32_t* idx,
                float* score, float* weight, void* stream) {
   int rc;
-  if ((rc = check_scores(x1, n, "x1")) || (rc = check_scores(x2, n, "x2"))) return rc;
-  if (!idx || !weight) return fail(SDM_ERR_INVALID, "idx and weight must not be NULL");
   if (units < 0) return fail(SDM_ERR_INVALID, "units must be >= 0");
   if ((rc = check_n_k(n, K, "K"))) return rc;
+  if (units == 0) return finish("sdm_select", hipSuccess, (hipStream_t)stream);  // arrays may be NULL
+  if ((rc = check_scores(x1, n, "x1")) || (rc = check_scores(x2, n, "x2"))) return rc;
+  if (!idx || !weight) return fail(SDM_ERR_INVALID, "idx and weight must not be NULL");
   if (units > ((int64_t)1 << 32)) return fail(SDM_ERR_INVALID, "units above 2^32");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_select", sdm::launch_select(x1, x2, units, n, K, idx, score, weight, s), s);
@@ -133,7 +134,9 @@ int check_scan_args(const void* M, int dtype, int B, int H, int64_t N, int d_v, 
                     const float* out) {
   int rc;
   if ((rc = check_state(M, dtype, N, d_v))) return rc;
-  if (!widx || !wk || !ridx || !rw || !v || !alpha || !beta || !out)
+  if (T < 0) return fail(SDM_ERR_INVALID, "T must be >= 0");
+  // with T = 0 every per-step array is empty and may be NULL
+  if (T > 0 && (!widx || !wk || !ridx || !rw || !v || !alpha || !beta || !out))
     return fail(SDM_ERR_INVALID, "a scan input or output pointer is NULL");
   if (!aligned(v, 16) || !aligned(out, 16))
     return fail(SDM_ERR_INVALID, "v and out must be 16-byte aligned");
@@ -177,7 +180,7 @@ int sdm_scan_train(void* M, int B, int H, int64_t N, int d_v, int64_t T, int W, 
   if ((rc = check_scan_args(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
                             beta, out)))
     return rc;
-  if (!tape) return fail(SDM_ERR_INVALID, "tape is NULL");
+  if (T > 0 && !tape) return fail(SDM_ERR_INVALID, "tape is NULL");
   if (!aligned(tape, 16)) return fail(SDM_ERR_INVALID, "tape must be 16-byte aligned");
   if (T * W * d_v * 4 >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*W*d_v*4 bytes) must be below 2 GiB; "
@@ -204,7 +207,8 @@ int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int
   if ((rc = check_scan_args(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
                             beta, dv)))
     return rc;
-  if (!tape || !dout || !G || !dwk || !drw || !dalpha || !dbeta || !workspace)
+  if (!G) return fail(SDM_ERR_INVALID, "G is NULL");
+  if (T > 0 && (!tape || !dout || !dwk || !drw || !dalpha || !dbeta || !workspace))
     return fail(SDM_ERR_INVALID, "a backward input or output pointer is NULL");
   if (!aligned(tape, 16) || !aligned(dout, 16) || !aligned(G, 16) || !aligned(workspace, 16))
     return fail(SDM_ERR_INVALID, "tape, dout, G and workspace must be 16-byte aligned");
@@ -231,6 +235,10 @@ int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int
 int sdm_select_backward(const int32_t* idx, const float* weight, const float* dweight,
                         int64_t units, int n, int K, float* dx1, float* dx2, void* stream) {
   int rc;
+  if (units < 0) return fail(SDM_ERR_INVALID, "units must be >= 0");
+  if ((rc = check_n_k(n, K, "K"))) return rc;
+  if (units == 0)  // the arrays are empty and may be NULL
+    return finish("sdm_select_backward", hipSuccess, (hipStream_t)stream);
   if (!idx || !weight || !dweight || !dx1 || !dx2)
     return fail(SDM_ERR_INVALID, "a selection-gradient pointer is NULL");
   if (!aligned(idx, 4) || !aligned(weight, 4) || !aligned(dweight, 4) || !aligned(dx1, 4) ||

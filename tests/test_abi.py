@@ -168,3 +168,20 @@ def test_fp8_state_validation():
     ok = [FAKE, 1, 1, 1, 64, 128, 8, 8] + [FAKE] * 8 + [None, None, None]
     ok[1] = 2
     assert L.sdm_step_decode(*ok) == 2 and "decode" in _err()
+
+
+def test_zero_length_calls_accept_null_arrays():
+    """T = 0 and units = 0 are no-ops whose empty arrays may be NULL (what an
+    empty tensor hands over); sizes and the state pointer are still checked."""
+    L = sdm.lib()
+    assert L.sdm_select(None, None, 0, 64, 8, None, None, None, None) == 0
+    assert L.sdm_select(None, None, 0, 64, 65, None, None, None, None) == 1  # K still checked
+    assert L.sdm_select_backward(None, None, None, 0, 64, 8, None, None, None) == 0
+    null9 = [None] * 8
+    assert L.sdm_scan(FAKE, 0, 1, 1, 4096, 16, 0, 8, 8, *null9, None) == 0
+    assert L.sdm_scan(None, 0, 1, 1, 4096, 16, 0, 8, 8, *null9, None) == 1  # M still required
+    assert L.sdm_scan_train(FAKE, 1, 1, 4096, 16, 0, 8, 8, *null9, None, None) == 0
+    args = [FAKE, 1, 1, 4096, 16, 0, 8, 8] + [None] * 9 + [FAKE] + [None] * 6 + [0, None]
+    assert L.sdm_scan_backward(*args) == 0
+    args[17] = None  # G is state-sized and still required
+    assert L.sdm_scan_backward(*args) == 1

@@ -196,3 +196,31 @@ def test_chunked_training_bitwise():
     assert torch.equal(M2, M) and torch.equal(M, sdm.state_init(M0, cfg.B))
     for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
         assert torch.equal(torch.cat([parts[0][k], parts[T1][k]], dim=2), whole[k]), k
+
+
+def test_training_degenerate_sizes():
+    """T = 0 calls are no-ops that leave every buffer as it was; W = R = 1
+    (single slot per step, weights exactly 1) matches the oracle; a selection
+    gradient over zero units is a no-op."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(B=1, H=2, n=16, d_v=32, T=50, W=1, R=1, seed=9400)
+    _train_case(cfg, seed_g=3)
+
+    B, H, N, d_v, W, R = 1, 2, 256, 32, 4, 4
+    M = torch.randn((B, H, N, d_v), device="cuda")
+    G = torch.randn_like(M)
+    M_before, G_before = M.clone(), G.clone()
+    e = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
+    widx, ridx = e(B, H, 0, W, dt=torch.int32), e(B, H, 0, R, dt=torch.int32)
+    wk, rw = e(B, H, 0, W), e(B, H, 0, R)
+    v, a, b = e(B, H, 0, d_v), e(B, H, 0), e(B, H, 0)
+    out, tape = sdm.scan_train(M, widx, wk, ridx, rw, v, a, b)
+    gr = sdm.scan_backward(M, widx, wk, ridx, rw, v, a, b, tape, e(B, H, 0, d_v), G)
+    d1, d2 = sdm.select_backward(e(0, 8, dt=torch.int32), e(0, 8), e(0, 8), 16)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and tape.numel() == 0 and gr["dv"].numel() == 0
+    assert d1.shape == (0, 16) and d2.shape == (0, 16)
+    assert torch.equal(M, M_before) and torch.equal(G, G_before)

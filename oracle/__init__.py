@@ -45,7 +45,7 @@ def _L():
         lib.oracle_scan.argtypes = [p, i32, i64, i32, i64, i32, i32, p, p, p, p, p, p, p, p,
                                     i32, i32]
         lib.oracle_step_decode.argtypes = [p, i32, i32, i32, i32, i32, i32, i32] + [p] * 10
-        lib.oracle_scan_backward.argtypes = [p, i64, i32, i64, i32, i32] + [p] * 16
+        lib.oracle_scan_backward.argtypes = [p, i64, i32, i64, i32, i32] + [p] * 17
         lib.oracle_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p]
         lib.oracle_last_error.restype = ctypes.c_char_p
         lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
@@ -179,7 +179,8 @@ def scan_backward(M0, widx, wk, ridx, rw, v, alpha, beta, dout, dMT=None):
     with respect to the read outputs; dMT [N,d_v] (default zero): with respect
     to the memory after the last step.  Returns a dict with dM0 [N,d_v],
     dv [T,d_v], dwk [T,W], drw [T,R], dalpha [T], dbeta [T] (all float64),
-    tape [T,W,d_v] (the pre-write rows, float32) and MT (the final memory)."""
+    tape [T,W,d_v] (the pre-write rows, float32), rtape [T,R,d_v] (the rows
+    each step's read saw, after its write, float32) and MT (the final memory)."""
     M0 = _c(M0, np.float32)
     N, d_v = M0.shape
     widx, ridx = _c(widx, np.int32), _c(ridx, np.int32)
@@ -196,13 +197,14 @@ def scan_backward(M0, widx, wk, ridx, rw, v, alpha, beta, dout, dMT=None):
     da = np.empty((T,), np.float64)
     db = np.empty((T,), np.float64)
     tape = np.empty((T, W, d_v), np.float32)
+    rtape = np.empty((T, R, d_v), np.float32)
     MT = np.empty((N, d_v), np.float32)
     _check(_L().oracle_scan_backward(_ptr(M0), N, d_v, T, W, R, _ptr(widx), _ptr(wk), _ptr(ridx),
                                      _ptr(rw), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(dout),
                                      _ptr(G), _ptr(dv), _ptr(dwk), _ptr(drw), _ptr(da), _ptr(db),
-                                     _ptr(tape), _ptr(MT)))
+                                     _ptr(tape), _ptr(rtape), _ptr(MT)))
     return {"dM0": G, "dv": dv, "dwk": dwk, "drw": drw, "dalpha": da, "dbeta": db,
-            "tape": tape, "MT": MT}
+            "tape": tape, "rtape": rtape, "MT": MT}
 
 
 def select_backward(idx, weight, dweight, n: int):

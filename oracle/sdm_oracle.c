@@ -376,14 +376,15 @@ int oracle_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, 
 /* One memory.  M0 [N,d_v] fp32: the memory before step 0.  G [N,d_v] double:
  * in, the gradient with respect to the memory after step T-1; out, with
  * respect to M0.  dout, dv [T,d_v]; dwk [T,W]; drw [T,R]; dalpha, dbeta [T].
- * tape [T,W,d_v] (may be NULL): the pre-write rows of every step.  MT [N,d_v]
- * (may be NULL): the memory after step T-1. */
+ * tape [T,W,d_v] (may be NULL): the pre-write rows of every step.  rtape
+ * [T,R,d_v] (may be NULL): the rows every step's read saw (after its write).
+ * MT [N,d_v] (may be NULL): the memory after step T-1. */
 int oracle_scan_backward(const float* M0, int64_t N, int d_v, int64_t T, int W, int R,
                          const int32_t* widx, const double* wk, const int32_t* ridx,
                          const double* rw, const float* v, const float* alpha,
                          const float* beta, const float* dout, double* G, double* dv,
                          double* dwk, double* drw, double* dalpha, double* dbeta, float* tape,
-                         float* MT) {
+                         float* rtape, float* MT) {
   if (!M0 || !widx || !wk || !ridx || !rw || !v || !alpha || !beta || !dout || !G || !dv ||
       !dwk || !drw || !dalpha || !dbeta)
     return fail("null pointer");
@@ -435,6 +436,7 @@ int oracle_scan_backward(const float* M0, int64_t N, int d_v, int64_t T, int W, 
       double s = 0.0;
       for (int c = 0; c < d_v; ++c) s += (double)dot[c] * (double)row[c];
       drw[t * R + j] = s;
+      if (rtape) memcpy(rtape + (t * R + j) * d_v, row, sizeof(float) * (size_t)d_v);
     }
     for (int j = 0; j < R; ++j) {
       double* g = G + (int64_t)ridx[t * R + j] * d_v;

@@ -18,7 +18,7 @@ int oracle_step_decode(void*, int, int, int, int, int, int, int, const float*, c
 int oracle_scan_backward(const float*, int64_t, int, int64_t, int, int, const int32_t*,
                          const double*, const int32_t*, const double*, const float*, const float*,
                          const float*, const float*, double*, double*, double*, double*, double*,
-                         double*, float*, float*);
+                         double*, float*, float*, float*);
 int oracle_select_backward(const int32_t*, const double*, const double*, int64_t, int, int,
                            double*, double*);
 const char* oracle_last_error(void);
@@ -69,17 +69,18 @@ int main(void) {
   double *dwk = malloc(sizeof(double) * T * W), *drw = malloc(sizeof(double) * T * R);
   double *da = malloc(sizeof(double) * T), *db = malloc(sizeof(double) * T);
   float *tape = malloc(sizeof(float) * T * W * D), *MT = malloc(sizeof(float) * N * D);
+  float *rtape = malloc(sizeof(float) * T * R * D);
   CHECK(oracle_scan_backward(M0, N, D, T, W, R, wi, wk, ri, rw, v, al, be, dout, G, dv, dwk, drw,
-                             da, db, tape, MT));
+                             da, db, tape, rtape, MT));
   double *dx1 = malloc(sizeof(double) * T * n), *dx2 = malloc(sizeof(double) * T * n);
   CHECK(oracle_select_backward(wi, wk, dwk, T, n, W, dx1, dx2));
   /* a rejected call must fail cleanly */
   wi[3] = wi[4];
   if (oracle_scan_backward(M0, N, D, T, W, R, wi, wk, ri, rw, v, al, be, dout, G, dv, dwk, drw, da,
-                           db, NULL, NULL) == 0) return 2;
+                           db, NULL, NULL, NULL) == 0) return 2;
   free(s1); free(s2); free(q1); free(q2); free(v); free(al); free(be); free(M0); free(dout);
   free(wi); free(ri); free(wk); free(rw); free(ws); free(G); free(dv); free(dwk); free(drw);
-  free(da); free(db); free(tape); free(MT); free(dx1); free(dx2);
+  free(da); free(db); free(tape); free(rtape); free(MT); free(dx1); free(dx2);
   puts("ok");
   return 0;
 }

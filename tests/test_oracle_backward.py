@@ -7,7 +7,8 @@ The oracle is checked against things other than itself:
   * the adjoint identity of the part that is linear in (M0, v), against the
     oracle's own forward scan (a separate function);
   * closed forms for alpha = 1, beta = 0 and for a single untouched row;
-  * the tape (pre-write rows) against step-by-step forward runs;
+  * the tape (pre-write rows) and the read rows against step-by-step
+    forward runs and the forward's outputs;
   * the softmax-through-halves gradient against finite differences.
 """
 import numpy as np
@@ -181,6 +182,26 @@ def test_tape_holds_pre_write_rows():
                     case["ridx"][t:t + 1], case["rw"][t:t + 1], case["v"][t:t + 1],
                     case["alpha"][t:t + 1], case["beta"][t:t + 1])
     assert np.array_equal(g["MT"], M)
+
+
+def test_read_rows_are_what_each_read_saw():
+    """rtape[t, j] is row ridx[t, j] of the memory after step t's write: equal
+    to a step-by-step run of the forward oracle, and its rw-weighted sum is
+    that forward's output (the read of "Meccanismo Core" item 4)."""
+    rng = np.random.default_rng(9)
+    T, d_v = 14, 6
+    case = _case(rng, N=12, d_v=d_v, T=T, W=4, R=5)
+    g = _bwd(case, np.zeros((T, d_v), np.float32), None)
+    M = case["M0"].copy()
+    outs = []
+    for t in range(T):
+        outs.append(oracle.scan(M, oracle.F32, case["widx"][t:t + 1], case["wk"][t:t + 1],
+                                case["ridx"][t:t + 1], case["rw"][t:t + 1], case["v"][t:t + 1],
+                                case["alpha"][t:t + 1], case["beta"][t:t + 1])[0])
+        assert np.array_equal(g["rtape"][t], M[case["ridx"][t]])
+    weighted = np.einsum("tj,tjc->tc", case["rw"], g["rtape"].astype(np.float64))
+    outs = np.array(outs, np.float64)  # binary32 outputs: one rounding each
+    assert np.all(np.abs(weighted - outs) <= 2.0 ** -23 * np.abs(outs))
 
 
 def test_backward_rejects_repeated_read_rows():

@@ -370,7 +370,7 @@ def run_train(cfg, args, torch, S, sdm):
     M = torch.empty((B, H, N, d_v), dtype=f32, device=dev)
     G = torch.empty((B, H, N, d_v), dtype=f32, device=dev)
     dM0 = torch.empty((H, N, d_v), dtype=f32, device=dev)
-    tape = torch.empty((B, H, T, W, d_v), dtype=f32, device=dev)
+    tape = torch.empty((B, H, T, W + R, d_v), dtype=f32, device=dev)
     widx = torch.empty((B, H, T, W), dtype=torch.int32, device=dev)
     wk = torch.empty((B, H, T, W), dtype=f32, device=dev)
     ridx = torch.empty((B, H, T, R), dtype=torch.int32, device=dev)
@@ -402,7 +402,7 @@ def run_train(cfg, args, torch, S, sdm):
         e[5].record(stream)
         G.zero_()
         e[6].record(stream)
-        g = sdm.scan_backward(M, widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], tape,
+        g = sdm.scan_backward(widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], tape,
                               inp["dout"], G, workspace=ws, stream=stream)
         e[7].record(stream)
         sdm.select_backward(widx, wk, g["dwk"], n, stream=stream)
@@ -430,8 +430,11 @@ def run_train(cfg, args, torch, S, sdm):
     bd = {"state_init": avg(0, 1), "select_write_read": avg(2, 3), "scan_train": avg(4, 5),
           "zero_G": avg(5, 6), "scan_backward": avg(6, 7), "select_backward": avg(7, 8),
           "state_init_backward": avg(8, 9), "overlap": "select || state_init"}
-    bwd_bytes = B * H * T * (4 * W + 3 * R) * d_v * 4
-    fwd_bytes = B * H * T * (3 * W + R) * d_v * 4
+    # reverse: G's W + R rows read and written, the tape's W + R rows read;
+    # forward with tape: M's W rows read and written and R rows read, W + R
+    # tape rows written
+    bwd_bytes = B * H * T * (3 * W + 3 * R) * d_v * 4
+    fwd_bytes = B * H * T * (3 * W + 2 * R) * d_v * 4
     gbps = bwd_bytes / (bd["scan_backward"] * 1e-3) / 1e9
     workload = (f"{cfg.name} training step: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
                 f"f32 state")

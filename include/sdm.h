@@ -133,10 +133,13 @@ int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int
  * chosen slots are piecewise constant in the scores; gradients reach the
  * scores through the selection weights only).  fp32 state only. */
 
-/* sdm_scan (fp32 state) that also keeps every step's pre-write rows.
- *   tape  [B, H, T, W, d_v] fp32 out: tape[b,h,t,j] = the stored row
- *         widx[b,h,t,j] just before step t's write (rows outside [0, N) are
- *         not written).  One memory's tape, T*W*d_v*4 bytes, must be below
+/* sdm_scan (fp32 state) that also keeps, per step, the rows the reverse pass
+ * needs, so that the reverse pass never reads or writes the state.
+ *   tape  [B, H, T, W + R, d_v] fp32 out: for j < W, tape[b,h,t,j] = the
+ *         stored row widx[b,h,t,j] just before step t's write; for j < R,
+ *         tape[b,h,t,W+j] = the stored row ridx[b,h,t,j] as step t's read
+ *         used it (after the write).  Slots of rows outside [0, N) are not
+ *         written.  One memory's tape, T*(W+R)*d_v*4 bytes, must be below
  *         2 GiB (split longer sequences into consecutive calls).
  * Every other argument and output is as for sdm_scan, and the results are
  * identical to it. */
@@ -148,14 +151,14 @@ int sdm_scan_train(void* M, int B, int H, int64_t N, int d_v, int64_t T, int W, 
 /* Bytes of workspace sdm_scan_backward needs for these sizes. */
 size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W, int R);
 
-/* Reverse pass over T steps, t = T-1 .. 0, for every (b,h) memory.
- *   M      [B, H, N, d_v] fp32 in/out: the state after the forward's last
- *          step; rolled back in place from the tape, it ends bit-identical to
- *          the state before the forward's first step.
+/* Reverse pass over T steps, t = T-1 .. 0, for every (b,h) memory.  It takes
+ * every row value it needs from the tape; the state itself is not an
+ * argument (the caller's state keeps whatever the forward left in it).
  *   widx, wk, ridx, rw, v, alpha, beta: the forward's inputs (shapes as for
  *          sdm_scan).  The rows of each step's widx must be distinct, and so
  *          must those of each step's ridx (sdm_select guarantees both).
- *   tape   [B, H, T, W, d_v] fp32 in: from sdm_scan_train on the same inputs.
+ *   tape   [B, H, T, W + R, d_v] fp32 in: from sdm_scan_train on the same
+ *          inputs.
  *   dout   [B, H, T, d_v] fp32 in: dL/d out.
  *   G      [B, H, N, d_v] fp32 in/out: in, dL/d(state after step T-1) (zeros
  *          when the final state is not used); out, dL/d(state before step 0).
@@ -170,12 +173,13 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  * the step's read contributions G[g_l] += r_l * dout_t:
  *   dv_t += beta*k_j*g;  dalpha_t += (1 - beta*k_j)*<g, P>;
  *   dk_j = beta*<g, v_t - alpha*P>;  dbeta_t += k_j*<g, v_t - alpha*P>;
- *   G[f_j] = alpha*(1 - beta*k_j)*g;   dr_l = <dout_t, M_t[g_l]>.
+ *   G[f_j] = alpha*(1 - beta*k_j)*g;   dr_l = <dout_t, M_t[g_l]>, with
+ * P and M_t[g_l] read from the tape.
  * Arithmetic in fp32; the tile partial sums are added in a fixed order, so
  * results are deterministic.  Sizes as for sdm_scan, plus T < 2^26 and
- * B*H*T < 2^33.  T = 0 is a valid no-op (M and G unchanged; every per-step
- * array and the workspace may then be NULL). */
-int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+ * B*H*T < 2^33.  T = 0 is a valid no-op (G unchanged; every per-step array
+ * and the workspace may then be NULL). */
+int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,
                       const float* rw, const float* v, const float* alpha, const float* beta,
                       const float* tape, const float* dout, float* G, float* dv, float* dwk,

@@ -25,6 +25,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdm.so")
+ABI_VERSION = 2  # the library's sdm_abi_version() this binding is written for
 
 SDM_F32 = 0
 SDM_BF16 = 1
@@ -61,7 +62,7 @@ def lib():
         L.sdm_scan_train.argtypes = [p, i32, i32, i64, i32, i64, i32, i32] + [p] * 10
         L.sdm_scan_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32, i32]
         L.sdm_scan_backward_workspace_size.restype = ctypes.c_size_t
-        L.sdm_scan_backward.argtypes = ([p, i32, i32, i64, i32, i64, i32, i32] + [p] * 16 +
+        L.sdm_scan_backward.argtypes = ([i32, i32, i64, i32, i64, i32, i32] + [p] * 16 +
                                         [ctypes.c_size_t, p])
         L.sdm_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p, p]
         L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p]
@@ -73,6 +74,9 @@ def lib():
         L.sdm_status_string.restype = ctypes.c_char_p
         L.sdm_last_error.argtypes = []
         L.sdm_last_error.restype = ctypes.c_char_p
+        if L.sdm_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI {L.sdm_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -225,6 +229,11 @@ def _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta):
     return B, H, N, d_v, T, W, R
 
 
+def _tape_shape(tape, shp):
+    if tuple(tape.shape) != shp:
+        raise ValueError(f"tape must be {shp}, got {tuple(tape.shape)}")
+
+
 def _scan_ptrs(widx, wk, ridx, rw, v, alpha, beta):
     import torch
 
@@ -235,15 +244,17 @@ def _scan_ptrs(widx, wk, ridx, rw, v, alpha, beta):
 
 
 def scan_train(M, widx, wk, ridx, rw, v, alpha, beta, out=None, tape=None, stream=None):
-    """scan() on an fp32 state that also keeps every step's pre-write rows:
-    returns (out [B,H,T,d_v], tape [B,H,T,W,d_v])."""
+    """scan() on an fp32 state that also keeps, per step, the W pre-write rows
+    and the R rows the read used: returns (out [B,H,T,d_v],
+    tape [B,H,T,W+R,d_v])."""
     import torch
 
     B, H, N, d_v, T, W, R = _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta)
     if out is None:
         out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
     if tape is None:
-        tape = torch.empty((B, H, T, W, d_v), dtype=torch.float32, device=M.device)
+        tape = torch.empty((B, H, T, W + R, d_v), dtype=torch.float32, device=M.device)
+    _tape_shape(tape, (B, H, T, W + R, d_v))
     _check(lib().sdm_scan_train(_dev(M, torch.float32, "M", 4), B, H, N, d_v, T, W, R,
                                 *_scan_ptrs(widx, wk, ridx, rw, v, alpha, beta),
                                 _dev(out, torch.float32, "out"),
@@ -251,16 +262,17 @@ def scan_train(M, widx, wk, ridx, rw, v, alpha, beta, out=None, tape=None, strea
     return out, tape
 
 
-def scan_backward(M, widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=None,
+def scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=None,
                   stream=None):
-    """Reverse pass: M (state after the forward) is rolled back in place to
-    the state before it; G (dL/d final state) becomes dL/d initial state.
+    """Reverse pass from the tape of scan_train (the state is not needed):
+    G (dL/d final state, [B,H,N,d_v]) becomes dL/d initial state in place.
     Returns dict dv [B,H,T,d_v], dwk [B,H,T,W], drw [B,H,T,R], dalpha,
     dbeta [B,H,T]."""
     import torch
 
-    B, H, N, d_v, T, W, R = _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta)
-    dev = M.device
+    B, H, N, d_v, T, W, R = _scan_shapes(G, widx, wk, ridx, rw, v, alpha, beta)
+    _tape_shape(tape, (B, H, T, W + R, d_v))
+    dev = G.device
     f32 = torch.float32
     o = {"dv": torch.empty((B, H, T, d_v), dtype=f32, device=dev),
          "dwk": torch.empty((B, H, T, W), dtype=f32, device=dev),
@@ -271,7 +283,7 @@ def scan_backward(M, widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspac
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=f32, device=dev)
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().sdm_scan_backward(_dev(M, f32, "M", 4), B, H, N, d_v, T, W, R,
+    _check(lib().sdm_scan_backward(B, H, N, d_v, T, W, R,
                                    *_scan_ptrs(widx, wk, ridx, rw, v, alpha, beta),
                                    _dev(tape, f32, "tape"), _dev(dout, f32, "dout"),
                                    _dev(G, f32, "G", 4), o["dv"].data_ptr(), o["dwk"].data_ptr(),

@@ -86,7 +86,7 @@ int64_t elem_bytes(int dtype) { return dtype == SDM_F32 ? 4 : (dtype == SDM_BF16
 
 extern "C" {
 
-int sdm_abi_version(void) { return 1; }
+int sdm_abi_version(void) { return 2; }
 
 const char* sdm_status_string(int status) {
   switch (status) {
@@ -182,8 +182,8 @@ int sdm_scan_train(void* M, int B, int H, int64_t N, int d_v, int64_t T, int W, 
     return rc;
   if (T > 0 && !tape) return fail(SDM_ERR_INVALID, "tape is NULL");
   if (!aligned(tape, 16)) return fail(SDM_ERR_INVALID, "tape must be 16-byte aligned");
-  if (T * W * d_v * 4 >= ((int64_t)1 << 31))
-    return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*W*d_v*4 bytes) must be below 2 GiB; "
+  if (T * (W + R) * d_v * 4 >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*(W+R)*d_v*4 bytes) must be below 2 GiB; "
                 "split the sequence into consecutive calls");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_scan_train",
@@ -197,17 +197,17 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
   return sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
 }
 
-int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,
                       const float* rw, const float* v, const float* alpha, const float* beta,
                       const float* tape, const float* dout, float* G, float* dv, float* dwk,
                       float* drw, float* dalpha, float* dbeta, void* workspace,
                       size_t workspace_bytes, void* stream) {
   int rc;
-  if ((rc = check_scan_args(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+  // G has the state's shape and type: it stands for the state in the shared checks
+  if ((rc = check_scan_args(G, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
                             beta, dv)))
     return rc;
-  if (!G) return fail(SDM_ERR_INVALID, "G is NULL");
   if (T > 0 && (!tape || !dout || !dwk || !drw || !dalpha || !dbeta || !workspace))
     return fail(SDM_ERR_INVALID, "a backward input or output pointer is NULL");
   if (!aligned(tape, 16) || !aligned(dout, 16) || !aligned(G, 16) || !aligned(workspace, 16))
@@ -217,8 +217,8 @@ int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int
   if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
   if ((int64_t)B * H * T >= ((int64_t)1 << 33))
     return fail(SDM_ERR_UNSUPPORTED, "B*H*T must be below 2^33 (one finishing wave per step)");
-  if (T * W * d_v * 4 >= ((int64_t)1 << 31))
-    return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*W*d_v*4 bytes) must be below 2 GiB; "
+  if (T * (W + R) * d_v * 4 >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*(W+R)*d_v*4 bytes) must be below 2 GiB; "
                 "split the sequence into consecutive calls");
   const size_t need = sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
   if (workspace_bytes < need)
@@ -226,7 +226,7 @@ int sdm_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int
                 workspace_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_scan_backward",
-                sdm::launch_scan_backward(M, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                sdm::launch_scan_backward(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
                                           beta, tape, dout, G, dv, dwk, drw, dalpha, dbeta,
                                           reinterpret_cast<float*>(workspace), s),
                 s);

@@ -14,19 +14,18 @@
 // Rows that a step does not write carry their gradient unchanged.
 //
 // scan_bwd_kernel walks t = T-1 .. 0 with one wavefront per (memory,
-// 32-column tile).  The state M (after the forward) is rolled back one step
-// at a time from the tape of pre-write rows that the training forward kept,
-// so a step's read sees exactly the stored values the forward read, and the
-// memory ends as it started.  The gradient table G (caller-owned, the shape
-// of M) starts as dL/dM_T and ends as dL/dM_0.  Each step gathers the read
-// rows of M and G and the write rows of G and of the tape (all 16-byte
-// buffer loads of one tile row per lane group), matches write rows against
-// this step's read rows through a hashed LDS table, and stores G's read
-// rows, then G's write rows, then M's restored rows -- in that order, so a
-// row that is both read and written ends with its write-side value.  All
-// accesses to a (row, tile) come from one wavefront, and the next step's
-// loads are issued after this step's stores, so program order keeps every
-// step's view current.  Per-tile partial sums of d(beta*k), dr and dalpha go
+// 32-column tile).  The training forward kept a tape of each step's W
+// pre-write rows and R read rows (the values the read used), so this pass
+// never touches the state M: every value it needs is on the tape, stored
+// contiguously per step.  The gradient table G (caller-owned, the shape of
+// M) starts as dL/dM_T and ends as dL/dM_0.  Each step gathers the read and
+// the write rows of G (16-byte buffer loads of one tile row per lane group)
+// and its tape rows, matches write rows against this step's read rows
+// through a hashed LDS table, and stores G's read rows, then G's write rows
+// -- in that order, so a row that is both read and written ends with its
+// write-side value.  All accesses to a (row, tile) of G come from one
+// wavefront, and the next step's loads are issued after this step's stores,
+// so program order keeps every step's view current.  Per-tile partial sums of d(beta*k), dr and dalpha go
 // to a caller-provided workspace; a finishing kernel adds the tiles in a
 // fixed order (deterministic) and applies beta and the k weights.  Nothing
 // here is a dense contraction: no MFMA.
@@ -99,7 +98,7 @@ __device__ __forceinline__ float col_sum(float x) {
 }
 
 template <int COLS>
-__global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, BwdArgs A) {
+__global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
   constexpr int LPR = COLS / 4;      // lanes per tile row (16 bytes each)
   constexpr int RPI = kWave / LPR;   // rows per wave instruction
   constexpr int NI = 64 / RPI;       // instructions for 64 row slots
@@ -122,13 +121,10 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
 
   const int64_t mem_elems = N * d_v;
   const int tile_bytes = tile * COLS * 4;
-  const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
-      M + (int64_t)mem * mem_elems + tile * COLS, 0, (int)(mem_elems * 4 - tile_bytes),
-      kBufWord3);
   const __amdgpu_buffer_rsrc_t gres = __builtin_amdgcn_make_buffer_rsrc(
       A.G + (int64_t)mem * mem_elems + tile * COLS, 0, (int)(mem_elems * 4 - tile_bytes),
       kBufWord3);
-  const int64_t tape_elems = T * W * d_v;
+  const int64_t tape_elems = T * (W + R) * d_v;  // per step: W pre-write rows, R read rows
   const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(A.tape) + (int64_t)mem * tape_elems + tile * COLS, 0,
       (int)(tape_elems * 4 - tile_bytes), kBufWord3);
@@ -181,7 +177,7 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
 
   for (int64_t t = T - 1; t >= 0; --t) {
     // ---- this step's offsets
-    uint32_t wrow[NI], wo[NI], ro[NI], to[NI];
+    uint32_t wrow[NI], wo[NI], ro[NI], to[NI], tr[NI];
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int j = k * RPI + lr;
@@ -189,13 +185,15 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
       wrow[k] = wv ? (uint32_t)fw_[k] : 0xFFFFFFFFu;
       wo[k] = wv ? (uint32_t)fw_[k] * row_bytes + lane_off : kOffNone;
       ro[k] = rv ? (uint32_t)fr_[k] * row_bytes + lane_off : kOffNone;
-      to[k] = wv ? ((uint32_t)t * (uint32_t)W + (uint32_t)j) * row_bytes + lane_off : kOffNone;
+      const uint32_t tstep = (uint32_t)t * (uint32_t)(W + R);
+      to[k] = wv ? (tstep + (uint32_t)j) * row_bytes + lane_off : kOffNone;
+      tr[k] = rv ? (tstep + (uint32_t)(W + j)) * row_bytes + lane_off : kOffNone;
     }
 
     // ---- gathers (all issued before any is used)
     u32x4 Mg[NI], Gg[NI], Gf[NI], P[NI];
 #pragma unroll
-    for (int k = 0; k < NI; ++k) Mg[k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ro[k], 0, 0);
+    for (int k = 0; k < NI; ++k) Mg[k] = __builtin_amdgcn_raw_buffer_load_b128(tres, tr[k], 0, 0);
 #pragma unroll
     for (int k = 0; k < NI; ++k) Gg[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, ro[k], 0, 0);
 #pragma unroll
@@ -283,13 +281,11 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(float* __restrict__ M, 
       const float c = a * (1.0f - bk);
       Gf[k] = as_u4(f32x4{c * g.x, c * g.y, c * g.z, c * g.w});
     }
-    // ---- stores: G read rows, then G write rows, then the restored M rows
+    // ---- stores: G read rows, then G write rows
 #pragma unroll
     for (int k = 0; k < NI; ++k) __builtin_amdgcn_raw_buffer_store_b128(Gg[k], gres, ro[k], 0, 0);
 #pragma unroll
     for (int k = 0; k < NI; ++k) __builtin_amdgcn_raw_buffer_store_b128(Gf[k], gres, wo[k], 0, 0);
-#pragma unroll
-    for (int k = 0; k < NI; ++k) __builtin_amdgcn_raw_buffer_store_b128(P[k], mres, wo[k], 0, 0);
 
     // ---- reductions and the step's partial sums
     float* wst = wsm + t * (int64_t)A.ntiles * ws_row;
@@ -467,7 +463,7 @@ size_t scan_backward_workspace_bytes(int n_mem, int d_v, int64_t T, int W, int R
   return (size_t)n_mem * (size_t)T * (size_t)(d_v / cols) * (size_t)(W + R + 1) * sizeof(float);
 }
 
-hipError_t launch_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W,
+hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W,
                                 int R, const int32_t* widx, const float* wk,
                                 const int32_t* ridx, const float* rw, const float* v,
                                 const float* alpha, const float* beta, const float* tape,
@@ -480,9 +476,9 @@ hipError_t launch_scan_backward(float* M, int B, int H, int64_t N, int d_v, int6
   const int groups = (A.n_mem + 7) / 8;
   const int64_t blocks = (int64_t)groups * A.ntiles * 8;
   if (cols == 32)
-    hipLaunchKernelGGL((scan_bwd_kernel<32>), dim3((unsigned)blocks), dim3(kWave), 0, stream, M, A);
+    hipLaunchKernelGGL((scan_bwd_kernel<32>), dim3((unsigned)blocks), dim3(kWave), 0, stream, A);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<16>), dim3((unsigned)blocks), dim3(kWave), 0, stream, M, A);
+    hipLaunchKernelGGL((scan_bwd_kernel<16>), dim3((unsigned)blocks), dim3(kWave), 0, stream, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)A.n_mem * T;

@@ -25,7 +25,7 @@ hipError_t launch_step_decode(void* M, int dtype, int B, int H, int n, int d_v, 
 
 size_t scan_backward_workspace_bytes(int n_mem, int d_v, int64_t T, int W, int R);
 
-hipError_t launch_scan_backward(float* M, int B, int H, int64_t N, int d_v, int64_t T, int W,
+hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W,
                                 int R, const int32_t* widx, const float* wk,
                                 const int32_t* ridx, const float* rw, const float* v,
                                 const float* alpha, const float* beta, const float* tape,

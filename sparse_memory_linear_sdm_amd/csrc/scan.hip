@@ -42,7 +42,8 @@
 //             binary32 order with no contraction) and stores them, and
 //             accumulates the R read rows.  The training variant (SAVE)
 //             also stores each write row's current value, before the update,
-//             to the tape the reverse pass reads.  Rows the plan forwards come
+//             and each row the read uses, after it, to the tape the reverse
+//             pass reads (so that pass never touches M).  Rows the plan forwards come
 //             from a small LDS ring of saved updated rows instead of the
 //             (possibly stale) loaded values.  Loads of step u + D are issued after the
 //             stores of every step before u by the same wavefront, so the
@@ -132,7 +133,8 @@ struct ScanArgs {
   const float* alpha;
   const float* beta;
   float* out;
-  void* tape;  // training forward: pre-write rows [n_mem, T, W, d_v] in the state type
+  void* tape;  // training forward: [n_mem, T, W + R, d_v] in the state type: per step the
+              // W pre-write rows, then the R rows the read used
   int ntiles;
   int shards;  // 1, or 2: rows split between two workgroups by row_shard()
 };
@@ -403,7 +405,8 @@ struct Consumer {
   u32x4v rv[D + 1][NI];
   __amdgpu_buffer_rsrc_t mres;  // this memory's tile column, range = the memory slice
   __amdgpu_buffer_rsrc_t tres;  // SAVE: this memory's tape slice, shifted to the tile column
-  uint32_t tape_step;            // SAVE: bytes of one step's W tape rows
+  uint32_t tape_step;            // SAVE: bytes of one step's W + R tape rows
+  uint32_t read_base;            // SAVE: bytes before a step's first read row (W rows)
   uint32_t row_bytes;            // SAVE: bytes of one full row
   uint32_t lane_off;             // lc * 16
   bool accumulate;               // rows split over two workgroups: add into out
@@ -542,6 +545,16 @@ struct Consumer {
         if (src) rv[SLOT][k] = lds_u4(sh.upd[(src - 1) >> 6][((src - 1) & 63) * LPR + lc]);
       }
     }
+    if constexpr (SAVE) {  // the rows the read uses, for the reverse pass
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const uint32_t to = p.rofs[lr * NI + k] == kOffNone
+                                ? kOffNone
+                                : (uint32_t)u * tape_step + read_base +
+                                      (uint32_t)(k * RPI + lr) * row_bytes + lane_off;
+        __builtin_amdgcn_raw_buffer_store_b128(rv[SLOT][k], tres, to, 0, 0);
+      }
+    }
     // sparse read (invalid rows carry weight 0 and load as zero)
     float acc[EPL];
 #pragma unroll
@@ -578,8 +591,8 @@ struct Consumer {
       issue<S>(sh, lr, S, T);
       const u32x4v zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < (SAVE ? 2 : 1) * NI; ++k)  // distinct offsets: identical stores would be merged
-        __builtin_amdgcn_raw_buffer_store_b128(zero, mres, kOffNone + (uint32_t)(S * 2 * NI + k) * 16u,
+      for (int k = 0; k < (SAVE ? 3 : 1) * NI; ++k)  // distinct offsets: identical stores would be merged
+        __builtin_amdgcn_raw_buffer_store_b128(zero, mres, kOffNone + (uint32_t)(S * 3 * NI + k) * 16u,
                                                0, 0);
       prologue<S + 1>(sh, lr, T);
     }
@@ -664,8 +677,9 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   cs.lane_off = (uint32_t)(lc * 16);
   cs.accumulate = A.shards > 1;
   if constexpr (SAVE) {
-    const int64_t tape_mem = T * A.W * d_v;  // elements of one memory's tape
-    cs.tape_step = (uint32_t)(A.W * d_v * (int)sizeof(DT));
+    const int64_t tape_mem = T * (A.W + A.R) * d_v;  // elements of one memory's tape
+    cs.tape_step = (uint32_t)((A.W + A.R) * d_v * (int)sizeof(DT));
+    cs.read_base = (uint32_t)(A.W * d_v * (int)sizeof(DT));
     cs.row_bytes = (uint32_t)(d_v * (int)sizeof(DT));
     cs.tres = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<DT*>(A.tape) + (int64_t)mem * tape_mem + (int64_t)tile * COLS, 0,
@@ -691,7 +705,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, int64
 template <typename DT, int COLS, int D, bool SAVE>
 hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
   static_assert(D >= 1 && D <= kChunk, "prefetch depth");
-  static_assert((SAVE ? 4 : 3) * Tile<DT, COLS>::NI * D <= 63,
+  static_assert((SAVE ? 5 : 3) * Tile<DT, COLS>::NI * D <= 63,
                 "outstanding vector memory operations");
   A.ntiles = A.d_v / COLS;
   const int groups = (A.n_mem + 7) / 8;
@@ -744,7 +758,7 @@ hipError_t launch_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int
   const int cus = compute_units();
   const bool narrow = d_v == 16 || (int64_t)A.n_mem * (d_v / 16) <= cus;
   if (dtype != 2 && narrow && 2 * (int64_t)A.n_mem * (d_v / 16) <= cus) A.shards = 2;
-  if (tape) {  // training forward (fp32 state): also keep the pre-write rows
+  if (tape) {  // training forward (fp32 state): also keep the pre-write and the read rows
     if (!narrow) return launch<float, 32, 1, true>(M, A, stream);
     if (A.shards == 2) return launch<float, 16, 3, true>(M, A, stream);
     return launch<float, 16, 2, true>(M, A, stream);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = sdm.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.sdm_abi_version() == 1
+    assert L.sdm_abi_version() == 2
     assert L.sdm_status_string(0) == b"SDM_OK"
     assert L.sdm_status_string(2) == b"SDM_ERR_UNSUPPORTED"
 
@@ -128,25 +128,31 @@ def test_training_calls_validation():
     assert L.sdm_scan_train(*a) == 1  # tape misaligned
     a = list(ok); a[5] = 1 << 22; a[4] = 256; a[6] = 64
     assert L.sdm_scan_train(*a) == 2 and "tape" in _err()  # one memory's tape above 2 GiB
+    a = list(ok); a[4] = 128; a[5] = 40000; a[6] = 64; a[7] = 64
+    assert L.sdm_scan_train(*a) == 2 and "W+R" in _err()  # the read rows count too
     need = L.sdm_scan_backward_workspace_size(2, 4, 128, 100, 64, 32)
     assert need == 2 * 4 * 100 * 4 * (64 + 32 + 1) * 4  # 4 column tiles of 32
     assert L.sdm_scan_backward_workspace_size(1, 1, 16, 10, 8, 8) == 10 * 1 * 17 * 4
     assert L.sdm_scan_backward_workspace_size(1, 1, 48, 10, 8, 8) == 0
-    # sdm_scan_backward: M, B, H, N, d_v, T, W, R, 7 inputs, tape, dout, G, dv, dwk, drw,
-    # dalpha, dbeta, workspace, bytes, stream
+    # sdm_scan_backward: B, H, N, d_v, T, W, R, 7 inputs, tape, dout, G, dv, dwk, drw,
+    # dalpha, dbeta, workspace, bytes, stream (the state is not an argument)
     wsb = L.sdm_scan_backward_workspace_size(1, 1, 16, 8, 8, 8)
-    ok = [FAKE, 1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 16 + [wsb, None]
-    assert len(ok) == 26
-    a = list(ok); a[24] = wsb - 4
+    ok = [1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 16 + [wsb, None]
+    assert len(ok) == 25
+    a = list(ok); a[23] = wsb - 4
     assert L.sdm_scan_backward(*a) == 1 and "workspace" in _err()
-    a = list(ok); a[17] = None  # G
+    a = list(ok); a[16] = None  # G
     assert L.sdm_scan_backward(*a) == 1
-    a = list(ok); a[5] = 1 << 26
+    a = list(ok); a[14] = FAKE + 4  # tape misaligned
+    assert L.sdm_scan_backward(*a) == 1
+    a = list(ok); a[4] = 1 << 26
     assert L.sdm_scan_backward(*a) == 2
-    a = list(ok); a[1] = 1 << 12; a[2] = 1 << 12; a[5] = 1 << 10
+    a = list(ok); a[0] = 1 << 12; a[1] = 1 << 12; a[4] = 1 << 10
     assert L.sdm_scan_backward(*a) == 2 and "2^33" in _err()
-    a = list(ok); a[4] = 24
+    a = list(ok); a[3] = 24
     assert L.sdm_scan_backward(*a) == 2
+    a = list(ok); a[3] = 128; a[4] = 40000; a[5] = 64; a[6] = 64
+    assert L.sdm_scan_backward(*a) == 2 and "W+R" in _err()
     # sdm_select_backward: idx, w, dw, units, n, K, dx1, dx2, stream
     ok = [FAKE, FAKE, FAKE, 10, 64, 8, FAKE, FAKE, None]
     a = list(ok); a[6] = None
@@ -181,7 +187,7 @@ def test_zero_length_calls_accept_null_arrays():
     assert L.sdm_scan(FAKE, 0, 1, 1, 4096, 16, 0, 8, 8, *null9, None) == 0
     assert L.sdm_scan(None, 0, 1, 1, 4096, 16, 0, 8, 8, *null9, None) == 1  # M still required
     assert L.sdm_scan_train(FAKE, 1, 1, 4096, 16, 0, 8, 8, *null9, None, None) == 0
-    args = [FAKE, 1, 1, 4096, 16, 0, 8, 8] + [None] * 9 + [FAKE] + [None] * 6 + [0, None]
+    args = [1, 1, 4096, 16, 0, 8, 8] + [None] * 9 + [FAKE] + [None] * 6 + [0, None]
     assert L.sdm_scan_backward(*args) == 0
-    args[17] = None  # G is state-sized and still required
+    args[16] = None  # G is state-sized and still required
     assert L.sdm_scan_backward(*args) == 1

@@ -186,8 +186,9 @@ def test_mid_config_training_full_size():
     """The training step of the mid workload in the benchmark's launch
     configuration (64 memories of 2^20 x 128, T = 4096, gradient table
     zeroed, loss on the outputs): two memories' gradients checked in full
-    against the oracle's reverse pass, the state rolled back bitwise to M0
-    for every memory, and dM0 against the plain sum of the GPU's G."""
+    against the oracle's reverse pass (their tapes and final states too),
+    the state left bitwise as the forward ended it for every memory, and dM0
+    against the plain sum of the GPU's G."""
     import torch
 
     import sparse_memory_linear_sdm_amd as sdm
@@ -204,13 +205,12 @@ def test_mid_config_training_full_size():
     ridx, _, rw = sdm.select(d["q1"], d["q2"], cfg.R)
     out, tape = sdm.scan_train(M, widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"])
     G = torch.zeros_like(M)
-    gr = sdm.scan_backward(M, widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"], tape, dout, G)
-    del tape
+    M_end = M.clone()
+    gr = sdm.scan_backward(widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"], tape, dout, G)
     dM0 = sdm.state_init_backward(G)
     torch.cuda.synchronize()
-    for b in range(B):
-        for h in range(H):
-            assert torch.equal(M[b, h], M0[h]), f"state of b={b} h={h} not restored"
+    assert torch.equal(M, M_end), "the reverse pass must not touch the state"
+    del M_end
     for b, h in ((0, 0), (6, 3)):
         host = host_inputs(cfg, b, 1, h, 1)
         M0h = S.host_block(cfg, "M0", h0=h, nh=1)[0]
@@ -227,11 +227,14 @@ def test_mid_config_training_full_size():
         for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
             _grad_close(gr[k][b, h].cpu().numpy(), o[k], f"{tag} {k}")
         _grad_close(G[b, h].cpu().numpy(), o["dM0"], tag + " G")
+        check_values(M[b, h].cpu().numpy(), o["MT"], F32, tag + " final state")
+        check_values(tape[b, h, :, :cfg.W].cpu().numpy(), o["tape"], F32, tag + " tape")
+        check_values(tape[b, h, :, cfg.W:].cpu().numpy(), o["rtape"], F32, tag + " read tape")
         del o
     for h in (0, 5):
         want = oracle.state_init_backward(G[:, h:h + 1].cpu().numpy())[0]
         _grad_close(dM0[h].cpu().numpy(), want, f"dM0 h={h}")
-    del d, dout, M0, M, G, gr, dM0, widx, wk, ridx, rw, out
+    del d, dout, M0, M, G, gr, dM0, widx, wk, ridx, rw, out, tape
     _free()
 
 

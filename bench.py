@@ -2,7 +2,7 @@
 """Throughput of the Sparse Delta Memory step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config mid]
-                    [--no-cpu-baseline] [--train]
+                    [--no-cpu-baseline] [--train [--train-dense]]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: the learned-state copy M[b,h] = M0[h] (sdm_state_init),
@@ -348,9 +348,11 @@ def cpu_baseline_train(cfg, n_mem: int = 8):
 def run_train(cfg, args, torch, S, sdm):
     """One training step over one batch: the forward (state init, two
     selections beside it, the scan keeping its tape) and the reverse pass
-    (gradient table zeroed -- the loss reads the outputs only --, the reverse
-    scan, both selection-weight gradients to the halves, and the M0
-    gradient)."""
+    (the reverse scan, both selection-weight gradients to the halves, and the
+    M0 gradient).  The loss reads the outputs only, so the final-state
+    gradient is zero: in the sparse mode (default) the rows' last selections
+    are recorded beside the forward scan and the gradient table is never
+    cleared; --train-dense zeroes it instead and sums all of it."""
     dev = torch.device("cuda:0")
     B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
     if args.state != "f32":
@@ -378,6 +380,11 @@ def run_train(cfg, args, torch, S, sdm):
     out = torch.empty((B, H, T, d_v), dtype=f32, device=dev)
     wsb = int(sdm.lib().sdm_scan_backward_workspace_size(B, H, d_v, T, W, R))
     ws = torch.empty((wsb + 3) // 4, dtype=f32, device=dev)
+    sparse = not args.train_dense
+    last = torch.empty((B, H, N), dtype=torch.int32, device=dev) if sparse else None
+    first = torch.empty((B, H, T, 2), dtype=torch.int64, device=dev) if sparse else None
+    if sparse:
+        G.fill_(float("nan"))  # contents never read in this mode
     torch.cuda.synchronize()
     calibration_copy(args, torch, dev)
     stream = torch.cuda.current_stream()
@@ -397,18 +404,24 @@ def run_train(cfg, args, torch, S, sdm):
         e[3].record(side)
         stream.wait_event(e[3])
         e[4].record(stream)
+        if sparse:  # beside the forward scan: it reads the selections only
+            sdm.touch_prepare(widx, ridx, N, last=last, first=first, stream=side)
+            e[10].record(side)
         sdm.scan_train(M, widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], out=out,
                        tape=tape, stream=stream)
         e[5].record(stream)
-        G.zero_()
+        if sparse:
+            stream.wait_event(e[10])
+        else:
+            G.zero_()
         e[6].record(stream)
         g = sdm.scan_backward(widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], tape,
-                              inp["dout"], G, workspace=ws, stream=stream)
+                              inp["dout"], G, workspace=ws, first=first, stream=stream)
         e[7].record(stream)
         sdm.select_backward(widx, wk, g["dwk"], n, stream=stream)
         sdm.select_backward(ridx, rw, g["drw"], n, stream=stream)
         e[8].record(stream)
-        sdm.state_init_backward(G, out=dM0, stream=stream)
+        sdm.state_init_backward(G, out=dM0, last=last, stream=stream)
         e[9].record(stream)
         if record is not None:
             record.append(e)
@@ -428,18 +441,33 @@ def run_train(cfg, args, torch, S, sdm):
     ms_step = g0.elapsed_time(g1) / args.steps
     avg = lambda a, b: sum(r[a].elapsed_time(r[b]) for r in recs) / args.steps  # noqa: E731
     bd = {"state_init": avg(0, 1), "select_write_read": avg(2, 3), "scan_train": avg(4, 5),
-          "zero_G": avg(5, 6), "scan_backward": avg(6, 7), "select_backward": avg(7, 8),
+          "scan_backward": avg(6, 7), "select_backward": avg(7, 8),
           "state_init_backward": avg(8, 9), "overlap": "select || state_init"}
+    if sparse:
+        bd["touch_prepare"] = avg(4, 10)
+        bd["overlap"] += "; touch_prepare || scan_train"
+        bd["mode"] = "sparse (gradient table never cleared)"
+    else:
+        bd["zero_G"] = avg(5, 6)
+        bd["mode"] = "dense (gradient table zeroed)"
     # reverse: G's W + R rows read and written, the tape's W + R rows read;
     # forward with tape: M's W rows read and written and R rows read, W + R
-    # tape rows written
+    # tape rows written.  In the sparse mode a row's first touch in reverse
+    # reads no G: those gathers (counted from the masks) are not algorithmic.
     bwd_bytes = B * H * T * (3 * W + 3 * R) * d_v * 4
+    if sparse:
+        import numpy as np
+
+        fm = first.cpu().numpy().view(np.uint8)
+        skipped = int(np.unpackbits(fm).sum())
+        bwd_bytes -= skipped * d_v * 4
+        bd["first_touch_slots"] = skipped
     fwd_bytes = B * H * T * (3 * W + 2 * R) * d_v * 4
     gbps = bwd_bytes / (bd["scan_backward"] * 1e-3) / 1e9
     workload = (f"{cfg.name} training step: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
-                f"f32 state")
+                f"f32 state, {'sparse' if sparse else 'dense'} gradient table")
     traffic = (measured_traffic(bwd_bytes, BWD_TRAFFIC_FILE, BWD_SOURCES)
-               if cfg.name == "mid" else None)
+               if cfg.name == "mid" and sparse else None)
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": "scan_bwd_kernel<32> + scan_bwd_finish",
@@ -653,6 +681,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (forward with tape + reverse pass) instead")
+    ap.add_argument("--train-dense", action="store_true",
+                    help="with --train: zero the gradient table and sum all of it (dense mode)"
+                         " instead of the sparse-mode bookkeeping")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the step's kernels back to back on one stream")
     ap.add_argument("--pipeline", action="store_true",

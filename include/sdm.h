@@ -166,6 +166,14 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  *   dwk    [B, H, T, W] fp32 out: dL/dk (the write weights).
  *   drw    [B, H, T, R] fp32 out: dL/dr (the read weights).
  *   dalpha, dbeta [B, H, T] fp32 out.
+ *   first  NULL (dense mode: G holds dL/dM_T for every row on entry), or
+ *          [B, H, T, 2] uint64 from sdm_touch_prepare on the same widx and
+ *          ridx (sparse mode: dL/dM_T is taken as zero, and G's contents on
+ *          entry do not matter -- each row's first touch in reverse time
+ *          starts from zero instead of reading G).  In sparse mode, G holds
+ *          dL/dM_0 on exit only for the rows the T steps select (last >= 0);
+ *          the other rows keep whatever they held.  Both modes give the same
+ *          bits for every output and every selected row of G.
  *   workspace  device buffer of at least
  *          sdm_scan_backward_workspace_size(B, H, d_v, T, W, R) bytes,
  *          16-byte aligned; its contents on entry do not matter.
@@ -183,8 +191,8 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,
                       const float* rw, const float* v, const float* alpha, const float* beta,
                       const float* tape, const float* dout, float* G, float* dv, float* dwk,
-                      float* drw, float* dalpha, float* dbeta, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      float* drw, float* dalpha, float* dbeta, const uint64_t* first,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gradient of the selection weights back to the halves ("Meccanismo Core",
  * item 2: slot f = a*n + b scores x1[a] + x2[b]), selections held fixed.
@@ -198,9 +206,27 @@ int sdm_select_backward(const int32_t* idx, const float* weight, const float* dw
 
 /* Gradient of the per-sequence copy M[b,h] = M0[h]:
  *   dM0[h] = sum over b = 0, 1, ... of G[b,h].
- *   G [B, H, N, d_v] fp32 in;  dM0 [H, N, d_v] fp32 out (16-byte aligned). */
-int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v, float* dM0,
-                            void* stream);
+ *   G [B, H, N, d_v] fp32 in;  dM0 [H, N, d_v] fp32 out (16-byte aligned).
+ *   last  NULL (every row of G counts), or [B, H, N] int32 from
+ *         sdm_touch_prepare (sparse mode: row r of G[b,h] counts only when
+ *         last[b,h,r] >= 0, and is not read otherwise; the sum is the same
+ *         as the dense one with those rows zero). */
+int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
+                            const int32_t* last, float* dM0, void* stream);
+
+/* Bookkeeping for the sparse training mode (the method touches only W + R
+ * rows per step, "Meccanismo Core" items 3 and 4, so most of the gradient
+ * table is never touched by one sequence).
+ *   widx [B, H, T, W], ridx [B, H, T, R] int32 in: the forward's selections.
+ *   last  [B, H, N] int32 out: the last step at which row r is selected
+ *         (write or read), -1 if never.
+ *   first [B, H, T, 2] uint64 out: bit j of first[b,h,t,0] is set when
+ *         widx[b,h,t,j]'s last selection is step t; first[b,h,t,1] likewise
+ *         for ridx.
+ * 1 <= W, R <= 64; 0 <= T < 2^26 (T = 0 only fills last with -1; the index
+ * arrays and first may then be NULL).  Indices outside [0, N) are ignored. */
+int sdm_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R, const int32_t* widx,
+                      const int32_t* ridx, int32_t* last, uint64_t* first, void* stream);
 
 /* Static text for a status code. */
 const char* sdm_status_string(int status);

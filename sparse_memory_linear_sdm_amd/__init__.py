@@ -25,7 +25,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdm.so")
-ABI_VERSION = 2  # the library's sdm_abi_version() this binding is written for
+ABI_VERSION = 3  # the library's sdm_abi_version() this binding is written for
 
 SDM_F32 = 0
 SDM_BF16 = 1
@@ -35,7 +35,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_INVALID", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_E
 # Every symbol include/sdm.h declares.
 EXPORTS = ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_scan_train",
            "sdm_scan_backward_workspace_size", "sdm_scan_backward", "sdm_select_backward",
-           "sdm_state_init_backward", "sdm_status_string", "sdm_last_error", "sdm_abi_version")
+           "sdm_state_init_backward", "sdm_touch_prepare", "sdm_status_string", "sdm_last_error",
+           "sdm_abi_version")
 
 _lib = None
 
@@ -62,13 +63,14 @@ def lib():
         L.sdm_scan_train.argtypes = [p, i32, i32, i64, i32, i64, i32, i32] + [p] * 10
         L.sdm_scan_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32, i32]
         L.sdm_scan_backward_workspace_size.restype = ctypes.c_size_t
-        L.sdm_scan_backward.argtypes = ([i32, i32, i64, i32, i64, i32, i32] + [p] * 16 +
+        L.sdm_scan_backward.argtypes = ([i32, i32, i64, i32, i64, i32, i32] + [p] * 17 +
                                         [ctypes.c_size_t, p])
+        L.sdm_touch_prepare.argtypes = [i32, i32, i64, i64, i32, i32, p, p, p, p, p]
         L.sdm_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p, p]
-        L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p]
+        L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p, p]
         for f in ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode",
                   "sdm_abi_version", "sdm_scan_train", "sdm_scan_backward",
-                  "sdm_select_backward", "sdm_state_init_backward"):
+                  "sdm_select_backward", "sdm_state_init_backward", "sdm_touch_prepare"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i32]
         L.sdm_status_string.restype = ctypes.c_char_p
@@ -263,15 +265,19 @@ def scan_train(M, widx, wk, ridx, rw, v, alpha, beta, out=None, tape=None, strea
 
 
 def scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=None,
-                  stream=None):
+                  first=None, stream=None):
     """Reverse pass from the tape of scan_train (the state is not needed):
     G (dL/d final state, [B,H,N,d_v]) becomes dL/d initial state in place.
-    Returns dict dv [B,H,T,d_v], dwk [B,H,T,W], drw [B,H,T,R], dalpha,
-    dbeta [B,H,T]."""
+    With first (from touch_prepare) the final-state gradient is taken as
+    zero and G need not be cleared; only the rows the steps select are
+    written.  Returns dict dv [B,H,T,d_v], dwk [B,H,T,W], drw [B,H,T,R],
+    dalpha, dbeta [B,H,T]."""
     import torch
 
     B, H, N, d_v, T, W, R = _scan_shapes(G, widx, wk, ridx, rw, v, alpha, beta)
     _tape_shape(tape, (B, H, T, W + R, d_v))
+    if first is not None and tuple(first.shape) != (B, H, T, 2):
+        raise ValueError(f"first must be {(B, H, T, 2)}, got {tuple(first.shape)}")
     dev = G.device
     f32 = torch.float32
     o = {"dv": torch.empty((B, H, T, d_v), dtype=f32, device=dev),
@@ -288,10 +294,34 @@ def scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=N
                                    _dev(tape, f32, "tape"), _dev(dout, f32, "dout"),
                                    _dev(G, f32, "G", 4), o["dv"].data_ptr(), o["dwk"].data_ptr(),
                                    o["drw"].data_ptr(), o["dalpha"].data_ptr(),
-                                   o["dbeta"].data_ptr(), _dev(workspace, workspace.dtype,
-                                                               "workspace"),
+                                   o["dbeta"].data_ptr(),
+                                   None if first is None else _dev(first, torch.int64, "first"),
+                                   _dev(workspace, workspace.dtype, "workspace"),
                                    nbytes, _stream(stream)))
     return o
+
+
+def touch_prepare(widx, ridx, N: int, last=None, first=None, stream=None):
+    """Bookkeeping of the sparse training mode: last [B,H,N] int32 (the last
+    step that selects each row, -1 if none) and first [B,H,T,2] int64 (the
+    bits of the uint64 masks of slots whose row is selected for the last
+    time at that step)."""
+    import torch
+
+    B, H, T, W = widx.shape
+    R = ridx.shape[3]
+    if tuple(ridx.shape) != (B, H, T, R):
+        raise ValueError(f"ridx must be {(B, H, T, R)}, got {tuple(ridx.shape)}")
+    dev = widx.device
+    if last is None:
+        last = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    if first is None:
+        first = torch.empty((B, H, T, 2), dtype=torch.int64, device=dev)
+    _check(lib().sdm_touch_prepare(B, H, N, T, W, R, _dev(widx, torch.int32, "widx"),
+                                   _dev(ridx, torch.int32, "ridx"),
+                                   _dev(last, torch.int32, "last", 3),
+                                   _dev(first, torch.int64, "first", 4), _stream(stream)))
+    return last, first
 
 
 def select_backward(idx, weight, dweight, n: int, stream=None):
@@ -313,12 +343,16 @@ def select_backward(idx, weight, dweight, n: int, stream=None):
     return dx1, dx2
 
 
-def state_init_backward(G, out=None, stream=None):
-    """dM0 [H,N,d_v] = sum over b of G [B,H,N,d_v]."""
+def state_init_backward(G, out=None, last=None, stream=None):
+    """dM0 [H,N,d_v] = sum over b of G [B,H,N,d_v]; with last (from
+    touch_prepare) only the rows each sequence selected count."""
     import torch
 
     B, H, N, d_v = G.shape
     dM0 = torch.empty((H, N, d_v), dtype=torch.float32, device=G.device) if out is None else out
+    if last is not None and tuple(last.shape) != (B, H, N):
+        raise ValueError(f"last must be {(B, H, N)}, got {tuple(last.shape)}")
     _check(lib().sdm_state_init_backward(_dev(G, torch.float32, "G", 4), B, H, N, d_v,
+                                         None if last is None else _dev(last, torch.int32, "last"),
                                          _dev(dM0, torch.float32, "dM0", 3), _stream(stream)))
     return dM0

@@ -86,7 +86,7 @@ int64_t elem_bytes(int dtype) { return dtype == SDM_F32 ? 4 : (dtype == SDM_BF16
 
 extern "C" {
 
-int sdm_abi_version(void) { return 2; }
+int sdm_abi_version(void) { return 3; }
 
 const char* sdm_status_string(int status) {
   switch (status) {
@@ -201,8 +201,8 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,
                       const float* rw, const float* v, const float* alpha, const float* beta,
                       const float* tape, const float* dout, float* G, float* dv, float* dwk,
-                      float* drw, float* dalpha, float* dbeta, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      float* drw, float* dalpha, float* dbeta, const uint64_t* first,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int rc;
   // G has the state's shape and type: it stands for the state in the shared checks
   if ((rc = check_scan_args(G, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
@@ -214,6 +214,7 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
     return fail(SDM_ERR_INVALID, "tape, dout, G and workspace must be 16-byte aligned");
   if (!aligned(dwk, 4) || !aligned(drw, 4) || !aligned(dalpha, 4) || !aligned(dbeta, 4))
     return fail(SDM_ERR_INVALID, "dwk, drw, dalpha and dbeta must be 4-byte aligned");
+  if (!aligned(first, 8)) return fail(SDM_ERR_INVALID, "first must be 8-byte aligned");
   if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
   if ((int64_t)B * H * T >= ((int64_t)1 << 33))
     return fail(SDM_ERR_UNSUPPORTED, "B*H*T must be below 2^33 (one finishing wave per step)");
@@ -227,7 +228,7 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_scan_backward",
                 sdm::launch_scan_backward(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
-                                          beta, tape, dout, G, dv, dwk, drw, dalpha, dbeta,
+                                          beta, tape, dout, G, dv, dwk, drw, dalpha, dbeta, first,
                                           reinterpret_cast<float*>(workspace), s),
                 s);
 }
@@ -252,16 +253,34 @@ int sdm_select_backward(const int32_t* idx, const float* weight, const float* dw
                 sdm::launch_select_backward(idx, weight, dweight, units, n, K, dx1, dx2, s), s);
 }
 
-int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v, float* dM0,
-                            void* stream) {
+int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
+                            const int32_t* last, float* dM0, void* stream) {
   int rc;
   if ((rc = check_state(G, SDM_F32, N, d_v))) return rc;
   if (!dM0) return fail(SDM_ERR_INVALID, "dM0 is NULL");
   if (!aligned(dM0, 16)) return fail(SDM_ERR_INVALID, "dM0 must be 16-byte aligned");
+  if (!aligned(last, 4)) return fail(SDM_ERR_INVALID, "last must be 4-byte aligned");
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_state_init_backward",
-                sdm::launch_state_init_backward(G, B, H, N, d_v, dM0, s), s);
+                sdm::launch_state_init_backward(G, B, H, N, d_v, last, dM0, s), s);
+}
+
+int sdm_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R, const int32_t* widx,
+                      const int32_t* ridx, int32_t* last, uint64_t* first, void* stream) {
+  if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  if (N < 1 || N > ((int64_t)1 << 31) - 1) return fail(SDM_ERR_INVALID, "N must be in [1, 2^31)");
+  if (W < 1 || W > 64 || R < 1 || R > 64) return fail(SDM_ERR_INVALID, "W and R must be in [1, 64]");
+  if (T < 0) return fail(SDM_ERR_INVALID, "T must be >= 0");
+  if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
+  if (!last) return fail(SDM_ERR_INVALID, "last is NULL");
+  if (T > 0 && (!widx || !ridx || !first))
+    return fail(SDM_ERR_INVALID, "widx, ridx and first must not be NULL");
+  if (!aligned(last, 4) || !aligned(widx, 4) || !aligned(ridx, 4) || !aligned(first, 8))
+    return fail(SDM_ERR_INVALID, "index arrays and last must be 4-byte, first 8-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_touch_prepare",
+                sdm::launch_touch_prepare(B, H, N, T, W, R, widx, ridx, last, first, s), s);
 }
 
 int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,

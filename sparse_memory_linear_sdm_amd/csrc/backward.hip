@@ -58,6 +58,7 @@ struct BwdArgs {
   float* dv;
   float* ws;
   int ntiles;
+  const uint64_t* first;  // optional: per step, the slots that are their row's last touch
 };
 
 __device__ __forceinline__ uint32_t hash_slot(uint32_t row) {
@@ -174,10 +175,16 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
     my_r = lane < R ? ridx[t * R + lane] : -1;
     my_rw = lane < R ? rw[t * R + lane] : 0.0f;
   }
+  // Sparse mode: a slot whose row the forward touches for the last time at
+  // this step is the row's first touch in reverse, where G holds dL/dM_T =
+  // 0 for it; its G gather is dropped (an out-of-range buffer load returns
+  // zero), so G needs no zeroing beforehand.
+  const uint64_t* firstm = A.first ? A.first + (int64_t)mem * T * 2 : nullptr;
+  uint64_t fm_w = firstm ? firstm[(T - 1) * 2] : 0ull, fm_r = firstm ? firstm[(T - 1) * 2 + 1] : 0ull;
 
   for (int64_t t = T - 1; t >= 0; --t) {
     // ---- this step's offsets
-    uint32_t wrow[NI], wo[NI], ro[NI], to[NI], tr[NI];
+    uint32_t wrow[NI], wo[NI], ro[NI], to[NI], tr[NI], wlo[NI], rlo[NI];
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int j = k * RPI + lr;
@@ -188,6 +195,8 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
       const uint32_t tstep = (uint32_t)t * (uint32_t)(W + R);
       to[k] = wv ? (tstep + (uint32_t)j) * row_bytes + lane_off : kOffNone;
       tr[k] = rv ? (tstep + (uint32_t)(W + j)) * row_bytes + lane_off : kOffNone;
+      wlo[k] = ((fm_w >> j) & 1ull) ? kOffNone : wo[k];  // G gathers (stores keep wo, ro)
+      rlo[k] = ((fm_r >> j) & 1ull) ? kOffNone : ro[k];
     }
 
     // ---- gathers (all issued before any is used)
@@ -195,9 +204,9 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
 #pragma unroll
     for (int k = 0; k < NI; ++k) Mg[k] = __builtin_amdgcn_raw_buffer_load_b128(tres, tr[k], 0, 0);
 #pragma unroll
-    for (int k = 0; k < NI; ++k) Gg[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, ro[k], 0, 0);
+    for (int k = 0; k < NI; ++k) Gg[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, rlo[k], 0, 0);
 #pragma unroll
-    for (int k = 0; k < NI; ++k) Gf[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, wo[k], 0, 0);
+    for (int k = 0; k < NI; ++k) Gf[k] = __builtin_amdgcn_raw_buffer_load_b128(gres, wlo[k], 0, 0);
 #pragma unroll
     for (int k = 0; k < NI; ++k) P[k] = __builtin_amdgcn_raw_buffer_load_b128(tres, to[k], 0, 0);
 
@@ -211,6 +220,7 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
     const f32x4 n_v = *reinterpret_cast<const f32x4*>(vm - lc * 4 + lv * 4 + tn * d_v);
     const f32x4 n_d = *reinterpret_cast<const f32x4*>(dom - lc * 4 + lv * 4 + tn * d_v);
     const float n_a = am[tn], n_b = bm[tn];
+    const uint64_t n_fw = firstm ? firstm[tn * 2] : 0ull, n_fr = firstm ? firstm[tn * 2 + 1] : 0ull;
 
     // ---- match write rows to this step's read rows while the gathers fly.
     // Lane j inserts read slot j; a read row whose table entry was taken by
@@ -329,6 +339,8 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
     dd = sm_d[lc];
     a = n_a;
     b = n_b;
+    fm_w = n_fw;
+    fm_r = n_fr;
     my_r = n_r;
     my_rw = n_rw;
     wave_sync();  // the LDS staging, rws and tab are rewritten by the next step
@@ -430,21 +442,86 @@ __global__ __launch_bounds__(256) void select_bwd_kernel(const int32_t* __restri
   }
 }
 
-// dM0[h] = sum over b of G[b, h], in order b = 0, 1, ...
+// dM0[h] = sum over b of G[b, h], in order b = 0, 1, ...  With last (the
+// sparse mode), rows a sequence never touched hold no gradient and are left
+// out (their G is not read): adding them as zeros gives the same sum.
+template <bool SPARSE>
 __global__ __launch_bounds__(256) void init_bwd_kernel(const float4* __restrict__ G,
                                                        float4* __restrict__ dM0, int B,
-                                                       int64_t per_seq4, int64_t n4) {
+                                                       int64_t per_seq4, int64_t n4,
+                                                       const int32_t* __restrict__ last,
+                                                       int64_t N, int d4) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * 256) {
-    float4 acc = G[i];
-    for (int b = 1; b < B; ++b) {
-      const float4 x = G[(int64_t)b * per_seq4 + i];
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+    float4 acc;
+    if constexpr (SPARSE) {
+      const int64_t hrow = i / d4;  // h * N + row
+      acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int b = 0; b < B; ++b) {
+        if (last[(int64_t)b * (per_seq4 / d4) + hrow] < 0) continue;
+        const float4 x = G[(int64_t)b * per_seq4 + i];
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
+    } else {
+      acc = G[i];
+      for (int b = 1; b < B; ++b) {
+        const float4 x = G[(int64_t)b * per_seq4 + i];
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
     }
     dM0[i] = acc;
+  }
+}
+
+// ---- sparse gradient bookkeeping
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n,
+                                                       int32_t value) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = value;
+}
+
+// last[mem][row] = the last step at which the row is selected (write or
+// read); rows never selected keep -1.
+__global__ __launch_bounds__(256) void touch_last_kernel(const int32_t* __restrict__ widx,
+                                                         const int32_t* __restrict__ ridx,
+                                                         int64_t n_mem, int64_t N, int64_t T,
+                                                         int W, int R, int32_t* __restrict__ last) {
+  const int64_t per = T * (W + R);
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n_mem * per;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t mem = e / per, r = e % per, t = r / (W + R);
+    const int j = (int)(r % (W + R));
+    const int32_t row = j < W ? widx[(mem * T + t) * W + j] : ridx[(mem * T + t) * R + (j - W)];
+    if ((uint64_t)(uint32_t)row < (uint64_t)N) atomicMax(&last[mem * N + row], (int32_t)t);
+  }
+}
+
+// first[mem][t] = {write mask, read mask}: bit j set when slot j's row is
+// touched for the last time at step t.  One wavefront per (memory, step).
+__global__ __launch_bounds__(256) void touch_first_kernel(const int32_t* __restrict__ widx,
+                                                          const int32_t* __restrict__ ridx,
+                                                          const int32_t* __restrict__ last,
+                                                          int64_t n_mem, int64_t N, int64_t T,
+                                                          int W, int R, uint64_t* __restrict__ first) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (u >= n_mem * T) return;  // whole wavefront leaves together
+  const int lane = lane_id();
+  const int64_t mem = u / T, t = u % T;
+  const int32_t wr = lane < W ? widx[u * W + lane] : -1;
+  const int32_t rr = lane < R ? ridx[u * R + lane] : -1;
+  const bool wf = (uint64_t)(uint32_t)wr < (uint64_t)N && last[mem * N + wr] == (int32_t)t;
+  const bool rf = (uint64_t)(uint32_t)rr < (uint64_t)N && last[mem * N + rr] == (int32_t)t;
+  const uint64_t wm = __ballot(wf), rm = __ballot(rf);
+  if (lane == 0) {
+    first[2 * u] = wm;
+    first[2 * u + 1] = rm;
   }
 }
 
@@ -468,11 +545,12 @@ hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int
                                 const int32_t* ridx, const float* rw, const float* v,
                                 const float* alpha, const float* beta, const float* tape,
                                 const float* dout, float* G, float* dv, float* dwk, float* drw,
-                                float* dalpha, float* dbeta, float* ws, hipStream_t stream) {
+                                float* dalpha, float* dbeta, const uint64_t* first, float* ws,
+                                hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int cols = d_v < 32 ? d_v : 32;
   BwdArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, dout, tape, G, dv, ws,
-            d_v / cols};
+            d_v / cols, first};
   const int groups = (A.n_mem + 7) / 8;
   const int64_t blocks = (int64_t)groups * A.ntiles * 8;
   if (cols == 32)
@@ -499,14 +577,36 @@ hipError_t launch_select_backward(const int32_t* idx, const float* w, const floa
 }
 
 hipError_t launch_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
-                                      float* dM0, hipStream_t stream) {
+                                      const int32_t* last, float* dM0, hipStream_t stream) {
   const int64_t n4 = (int64_t)H * N * d_v / 4;
   int64_t blocks = (n4 + 255) / 256;
   const int64_t cap = (int64_t)cu_count() * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(init_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const float4*>(G), reinterpret_cast<float4*>(dM0), B, n4,
-                     n4);
+  if (last)
+    hipLaunchKernelGGL(init_bwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(G), reinterpret_cast<float4*>(dM0), B, n4,
+                       n4, last, N, d_v / 4);
+  else
+    hipLaunchKernelGGL(init_bwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(G), reinterpret_cast<float4*>(dM0), B, n4,
+                       n4, last, N, d_v / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R,
+                                const int32_t* widx, const int32_t* ridx, int32_t* last,
+                                uint64_t* first, hipStream_t stream) {
+  const int64_t n_mem = (int64_t)B * H;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  int64_t blocks = (n_mem * N + 255) / 256;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0,
+                     stream, last, n_mem * N, -1);
+  if (T == 0) return hipGetLastError();
+  blocks = (n_mem * T * (W + R) + 255) / 256;
+  hipLaunchKernelGGL(touch_last_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256),
+                     0, stream, widx, ridx, n_mem, N, T, W, R, last);
+  hipLaunchKernelGGL(touch_first_kernel, dim3((unsigned)((n_mem * T + 3) / 4)), dim3(256), 0,
+                     stream, widx, ridx, last, n_mem, N, T, W, R, first);
   return hipGetLastError();
 }
 

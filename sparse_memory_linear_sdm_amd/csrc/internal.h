@@ -30,13 +30,17 @@ hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int
                                 const int32_t* ridx, const float* rw, const float* v,
                                 const float* alpha, const float* beta, const float* tape,
                                 const float* dout, float* G, float* dv, float* dwk, float* drw,
-                                float* dalpha, float* dbeta, float* ws, hipStream_t stream);
+                                float* dalpha, float* dbeta, const uint64_t* first, float* ws,
+                                hipStream_t stream);
 
 hipError_t launch_select_backward(const int32_t* idx, const float* w, const float* dw,
                                   int64_t units, int n, int K, float* dx1, float* dx2,
                                   hipStream_t stream);
 
 hipError_t launch_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
-                                      float* dM0, hipStream_t stream);
+                                      const int32_t* last, float* dM0, hipStream_t stream);
+hipError_t launch_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R,
+                                const int32_t* widx, const int32_t* ridx, int32_t* last,
+                                uint64_t* first, hipStream_t stream);
 
 }  // namespace sdm

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = sdm.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.sdm_abi_version() == 2
+    assert L.sdm_abi_version() == 3
     assert L.sdm_status_string(0) == b"SDM_OK"
     assert L.sdm_status_string(2) == b"SDM_ERR_UNSUPPORTED"
 
@@ -135,11 +135,13 @@ def test_training_calls_validation():
     assert L.sdm_scan_backward_workspace_size(1, 1, 16, 10, 8, 8) == 10 * 1 * 17 * 4
     assert L.sdm_scan_backward_workspace_size(1, 1, 48, 10, 8, 8) == 0
     # sdm_scan_backward: B, H, N, d_v, T, W, R, 7 inputs, tape, dout, G, dv, dwk, drw,
-    # dalpha, dbeta, workspace, bytes, stream (the state is not an argument)
+    # dalpha, dbeta, first, workspace, bytes, stream (the state is not an argument)
     wsb = L.sdm_scan_backward_workspace_size(1, 1, 16, 8, 8, 8)
-    ok = [1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 16 + [wsb, None]
-    assert len(ok) == 25
-    a = list(ok); a[23] = wsb - 4
+    ok = [1, 1, 4096, 16, 8, 8, 8] + [FAKE] * 17 + [wsb, None]
+    assert len(ok) == 26
+    a = list(ok); a[22] = FAKE + 4  # first misaligned
+    assert L.sdm_scan_backward(*a) == 1 and "first" in _err()
+    a = list(ok); a[24] = wsb - 4
     assert L.sdm_scan_backward(*a) == 1 and "workspace" in _err()
     a = list(ok); a[16] = None  # G
     assert L.sdm_scan_backward(*a) == 1
@@ -161,10 +163,19 @@ def test_training_calls_validation():
     assert L.sdm_select_backward(*a) == 1
     a = list(ok); a[4] = 100
     assert L.sdm_select_backward(*a) == 2
-    # sdm_state_init_backward: G, B, H, N, d_v, dM0, stream
-    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 16, None, None) == 1
-    assert L.sdm_state_init_backward(FAKE, 0, 1, 16, 16, FAKE, None) == 1
-    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 20, FAKE, None) == 2
+    # sdm_state_init_backward: G, B, H, N, d_v, last, dM0, stream
+    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 16, None, None, None) == 1
+    assert L.sdm_state_init_backward(FAKE, 0, 1, 16, 16, None, FAKE, None) == 1
+    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 20, None, FAKE, None) == 2
+    assert L.sdm_state_init_backward(FAKE, 1, 1, 16, 16, FAKE + 2, FAKE, None) == 1
+    # sdm_touch_prepare: B, H, N, T, W, R, widx, ridx, last, first, stream
+    ok = [1, 1, 4096, 8, 8, 8, FAKE, FAKE, FAKE, FAKE, None]
+    for i, bad, want in ((4, 65, 1), (5, 0, 1), (2, 0, 1), (8, None, 1), (9, FAKE + 4, 1),
+                         (3, 1 << 26, 2), (3, -1, 1), (0, 0, 1)):
+        a = list(ok); a[i] = bad
+        assert L.sdm_touch_prepare(*a) == want, (i, bad)
+    a = list(ok); a[6] = None
+    assert L.sdm_touch_prepare(*a) == 1  # widx NULL with T > 0
 
 
 def test_fp8_state_validation():
@@ -187,7 +198,7 @@ def test_zero_length_calls_accept_null_arrays():
     assert L.sdm_scan(FAKE, 0, 1, 1, 4096, 16, 0, 8, 8, *null9, None) == 0
     assert L.sdm_scan(None, 0, 1, 1, 4096, 16, 0, 8, 8, *null9, None) == 1  # M still required
     assert L.sdm_scan_train(FAKE, 1, 1, 4096, 16, 0, 8, 8, *null9, None, None) == 0
-    args = [1, 1, 4096, 16, 0, 8, 8] + [None] * 9 + [FAKE] + [None] * 6 + [0, None]
+    args = [1, 1, 4096, 16, 0, 8, 8] + [None] * 9 + [FAKE] + [None] * 7 + [0, None]
     assert L.sdm_scan_backward(*args) == 0
     args[16] = None  # G is state-sized and still required
     assert L.sdm_scan_backward(*args) == 1

@@ -203,6 +203,65 @@ def test_chunked_training_bitwise():
         assert torch.equal(torch.cat([parts[0][k], parts[T1][k]], dim=2), whole[k]), k
 
 
+def _touch_reference(widx, ridx, N):
+    """The sparse mode's bookkeeping from the index arrays on the host: the
+    last step selecting each row, and per step the slots whose row is
+    selected for the last time (integer work, compared bit for bit)."""
+    B, H, T, W = widx.shape
+    R = ridx.shape[3]
+    last = np.full((B, H, N), -1, np.int64)
+    first = np.zeros((B, H, T, 2), np.uint64)
+    steps = np.arange(T)
+    for b in range(B):
+        for h in range(H):
+            rows = np.concatenate([widx[b, h], ridx[b, h]], axis=1)
+            np.maximum.at(last[b, h], rows.ravel(), np.repeat(steps, W + R))
+            for m, idx in enumerate((widx[b, h], ridx[b, h])):
+                hit = last[b, h][idx] == steps[:, None]
+                bits = np.left_shift(np.uint64(1), np.arange(idx.shape[1], dtype=np.uint64))
+                first[b, h, :, m] = np.bitwise_or.reduce(np.where(hit, bits, np.uint64(0)), axis=1)
+    return last.astype(np.int32), first
+
+
+@pytest.mark.parametrize("B,H,n,d_v,T,W,R", CASES[:4] + [(2, 3, 8, 32, 200, 8, 8)])
+def test_sparse_mode_matches_dense(B, H, n, d_v, T, W, R):
+    """The sparse training mode (no zeroed G; each row's first touch in
+    reverse starts from zero; the M0 gradient reads selected rows only) gives
+    the dense mode's bits for every output, every selected row of G and dM0.
+    G starts full of NaN, so reading any row the mode must not read shows."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(B=B, H=H, n=n, d_v=d_v, T=T, W=W, R=R,
+                                  seed=9500 + B * 100 + H * 10 + W)
+    dev = to_dev(host_inputs(cfg))
+    dout = torch.from_numpy(S.host_block(cfg, "dout")).cuda()
+    M = sdm.state_init(torch.from_numpy(S.host_block(cfg, "M0")).cuda(), cfg.B)
+    widx, _, wk = sdm.select(dev["s1"], dev["s2"], cfg.W)
+    ridx, _, rw = sdm.select(dev["q1"], dev["q2"], cfg.R)
+    names = ("v", "alpha", "beta")
+    _, tape = sdm.scan_train(M, widx, wk, ridx, rw, *(dev[k] for k in names))
+    G = torch.zeros_like(M)
+    gd = sdm.scan_backward(widx, wk, ridx, rw, *(dev[k] for k in names), tape, dout, G)
+    dM0 = sdm.state_init_backward(G)
+    last, first = sdm.touch_prepare(widx, ridx, cfg.N)
+    Gs = torch.full_like(M, float("nan"))
+    gs = sdm.scan_backward(widx, wk, ridx, rw, *(dev[k] for k in names), tape, dout, Gs,
+                           first=first)
+    dM0s = sdm.state_init_backward(Gs, last=last)
+    torch.cuda.synchronize()
+    want_last, want_first = _touch_reference(widx.cpu().numpy(), ridx.cpu().numpy(), cfg.N)
+    assert np.array_equal(last.cpu().numpy(), want_last)
+    assert np.array_equal(first.cpu().numpy().view(np.uint64), want_first)
+    for k in gd:
+        assert torch.equal(gd[k], gs[k]), k
+    touched = last >= 0
+    assert torch.equal(G[touched], Gs[touched])
+    assert torch.isnan(Gs[~touched]).all()  # never written
+    assert torch.equal(dM0, dM0s)
+
+
 def test_training_degenerate_sizes():
     """T = 0 calls are no-ops that leave every buffer as it was; W = R = 1
     (single slot per step, weights exactly 1) matches the oracle; a selection
@@ -226,6 +285,9 @@ def test_training_degenerate_sizes():
     gr = sdm.scan_backward(widx, wk, ridx, rw, v, a, b, tape, e(B, H, 0, d_v), G)
     d1, d2 = sdm.select_backward(e(0, 8, dt=torch.int32), e(0, 8), e(0, 8), 16)
     torch.cuda.synchronize()
+    last, first = sdm.touch_prepare(widx, ridx, N)
+    torch.cuda.synchronize()
+    assert first.numel() == 0 and bool((last == -1).all())
     assert out.numel() == 0 and tape.numel() == 0 and gr["dv"].numel() == 0
     assert d1.shape == (0, 16) and d2.shape == (0, 16)
     assert torch.equal(M, M_before) and torch.equal(G, G_before)

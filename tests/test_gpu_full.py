@@ -234,6 +234,20 @@ def test_mid_config_training_full_size():
     for h in (0, 5):
         want = oracle.state_init_backward(G[:, h:h + 1].cpu().numpy())[0]
         _grad_close(dM0[h].cpu().numpy(), want, f"dM0 h={h}")
+    # the sparse mode, as the benchmark runs it: the same bits, with G never cleared
+    last, first = sdm.touch_prepare(widx, ridx, cfg.N)
+    Gs = torch.full_like(G, float("nan"))
+    gs = sdm.scan_backward(widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"], tape, dout, Gs,
+                           first=first)
+    dM0s = sdm.state_init_backward(Gs, last=last)
+    torch.cuda.synchronize()
+    for k in gr:
+        assert torch.equal(gr[k], gs[k]), f"sparse mode {k}"
+    assert torch.equal(dM0, dM0s), "sparse mode dM0"
+    touched = last >= 0
+    for b in range(B):  # per sequence, to bound the temporaries
+        assert torch.equal(G[b][touched[b]], Gs[b][touched[b]]), f"sparse mode G b={b}"
+    del last, first, Gs, gs, dM0s, touched
     del d, dout, M0, M, G, gr, dM0, widx, wk, ridx, rw, out, tape
     _free()
 

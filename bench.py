@@ -470,7 +470,7 @@ def run_train(cfg, args, torch, S, sdm):
                if cfg.name == "mid" and sparse else None)
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
-                "kernel": "scan_bwd_kernel<32> + scan_bwd_finish",
+                "kernel": ("scan_bwd_kernel<16>" if sparse else "scan_bwd_kernel<32>") + " + scan_bwd_finish",
                 "algorithmic_bytes_per_launch": bwd_bytes}
     extra = {"breakdown_ms": bd, "wall_s": wall,
              "scan_train_GBps": fwd_bytes / (bd["scan_train"] * 1e-3) / 1e9,

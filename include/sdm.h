@@ -173,7 +173,9 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  *          starts from zero instead of reading G).  In sparse mode, G holds
  *          dL/dM_0 on exit only for the rows the T steps select (last >= 0);
  *          the other rows keep whatever they held.  Both modes give the same
- *          bits for every output and every selected row of G.  (A chunk of a
+ *          bits for every selected row of G; the per-step sums (dv, dwk, drw,
+ *          dalpha, dbeta) may differ in the last bits (the sparse mode uses
+ *          narrower column tiles, so it adds them in another order).  (A chunk of a
  *          sequence whose later chunks' reverse passes already wrote G has a
  *          nonzero dL/dM_T: use the dense mode there.)
  *   workspace  device buffer of at least

@@ -536,7 +536,7 @@ int cu_count() {
 }  // namespace
 
 size_t scan_backward_workspace_bytes(int n_mem, int d_v, int64_t T, int W, int R) {
-  const int cols = d_v < 32 ? d_v : 32;
+  const int cols = d_v < 16 ? d_v : 16;  // the narrowest tiles either mode uses
   return (size_t)n_mem * (size_t)T * (size_t)(d_v / cols) * (size_t)(W + R + 1) * sizeof(float);
 }
 
@@ -548,7 +548,13 @@ hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int
                                 float* dalpha, float* dbeta, const uint64_t* first, float* ws,
                                 hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int cols = d_v < 32 ? d_v : 32;
+  // Tile width (measured at mid): the dense mode gathers every G row at
+  // random, so whole 128-byte lines (32 columns, one wave per compute unit)
+  // are fastest (14.1 ms against 17.3 with 16 columns).  In the sparse mode
+  // most G gathers are dropped and the tape rows are read in order, so twice
+  // the wavefronts with half the arithmetic each win (16 columns: 11.5 ms
+  // against 13.4).
+  const int cols = first ? (d_v < 16 ? d_v : 16) : (d_v < 32 ? d_v : 32);
   BwdArgs A{B * H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, dout, tape, G, dv, ws,
             d_v / cols, first};
   const int groups = (A.n_mem + 7) / 8;

@@ -131,7 +131,7 @@ def test_training_calls_validation():
     a = list(ok); a[4] = 128; a[5] = 40000; a[6] = 64; a[7] = 64
     assert L.sdm_scan_train(*a) == 2 and "W+R" in _err()  # the read rows count too
     need = L.sdm_scan_backward_workspace_size(2, 4, 128, 100, 64, 32)
-    assert need == 2 * 4 * 100 * 4 * (64 + 32 + 1) * 4  # 4 column tiles of 32
+    assert need == 2 * 4 * 100 * 8 * (64 + 32 + 1) * 4  # 8 column tiles of 16 (the narrowest)
     assert L.sdm_scan_backward_workspace_size(1, 1, 16, 10, 8, 8) == 10 * 1 * 17 * 4
     assert L.sdm_scan_backward_workspace_size(1, 1, 48, 10, 8, 8) == 0
     # sdm_scan_backward: B, H, N, d_v, T, W, R, 7 inputs, tape, dout, G, dv, dwk, drw,

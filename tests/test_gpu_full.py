@@ -234,15 +234,18 @@ def test_mid_config_training_full_size():
     for h in (0, 5):
         want = oracle.state_init_backward(G[:, h:h + 1].cpu().numpy())[0]
         _grad_close(dM0[h].cpu().numpy(), want, f"dM0 h={h}")
-    # the sparse mode, as the benchmark runs it: the same bits, with G never cleared
+    # the sparse mode, as the benchmark runs it, with G never cleared: the same bits for G and
+    # dM0; its per-step sums use 16-column tiles (another order of the same additions)
     last, first = sdm.touch_prepare(widx, ridx, cfg.N)
     Gs = torch.full_like(G, float("nan"))
     gs = sdm.scan_backward(widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"], tape, dout, Gs,
                            first=first)
     dM0s = sdm.state_init_backward(Gs, last=last)
     torch.cuda.synchronize()
-    for k in gr:
-        assert torch.equal(gr[k], gs[k]), f"sparse mode {k}"
+    for k in gr:  # the same sums over another tile width: the bar against the dense ones
+        for b, h in ((0, 0), (6, 3)):
+            _grad_close(gs[k][b, h].cpu().numpy(), gr[k][b, h].cpu().numpy(),
+                        f"sparse mode {k} b={b} h={h}")
     assert torch.equal(dM0, dM0s), "sparse mode dM0"
     touched = last >= 0
     for b in range(B):  # per sequence, to bound the temporaries

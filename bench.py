@@ -404,7 +404,8 @@ def run_train(cfg, args, torch, S, sdm):
         e[3].record(side)
         stream.wait_event(e[3])
         e[4].record(stream)
-        if sparse:  # beside the forward scan: it reads the selections only
+        if sparse:  # after the selections, beside the init or the forward scan
+            e[11].record(side)
             sdm.touch_prepare(widx, ridx, N, last=last, first=first, stream=side)
             e[10].record(side)
         sdm.scan_train(M, widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], out=out,
@@ -444,8 +445,8 @@ def run_train(cfg, args, torch, S, sdm):
           "scan_backward": avg(6, 7), "select_backward": avg(7, 8),
           "state_init_backward": avg(8, 9), "overlap": "select || state_init"}
     if sparse:
-        bd["touch_prepare"] = avg(4, 10)
-        bd["overlap"] += "; touch_prepare || scan_train"
+        bd["touch_prepare"] = avg(11, 10)
+        bd["overlap"] += "; touch_prepare after the selections, beside state_init or scan_train"
         bd["mode"] = "sparse (gradient table never cleared)"
     else:
         bd["zero_G"] = avg(5, 6)

@@ -381,7 +381,7 @@ def run_train(cfg, args, torch, S, sdm):
     wsb = int(sdm.lib().sdm_scan_backward_workspace_size(B, H, d_v, T, W, R))
     ws = torch.empty((wsb + 3) // 4, dtype=f32, device=dev)
     sparse = not args.train_dense
-    last = torch.empty((B, H, N), dtype=torch.int32, device=dev) if sparse else None
+    seen = torch.empty((B, H, (N + 31) // 32), dtype=torch.int32, device=dev) if sparse else None
     first = torch.empty((B, H, T, 2), dtype=torch.int64, device=dev) if sparse else None
     if sparse:
         G.fill_(float("nan"))  # contents never read in this mode
@@ -406,7 +406,7 @@ def run_train(cfg, args, torch, S, sdm):
         e[4].record(stream)
         if sparse:  # after the selections, beside the init or the forward scan
             e[11].record(side)
-            sdm.touch_prepare(widx, ridx, N, last=last, first=first, stream=side)
+            sdm.touch_prepare(widx, ridx, N, seen=seen, first=first, stream=side)
             e[10].record(side)
         sdm.scan_train(M, widx, wk, ridx, rw, x["v"], x["alpha"], x["beta"], out=out,
                        tape=tape, stream=stream)
@@ -422,7 +422,7 @@ def run_train(cfg, args, torch, S, sdm):
         sdm.select_backward(widx, wk, g["dwk"], n, stream=stream)
         sdm.select_backward(ridx, rw, g["drw"], n, stream=stream)
         e[8].record(stream)
-        sdm.state_init_backward(G, out=dM0, last=last, stream=stream)
+        sdm.state_init_backward(G, out=dM0, seen=seen, stream=stream)
         e[9].record(stream)
         if record is not None:
             record.append(e)

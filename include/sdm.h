@@ -171,7 +171,7 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  *          ridx (sparse mode: dL/dM_T is taken as zero, and G's contents on
  *          entry do not matter -- each row's first touch in reverse time
  *          starts from zero instead of reading G).  In sparse mode, G holds
- *          dL/dM_0 on exit only for the rows the T steps select (last >= 0);
+ *          dL/dM_0 on exit only for the rows the T steps select (seen);
  *          the other rows keep whatever they held.  Both modes give the same
  *          bits for every selected row of G; the per-step sums (dv, dwk, drw,
  *          dalpha, dbeta) may differ in the last bits (the sparse mode uses
@@ -211,26 +211,28 @@ int sdm_select_backward(const int32_t* idx, const float* weight, const float* dw
 /* Gradient of the per-sequence copy M[b,h] = M0[h]:
  *   dM0[h] = sum over b = 0, 1, ... of G[b,h].
  *   G [B, H, N, d_v] fp32 in;  dM0 [H, N, d_v] fp32 out (16-byte aligned).
- *   last  NULL (every row of G counts), or [B, H, N] int32 from
+ *   seen  NULL (every row of G counts), or [B, H, ceil(N/32)] uint32 from
  *         sdm_touch_prepare (sparse mode: row r of G[b,h] counts only when
- *         last[b,h,r] >= 0, and is not read otherwise; the sum is the same
- *         as the dense one with those rows zero). */
+ *         bit r of seen[b,h] is set, and is not read otherwise; the sum is
+ *         the same as the dense one with those rows zero). */
 int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
-                            const int32_t* last, float* dM0, void* stream);
+                            const uint32_t* seen, float* dM0, void* stream);
 
 /* Bookkeeping for the sparse training mode (the method touches only W + R
  * rows per step, "Meccanismo Core" items 3 and 4, so most of the gradient
  * table is never touched by one sequence).
  *   widx [B, H, T, W], ridx [B, H, T, R] int32 in: the forward's selections.
- *   last  [B, H, N] int32 out: the last step at which row r is selected
- *         (write or read), -1 if never.
+ *   seen  [B, H, ceil(N/32)] uint32 out: bit (r % 32) of word r / 32 is set
+ *         when row r is selected (write or read) at any of the T steps.
  *   first [B, H, T, 2] uint64 out: bit j of first[b,h,t,0] is set when
  *         widx[b,h,t,j]'s last selection is step t; first[b,h,t,1] likewise
  *         for ridx.
- * 1 <= W, R <= 64; 0 <= T < 2^26 (T = 0 only fills last with -1; the index
- * arrays and first may then be NULL).  Indices outside [0, N) are ignored. */
+ * 1 <= W, R <= 64; 1 <= N <= 2^20 (one N-bit table per memory is kept on
+ * chip); 0 <= T < 2^26 with T*max(W,R)*4 below 2^31 (T = 0 only clears
+ * seen; the index arrays and first may then be NULL).  Indices outside
+ * [0, N) are ignored. */
 int sdm_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R, const int32_t* widx,
-                      const int32_t* ridx, int32_t* last, uint64_t* first, void* stream);
+                      const int32_t* ridx, uint32_t* seen, uint64_t* first, void* stream);
 
 /* Static text for a status code. */
 const char* sdm_status_string(int status);

@@ -301,11 +301,11 @@ def scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=N
     return o
 
 
-def touch_prepare(widx, ridx, N: int, last=None, first=None, stream=None):
-    """Bookkeeping of the sparse training mode: last [B,H,N] int32 (the last
-    step that selects each row, -1 if none) and first [B,H,T,2] int64 (the
-    bits of the uint64 masks of slots whose row is selected for the last
-    time at that step)."""
+def touch_prepare(widx, ridx, N: int, seen=None, first=None, stream=None):
+    """Bookkeeping of the sparse training mode: seen [B,H,ceil(N/32)] int32
+    (the bits of the uint32 words: row r is selected at some step) and first
+    [B,H,T,2] int64 (the bits of the uint64 masks of slots whose row is
+    selected for the last time at that step).  N <= 2^20."""
     import torch
 
     B, H, T, W = widx.shape
@@ -313,15 +313,24 @@ def touch_prepare(widx, ridx, N: int, last=None, first=None, stream=None):
     if tuple(ridx.shape) != (B, H, T, R):
         raise ValueError(f"ridx must be {(B, H, T, R)}, got {tuple(ridx.shape)}")
     dev = widx.device
-    if last is None:
-        last = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    if seen is None:
+        seen = torch.empty((B, H, (N + 31) // 32), dtype=torch.int32, device=dev)
     if first is None:
         first = torch.empty((B, H, T, 2), dtype=torch.int64, device=dev)
     _check(lib().sdm_touch_prepare(B, H, N, T, W, R, _dev(widx, torch.int32, "widx"),
                                    _dev(ridx, torch.int32, "ridx"),
-                                   _dev(last, torch.int32, "last", 3),
+                                   _dev(seen, torch.int32, "seen", 3),
                                    _dev(first, torch.int64, "first", 4), _stream(stream)))
-    return last, first
+    return seen, first
+
+
+def seen_rows(seen, N: int):
+    """The seen bitmap of touch_prepare as a [B,H,N] bool tensor."""
+    import torch
+
+    shifts = torch.arange(32, dtype=torch.int32, device=seen.device)
+    bits = (seen.unsqueeze(-1) >> shifts) & 1
+    return bits.reshape(seen.shape[0], seen.shape[1], -1)[:, :, :N].bool()
 
 
 def select_backward(idx, weight, dweight, n: int, stream=None):
@@ -343,16 +352,16 @@ def select_backward(idx, weight, dweight, n: int, stream=None):
     return dx1, dx2
 
 
-def state_init_backward(G, out=None, last=None, stream=None):
-    """dM0 [H,N,d_v] = sum over b of G [B,H,N,d_v]; with last (from
+def state_init_backward(G, out=None, seen=None, stream=None):
+    """dM0 [H,N,d_v] = sum over b of G [B,H,N,d_v]; with seen (from
     touch_prepare) only the rows each sequence selected count."""
     import torch
 
     B, H, N, d_v = G.shape
     dM0 = torch.empty((H, N, d_v), dtype=torch.float32, device=G.device) if out is None else out
-    if last is not None and tuple(last.shape) != (B, H, N):
-        raise ValueError(f"last must be {(B, H, N)}, got {tuple(last.shape)}")
+    if seen is not None and tuple(seen.shape) != (B, H, (N + 31) // 32):
+        raise ValueError(f"seen must be {(B, H, (N + 31) // 32)}, got {tuple(seen.shape)}")
     _check(lib().sdm_state_init_backward(_dev(G, torch.float32, "G", 4), B, H, N, d_v,
-                                         None if last is None else _dev(last, torch.int32, "last"),
+                                         None if seen is None else _dev(seen, torch.int32, "seen"),
                                          _dev(dM0, torch.float32, "dM0", 3), _stream(stream)))
     return dM0

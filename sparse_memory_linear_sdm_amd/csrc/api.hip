@@ -254,33 +254,37 @@ int sdm_select_backward(const int32_t* idx, const float* weight, const float* dw
 }
 
 int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
-                            const int32_t* last, float* dM0, void* stream) {
+                            const uint32_t* seen, float* dM0, void* stream) {
   int rc;
   if ((rc = check_state(G, SDM_F32, N, d_v))) return rc;
   if (!dM0) return fail(SDM_ERR_INVALID, "dM0 is NULL");
   if (!aligned(dM0, 16)) return fail(SDM_ERR_INVALID, "dM0 must be 16-byte aligned");
-  if (!aligned(last, 4)) return fail(SDM_ERR_INVALID, "last must be 4-byte aligned");
+  if (!aligned(seen, 4)) return fail(SDM_ERR_INVALID, "seen must be 4-byte aligned");
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_state_init_backward",
-                sdm::launch_state_init_backward(G, B, H, N, d_v, last, dM0, s), s);
+                sdm::launch_state_init_backward(G, B, H, N, d_v, seen, dM0, s), s);
 }
 
 int sdm_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R, const int32_t* widx,
-                      const int32_t* ridx, int32_t* last, uint64_t* first, void* stream) {
+                      const int32_t* ridx, uint32_t* seen, uint64_t* first, void* stream) {
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
-  if (N < 1 || N > ((int64_t)1 << 31) - 1) return fail(SDM_ERR_INVALID, "N must be in [1, 2^31)");
+  if (N < 1) return fail(SDM_ERR_INVALID, "N must be >= 1");
+  if (N > sdm::kTouchMaxN)
+    return fail(SDM_ERR_UNSUPPORTED, "N must be at most 2^20 (one N-bit table per memory in LDS)");
   if (W < 1 || W > 64 || R < 1 || R > 64) return fail(SDM_ERR_INVALID, "W and R must be in [1, 64]");
   if (T < 0) return fail(SDM_ERR_INVALID, "T must be >= 0");
   if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
-  if (!last) return fail(SDM_ERR_INVALID, "last is NULL");
+  if (T * (W > R ? W : R) * 4 >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's index arrays must be below 2 GiB");
+  if (!seen) return fail(SDM_ERR_INVALID, "seen is NULL");
   if (T > 0 && (!widx || !ridx || !first))
     return fail(SDM_ERR_INVALID, "widx, ridx and first must not be NULL");
-  if (!aligned(last, 4) || !aligned(widx, 4) || !aligned(ridx, 4) || !aligned(first, 8))
-    return fail(SDM_ERR_INVALID, "index arrays and last must be 4-byte, first 8-byte aligned");
+  if (!aligned(seen, 4) || !aligned(widx, 4) || !aligned(ridx, 4) || !aligned(first, 8))
+    return fail(SDM_ERR_INVALID, "index arrays and seen must be 4-byte, first 8-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_touch_prepare",
-                sdm::launch_touch_prepare(B, H, N, T, W, R, widx, ridx, last, first, s), s);
+                sdm::launch_touch_prepare(B, H, N, T, W, R, widx, ridx, seen, first, s), s);
 }
 
 int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int R,

@@ -442,23 +442,26 @@ __global__ __launch_bounds__(256) void select_bwd_kernel(const int32_t* __restri
   }
 }
 
-// dM0[h] = sum over b of G[b, h], in order b = 0, 1, ...  With last (the
-// sparse mode), rows a sequence never touched hold no gradient and are left
+// dM0[h] = sum over b of G[b, h], in order b = 0, 1, ...  With seen (the
+// sparse mode), rows a sequence never selected hold no gradient and are left
 // out (their G is not read): adding them as zeros gives the same sum.
 template <bool SPARSE>
 __global__ __launch_bounds__(256) void init_bwd_kernel(const float4* __restrict__ G,
                                                        float4* __restrict__ dM0, int B,
                                                        int64_t per_seq4, int64_t n4,
-                                                       const int32_t* __restrict__ last,
+                                                       const uint32_t* __restrict__ seen,
                                                        int64_t N, int d4) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * 256) {
     float4 acc;
     if constexpr (SPARSE) {
       const int64_t hrow = i / d4;  // h * N + row
+      const int64_t H = per_seq4 / d4 / N;
+      const int64_t h = hrow / N, row = hrow % N;
+      const int64_t words = (N + 31) / 32;
       acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int b = 0; b < B; ++b) {
-        if (last[(int64_t)b * (per_seq4 / d4) + hrow] < 0) continue;
+        if (!((seen[((int64_t)b * H + h) * words + (row >> 5)] >> (row & 31)) & 1u)) continue;
         const float4 x = G[(int64_t)b * per_seq4 + i];
         acc.x += x.x;
         acc.y += x.y;
@@ -481,48 +484,81 @@ __global__ __launch_bounds__(256) void init_bwd_kernel(const float4* __restrict_
 
 // ---- sparse gradient bookkeeping
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n,
-                                                       int32_t value) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = value;
-}
+constexpr int kTouchChunk = 16;  // steps of indices each lane holds ahead in registers
 
-// last[mem][row] = the last step at which the row is selected (write or
-// read); rows never selected keep -1.
-__global__ __launch_bounds__(256) void touch_last_kernel(const int32_t* __restrict__ widx,
-                                                         const int32_t* __restrict__ ridx,
-                                                         int64_t n_mem, int64_t N, int64_t T,
-                                                         int W, int R, int32_t* __restrict__ last) {
-  const int64_t per = T * (W + R);
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n_mem * per;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t mem = e / per, r = e % per, t = r / (W + R);
-    const int j = (int)(r % (W + R));
-    const int32_t row = j < W ? widx[(mem * T + t) * W + j] : ridx[(mem * T + t) * R + (j - W)];
-    if ((uint64_t)(uint32_t)row < (uint64_t)N) atomicMax(&last[mem * N + row], (int32_t)t);
-  }
-}
-
-// first[mem][t] = {write mask, read mask}: bit j set when slot j's row is
-// touched for the last time at step t.  One wavefront per (memory, step).
-__global__ __launch_bounds__(256) void touch_first_kernel(const int32_t* __restrict__ widx,
-                                                          const int32_t* __restrict__ ridx,
-                                                          const int32_t* __restrict__ last,
-                                                          int64_t n_mem, int64_t N, int64_t T,
-                                                          int W, int R, uint64_t* __restrict__ first) {
-  const int64_t u = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (u >= n_mem * T) return;  // whole wavefront leaves together
+// One wavefront per memory walks the steps backwards with an N-bit "seen"
+// table in LDS (N <= 2^20: 128 KiB).  Lane j owns write slot j and read
+// slot j.  At step t every slot first tests its row (a row not seen at any
+// later step is selected here for the last time: its bit goes into
+// first[t]), then every slot marks its row; one wavefront executes its LDS
+// instructions in order, so a row that is both read and written at t is
+// flagged in both masks.  The final table says which rows the sequence
+// selects at all.  Only wave-level ordering is needed: no workgroup
+// barrier (whose fence would also wait for the mask stores and the index
+// prefetch).
+__global__ __launch_bounds__(kWave) void touch_kernel(const int32_t* __restrict__ widx,
+                                                      const int32_t* __restrict__ ridx,
+                                                      int64_t N, int64_t T, int W, int R,
+                                                      uint32_t* __restrict__ seen_out,
+                                                      uint64_t* __restrict__ first) {
+  __shared__ uint32_t seen[kTouchMaxN / 32];
+  const int64_t mem = blockIdx.x;
   const int lane = lane_id();
-  const int64_t mem = u / T, t = u % T;
-  const int32_t wr = lane < W ? widx[u * W + lane] : -1;
-  const int32_t rr = lane < R ? ridx[u * R + lane] : -1;
-  const bool wf = (uint64_t)(uint32_t)wr < (uint64_t)N && last[mem * N + wr] == (int32_t)t;
-  const bool rf = (uint64_t)(uint32_t)rr < (uint64_t)N && last[mem * N + rr] == (int32_t)t;
-  const uint64_t wm = __ballot(wf), rm = __ballot(rf);
-  if (lane == 0) {
-    first[2 * u] = wm;
-    first[2 * u + 1] = rm;
+  const int words = (int)((N + 31) / 32);
+  for (int i = lane; i < words; i += kWave) seen[i] = 0u;
+  // Buffer loads and stores with out-of-range offsets instead of branches,
+  // so the compiler's wait counts stay exact and the index prefetch stays
+  // in flight while a chunk is walked.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(widx) + mem * T * W, 0, (int)(T * W * 4), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(ridx) + mem * T * R, 0, (int)(T * R * 4), kBufWord3);
+  const __amdgpu_buffer_rsrc_t fres =
+      __builtin_amdgcn_make_buffer_rsrc(first + mem * T * 2, 0, (int)(T * 16), kBufWord3);
+  const bool ow = lane < W, orr = lane < R;
+  uint32_t cw[kTouchChunk], cr[kTouchChunk], nw[kTouchChunk], nr[kTouchChunk];
+  auto load = [&](uint32_t (&w)[kTouchChunk], uint32_t (&r)[kTouchChunk], int64_t c0)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kTouchChunk; ++s) {
+      const bool live = c0 >= 0 && c0 + s < T;
+      const uint32_t wo = live && ow ? (uint32_t)((c0 + s) * W + lane) * 4u : kOffNone;
+      const uint32_t ro = live && orr ? (uint32_t)((c0 + s) * R + lane) * 4u : kOffNone;
+      w[s] = __builtin_amdgcn_raw_buffer_load_b32(wres, wo, 0, 0);
+      r[s] = __builtin_amdgcn_raw_buffer_load_b32(rres, ro, 0, 0);
+    }
+  };
+  // chunks from the end: a chunk covers steps [t0, t0 + kTouchChunk), clipped to [0, T)
+  int64_t t0 = T > 0 ? ((T - 1) / kTouchChunk) * kTouchChunk : -1;
+  load(cw, cr, t0);
+  wave_sync();
+  for (; t0 >= 0; t0 -= kTouchChunk) {
+    load(nw, nr, t0 - kTouchChunk);  // the next chunk, in flight while this one is walked
+#pragma unroll
+    for (int s = kTouchChunk - 1; s >= 0; --s) {
+      const int64_t t = t0 + s;
+      if (t >= T) continue;  // the ragged last chunk (uniform over the wave)
+      const bool vw = ow && (uint64_t)cw[s] < (uint64_t)N;
+      const bool vr = orr && (uint64_t)cr[s] < (uint64_t)N;
+      const uint32_t hw = vw ? cw[s] : 0u, hr = vr ? cr[s] : 0u;
+      const bool fw = vw && !((seen[hw >> 5] >> (hw & 31)) & 1u);
+      const bool fr = vr && !((seen[hr >> 5] >> (hr & 31)) & 1u);
+      const uint64_t mw = __ballot(fw), mr = __ballot(fr);
+      const u32x4 q = {(uint32_t)mw, (uint32_t)(mw >> 32), (uint32_t)mr, (uint32_t)(mr >> 32)};
+      __builtin_amdgcn_raw_buffer_store_b128(q, fres, lane == 0 ? (uint32_t)t * 16u : kOffNone, 0,
+                                             0);
+      wave_sync();  // every test of step t before any mark
+      if (vw) atomicOr(&seen[hw >> 5], 1u << (hw & 31));
+      if (vr) atomicOr(&seen[hr >> 5], 1u << (hr & 31));
+      wave_sync();  // the marks before step t - 1's tests
+    }
+#pragma unroll
+    for (int s = 0; s < kTouchChunk; ++s) {
+      cw[s] = nw[s];
+      cr[s] = nr[s];
+    }
   }
+  for (int i = lane; i < words; i += kWave) seen_out[mem * words + i] = seen[i];
 }
 
 int cu_count() {
@@ -583,36 +619,27 @@ hipError_t launch_select_backward(const int32_t* idx, const float* w, const floa
 }
 
 hipError_t launch_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
-                                      const int32_t* last, float* dM0, hipStream_t stream) {
+                                      const uint32_t* seen, float* dM0, hipStream_t stream) {
   const int64_t n4 = (int64_t)H * N * d_v / 4;
   int64_t blocks = (n4 + 255) / 256;
   const int64_t cap = (int64_t)cu_count() * 8;
   if (blocks > cap) blocks = cap;
-  if (last)
+  if (seen)
     hipLaunchKernelGGL(init_bwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const float4*>(G), reinterpret_cast<float4*>(dM0), B, n4,
-                       n4, last, N, d_v / 4);
+                       n4, seen, N, d_v / 4);
   else
     hipLaunchKernelGGL(init_bwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const float4*>(G), reinterpret_cast<float4*>(dM0), B, n4,
-                       n4, last, N, d_v / 4);
+                       n4, seen, N, d_v / 4);
   return hipGetLastError();
 }
 
 hipError_t launch_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R,
-                                const int32_t* widx, const int32_t* ridx, int32_t* last,
+                                const int32_t* widx, const int32_t* ridx, uint32_t* seen,
                                 uint64_t* first, hipStream_t stream) {
-  const int64_t n_mem = (int64_t)B * H;
-  const int64_t cap = (int64_t)cu_count() * 8;
-  int64_t blocks = (n_mem * N + 255) / 256;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0,
-                     stream, last, n_mem * N, -1);
-  if (T == 0) return hipGetLastError();
-  blocks = (n_mem * T * (W + R) + 255) / 256;
-  hipLaunchKernelGGL(touch_last_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256),
-                     0, stream, widx, ridx, n_mem, N, T, W, R, last);
-  hipLaunchKernelGGL(touch_first_kernel, dim3((unsigned)((n_mem * T + 3) / 4)), dim3(256), 0,
-                     stream, widx, ridx, last, n_mem, N, T, W, R, first);
+  hipLaunchKernelGGL(touch_kernel, dim3((unsigned)((int64_t)B * H)), dim3(kWave), 0, stream, widx,
+                     ridx, N, T, W, R, seen, first);
   return hipGetLastError();
 }
 

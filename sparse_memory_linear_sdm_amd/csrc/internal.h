@@ -38,9 +38,11 @@ hipError_t launch_select_backward(const int32_t* idx, const float* w, const floa
                                   hipStream_t stream);
 
 hipError_t launch_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
-                                      const int32_t* last, float* dM0, hipStream_t stream);
+                                      const uint32_t* seen, float* dM0, hipStream_t stream);
+// The sparse-mode bookkeeping keeps one N-bit table per memory in LDS.
+constexpr int64_t kTouchMaxN = (int64_t)1 << 20;
 hipError_t launch_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R,
-                                const int32_t* widx, const int32_t* ridx, int32_t* last,
+                                const int32_t* widx, const int32_t* ridx, uint32_t* seen,
                                 uint64_t* first, hipStream_t stream);
 
 }  // namespace sdm

@@ -171,9 +171,11 @@ def test_training_calls_validation():
     # sdm_touch_prepare: B, H, N, T, W, R, widx, ridx, last, first, stream
     ok = [1, 1, 4096, 8, 8, 8, FAKE, FAKE, FAKE, FAKE, None]
     for i, bad, want in ((4, 65, 1), (5, 0, 1), (2, 0, 1), (8, None, 1), (9, FAKE + 4, 1),
-                         (3, 1 << 26, 2), (3, -1, 1), (0, 0, 1)):
+                         (3, 1 << 26, 2), (3, -1, 1), (0, 0, 1), (2, (1 << 20) + 1, 2)):
         a = list(ok); a[i] = bad
         assert L.sdm_touch_prepare(*a) == want, (i, bad)
+    a = list(ok); a[3] = 1 << 23; a[4] = 64  # T * W * 4 = 2^31: index arrays too large
+    assert L.sdm_touch_prepare(*a) == 2 and "2 GiB" in _err()
     a = list(ok); a[6] = None
     assert L.sdm_touch_prepare(*a) == 1  # widx NULL with T > 0
 

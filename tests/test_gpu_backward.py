@@ -205,8 +205,9 @@ def test_chunked_training_bitwise():
 
 def _touch_reference(widx, ridx, N):
     """The sparse mode's bookkeeping from the index arrays on the host: the
-    last step selecting each row, and per step the slots whose row is
-    selected for the last time (integer work, compared bit for bit)."""
+    rows selected at all (as the packed bit table) and, per step, the slots
+    whose row is selected for the last time (integer work, compared bit for
+    bit)."""
     B, H, T, W = widx.shape
     R = ridx.shape[3]
     last = np.full((B, H, N), -1, np.int64)
@@ -220,7 +221,12 @@ def _touch_reference(widx, ridx, N):
                 hit = last[b, h][idx] == steps[:, None]
                 bits = np.left_shift(np.uint64(1), np.arange(idx.shape[1], dtype=np.uint64))
                 first[b, h, :, m] = np.bitwise_or.reduce(np.where(hit, bits, np.uint64(0)), axis=1)
-    return last.astype(np.int32), first
+    words = (N + 31) // 32
+    sel = np.zeros((B, H, words * 32), bool)
+    sel[:, :, :N] = last >= 0
+    weights = np.left_shift(np.uint64(1), np.arange(32, dtype=np.uint64))
+    seen = (sel.reshape(B, H, words, 32) * weights).sum(-1).astype(np.uint32)
+    return seen, first
 
 
 @pytest.mark.parametrize("B,H,n,d_v,T,W,R", CASES[:4] + [(2, 3, 8, 32, 200, 8, 8)])
@@ -250,16 +256,16 @@ def test_sparse_mode_matches_dense(B, H, n, d_v, T, W, R):
     G = torch.zeros_like(M)
     gd = sdm.scan_backward(widx, wk, ridx, rw, *(dev[k] for k in names), tape, dout, G)
     dM0 = sdm.state_init_backward(G)
-    last, first = sdm.touch_prepare(widx, ridx, cfg.N)
+    seen, first = sdm.touch_prepare(widx, ridx, cfg.N)
     Gs = torch.full_like(M, float("nan"))
     gs = sdm.scan_backward(widx, wk, ridx, rw, *(dev[k] for k in names), tape, dout, Gs,
                            first=first)
-    dM0s = sdm.state_init_backward(Gs, last=last)
+    dM0s = sdm.state_init_backward(Gs, seen=seen)
     torch.cuda.synchronize()
-    want_last, want_first = _touch_reference(widx.cpu().numpy(), ridx.cpu().numpy(), cfg.N)
-    assert np.array_equal(last.cpu().numpy(), want_last)
+    want_seen, want_first = _touch_reference(widx.cpu().numpy(), ridx.cpu().numpy(), cfg.N)
+    assert np.array_equal(seen.cpu().numpy().view(np.uint32), want_seen)
     assert np.array_equal(first.cpu().numpy().view(np.uint64), want_first)
-    touched = last >= 0
+    touched = sdm.seen_rows(seen, cfg.N)
     assert torch.equal(G[touched], Gs[touched])
     assert torch.isnan(Gs[~touched]).all()  # never written
     assert torch.equal(dM0, dM0s)
@@ -297,9 +303,9 @@ def test_training_degenerate_sizes():
     gr = sdm.scan_backward(widx, wk, ridx, rw, v, a, b, tape, e(B, H, 0, d_v), G)
     d1, d2 = sdm.select_backward(e(0, 8, dt=torch.int32), e(0, 8), e(0, 8), 16)
     torch.cuda.synchronize()
-    last, first = sdm.touch_prepare(widx, ridx, N)
+    seen, first = sdm.touch_prepare(widx, ridx, N)
     torch.cuda.synchronize()
-    assert first.numel() == 0 and bool((last == -1).all())
+    assert first.numel() == 0 and bool((seen == 0).all())
     assert out.numel() == 0 and tape.numel() == 0 and gr["dv"].numel() == 0
     assert d1.shape == (0, 16) and d2.shape == (0, 16)
     assert torch.equal(M, M_before) and torch.equal(G, G_before)

@@ -236,21 +236,21 @@ def test_mid_config_training_full_size():
         _grad_close(dM0[h].cpu().numpy(), want, f"dM0 h={h}")
     # the sparse mode, as the benchmark runs it, with G never cleared: the same bits for G and
     # dM0; its per-step sums use 16-column tiles (another order of the same additions)
-    last, first = sdm.touch_prepare(widx, ridx, cfg.N)
+    seen, first = sdm.touch_prepare(widx, ridx, cfg.N)
     Gs = torch.full_like(G, float("nan"))
     gs = sdm.scan_backward(widx, wk, ridx, rw, d["v"], d["alpha"], d["beta"], tape, dout, Gs,
                            first=first)
-    dM0s = sdm.state_init_backward(Gs, last=last)
+    dM0s = sdm.state_init_backward(Gs, seen=seen)
     torch.cuda.synchronize()
     for k in gr:  # the same sums over another tile width: the bar against the dense ones
         for b, h in ((0, 0), (6, 3)):
             _grad_close(gs[k][b, h].cpu().numpy(), gr[k][b, h].cpu().numpy(),
                         f"sparse mode {k} b={b} h={h}")
     assert torch.equal(dM0, dM0s), "sparse mode dM0"
-    touched = last >= 0
+    touched = sdm.seen_rows(seen, cfg.N)
     for b in range(B):  # per sequence, to bound the temporaries
         assert torch.equal(G[b][touched[b]], Gs[b][touched[b]]), f"sparse mode G b={b}"
-    del last, first, Gs, gs, dM0s, touched
+    del seen, first, Gs, gs, dM0s, touched
     del d, dout, M0, M, G, gr, dM0, widx, wk, ridx, rw, out, tape
     _free()
 

@@ -215,10 +215,13 @@ def _touch_reference(widx, ridx, N):
     steps = np.arange(T)
     for b in range(B):
         for h in range(H):
-            rows = np.concatenate([widx[b, h], ridx[b, h]], axis=1)
-            np.maximum.at(last[b, h], rows.ravel(), np.repeat(steps, W + R))
+            rows = np.concatenate([widx[b, h], ridx[b, h]], axis=1).ravel()
+            t_of = np.repeat(steps, W + R)
+            ok = (rows >= 0) & (rows < N)  # indices outside [0, N) are ignored
+            np.maximum.at(last[b, h], rows[ok], t_of[ok])
             for m, idx in enumerate((widx[b, h], ridx[b, h])):
-                hit = last[b, h][idx] == steps[:, None]
+                valid = (idx >= 0) & (idx < N)
+                hit = valid & (last[b, h][np.where(valid, idx, 0)] == steps[:, None])
                 bits = np.left_shift(np.uint64(1), np.arange(idx.shape[1], dtype=np.uint64))
                 first[b, h, :, m] = np.bitwise_or.reduce(np.where(hit, bits, np.uint64(0)), axis=1)
     words = (N + 31) // 32
@@ -278,6 +281,36 @@ def test_sparse_mode_matches_dense(B, H, n, d_v, T, W, R):
                                      host["alpha"][b, h], host["beta"][b, h], dout_h[b, h])
             for k in ("dv", "dwk", "drw", "dalpha", "dbeta"):
                 _close(gs[k][b, h], o[k], f"sparse b={b} h={h} {k}")
+
+
+def test_touch_prepare_ignores_out_of_range_rows():
+    """Hand-built selections with indices outside [0, N) (ignored), W != R
+    below 64, repeated rows across steps and a row both read and written in
+    one step: the masks and the bitmap equal the host's bookkeeping bit for
+    bit, over a ragged number of steps (not a multiple of the prefetch)."""
+    import torch
+
+    import sparse_memory_linear_sdm_amd as sdm
+
+    rng = np.random.default_rng(12)
+    B, H, N, T, W, R = 2, 3, 300, 53, 7, 5
+    widx = np.stack([[[rng.choice(N, W, replace=False) for _ in range(T)] for _ in range(H)]
+                     for _ in range(B)]).astype(np.int32)
+    ridx = np.stack([[[rng.choice(N, R, replace=False) for _ in range(T)] for _ in range(H)]
+                     for _ in range(B)]).astype(np.int32)
+    widx[0, 0, 3, 2] = -1
+    widx[1, 2, 50, 0] = N + 5
+    ridx[0, 1, 7, 4] = -7
+    ridx[1, 0, 52, 1] = N
+    ridx[0, 0, 10, 0] = widx[0, 0, 10, 1]  # read and written in one step
+    seen, first = sdm.touch_prepare(torch.from_numpy(widx).cuda(), torch.from_numpy(ridx).cuda(), N)
+    torch.cuda.synchronize()
+    want_seen, want_first = _touch_reference(widx, ridx, N)
+    assert np.array_equal(seen.cpu().numpy().view(np.uint32), want_seen)
+    assert np.array_equal(first.cpu().numpy().view(np.uint64), want_first)
+    f = first.cpu().numpy().view(np.uint64)
+    one = np.uint64(1)
+    assert (f[0, 0, 10, 0] >> one) & one == f[0, 0, 10, 1] & one  # the same row, the same flag
 
 
 def test_training_degenerate_sizes():

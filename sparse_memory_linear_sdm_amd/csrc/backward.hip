@@ -14,7 +14,7 @@
 // Rows that a step does not write carry their gradient unchanged.
 //
 // scan_bwd_kernel walks t = T-1 .. 0 with one wavefront per (memory,
-// 32-column tile).  The training forward kept a tape of each step's W
+// column tile: 32 columns, or 16 in the sparse mode).  The training forward kept a tape of each step's W
 // pre-write rows and R read rows (the values the read used), so this pass
 // never touches the state M: every value it needs is on the tape, stored
 // contiguously per step.  The gradient table G (caller-owned, the shape of
@@ -25,10 +25,16 @@
 // -- in that order, so a row that is both read and written ends with its
 // write-side value.  All accesses to a (row, tile) of G come from one
 // wavefront, and the next step's loads are issued after this step's stores,
-// so program order keeps every step's view current.  Per-tile partial sums of d(beta*k), dr and dalpha go
-// to a caller-provided workspace; a finishing kernel adds the tiles in a
-// fixed order (deterministic) and applies beta and the k weights.  Nothing
-// here is a dense contraction: no MFMA.
+// so program order keeps every step's view current.  Per-tile partial sums
+// of d(beta*k), dr and dalpha go to a caller-provided workspace; a
+// finishing kernel adds the tiles in a fixed order (deterministic) and
+// applies beta and the k weights.
+//
+// Sparse mode (the final-state gradient is zero): touch_kernel marks, per
+// step, the slots whose row the forward selects there for the last time;
+// the reverse scan gathers no G for them (zero, as a cleared table would
+// give), so G is never cleared, and the M0 gradient reads only the rows a
+// sequence selects.  Nothing here is a dense contraction: no MFMA.
 #include "device_common.h"
 #include "internal.h"
 

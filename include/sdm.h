@@ -49,6 +49,12 @@
  *     codes are a function of the binary32 inputs alone.  Pointers to M, M0 and v must be
  *     16-byte aligned; sub-score pointers must be 16-byte aligned when
  *     n >= 256 and 4-byte aligned otherwise.
+ *   - Size limits per call (a kernel launch counts its work-items in 32 bits):
+ *     at most 2^20 memories (B*H) for every call that walks memories, and at
+ *     most 2^26 - 4 selection units (sdm_select, sdm_select_backward) or
+ *     memory-steps B*H*T (sdm_scan_backward); larger work is split by the
+ *     caller into several calls.  Beyond them a call returns
+ *     SDM_ERR_UNSUPPORTED before launching anything.
  *   - Calls on different streams are independent as long as they do not
  *     share an output buffer (including M).
  */
@@ -189,7 +195,7 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
  * P and M_t[g_l] read from the tape.
  * Arithmetic in fp32; the tile partial sums are added in a fixed order, so
  * results are deterministic.  Sizes as for sdm_scan, plus T < 2^26 and
- * B*H*T < 2^33.  T = 0 is a valid no-op (G unchanged; every per-step array
+ * B*H*T <= 2^26 - 4.  T = 0 is a valid no-op (G unchanged; every per-step array
  * and the workspace may then be NULL). */
 int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       const int32_t* widx, const float* wk, const int32_t* ridx,

@@ -324,7 +324,8 @@ int oracle_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, 
                        const float* s1, const float* s2, const float* q1, const float* q2,
                        const float* v, const float* alpha, const float* beta, float* out,
                        int32_t* widx, int32_t* ridx) {
-  if (B < 1 || H < 1 || n < 1 || W < 1 || R < 1 || W > n || R > n) return fail("bad sizes");
+  if (B < 1 || H < 1 || n < 1 || W < 1 || R < 1 || W > n || R > n || dtype < 0 || dtype > 2)
+    return fail("bad sizes");
   int64_t N = (int64_t)n * n;
   int32_t* wi = (int32_t*)malloc(sizeof(int32_t) * (size_t)W);
   int32_t* ri = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
@@ -335,7 +336,8 @@ int oracle_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, 
     rc = oracle_select(s1 + u * n, s2 + u * n, 1, n, W, wi, NULL, wk);
     if (rc == 0) rc = oracle_select(q1 + u * n, q2 + u * n, 1, n, R, ri, NULL, rw);
     if (rc != 0) break;
-    size_t es = dtype == 0 ? sizeof(float) : sizeof(uint16_t);
+    /* bytes per state element: fp32 4, bf16 2, fp8 E4M3 1 */
+    size_t es = dtype == 0 ? sizeof(float) : (dtype == 1 ? sizeof(uint16_t) : sizeof(uint8_t));
     void* Mu = (char*)M + (size_t)u * (size_t)N * (size_t)d_v * es;
     rc = oracle_scan(Mu, dtype, N, d_v, 1, W, R, wi, wk, ri, rw, v + u * d_v, alpha + u,
                      beta + u, out + u * d_v, 0, d_v);

@@ -14,7 +14,8 @@ Calls (same names as the C ABI without the "sdm_" prefix):
   step_decode(M, s1, s2, q1, q2, v, alpha, beta, W, R) -> (out, widx, ridx)
 Training (fp32 state; selections held fixed):
   scan_train(M, widx, wk, ridx, rw, v, alpha, beta) -> (out, tape)
-  scan_backward(M, widx, wk, ridx, rw, v, alpha, beta, tape, dout, G) -> dict
+  scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G) -> dict
+  touch_prepare(widx, ridx, N) -> (seen, first)
   select_backward(idx, weight, dweight, n) -> (dx1, dx2)
   state_init_backward(G) -> dM0
 """
@@ -98,20 +99,48 @@ def _stream(stream):
     return int(stream)
 
 
-def _dev(t, dtype, name, ndim=None):
+def _arg(t, dtype, shape, name):
+    """Check one tensor argument: type, exact shape (the one the call derives
+    from its other arguments), dtype (one dtype or a tuple of allowed ones;
+    None = any) and contiguity.  Returns (name, tensor) for _gpu().  A
+    mismatch raises ValueError (TypeError for a non-tensor): the kernels
+    index every buffer by sizes taken from other arguments, so a short or
+    strided buffer must never reach them.  Every argument of a call passes
+    these checks before any device check, so a call fails on the first bad
+    shape whatever device its tensors are on."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
-    if t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if dtype is not None and t.dtype not in allowed:
+        raise ValueError(f"{name} must be {' or '.join(map(str, allowed))}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
-    return t.data_ptr()
+    return (name, t)
+
+
+def _gpu(*args):
+    """Device pointers of checked arguments ((name, tensor) pairs from _arg,
+    or None for an absent optional one): every tensor must be on the GPU, all
+    on the same device."""
+    dev = None
+    ptrs = []
+    for a in args:
+        if a is None:
+            ptrs.append(None)
+            continue
+        name, t = a
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call's other tensors on {dev}")
+        ptrs.append(t.data_ptr())
+    return ptrs
 
 
 def _state_dtype(M):
@@ -126,41 +155,84 @@ def _state_dtype(M):
     raise ValueError(f"state must be float32, bfloat16 or float8_e4m3fn, got {M.dtype}")
 
 
-def select(x1, x2, K: int, out=None, stream=None):
-    """Top-K slots of the product-key table for every leading index of
-    x1, x2 [..., n]: returns idx int32, score fp32, weight fp32 [..., K]."""
+def _state_types():
     import torch
 
-    if x1.shape != x2.shape:
-        raise ValueError("x1 and x2 must have the same shape")
-    n = x1.shape[-1]
-    lead = tuple(x1.shape[:-1])
+    return (torch.float32, torch.bfloat16, torch.float8_e4m3fn)
+
+
+def _units(lead):
     units = 1
     for s in lead:
         units *= s
+    return units
+
+
+def select(x1, x2, K: int, out=None, stream=None):
+    """Top-K slots of the product-key table for every leading index of
+    x1, x2 [..., n]: returns idx int32, score fp32, weight fp32 [..., K].
+    out = (idx, score, weight) writes into caller tensors (score may be
+    None)."""
+    import torch
+
+    f32 = torch.float32
+    shape = tuple(x1.shape)
+    if len(shape) < 1:
+        raise ValueError("x1 and x2 must have a last dimension n")
+    n, lead = shape[-1], shape[:-1]
     if out is None:
         idx = torch.empty(lead + (K,), dtype=torch.int32, device=x1.device)
-        score = torch.empty(lead + (K,), dtype=torch.float32, device=x1.device)
-        weight = torch.empty(lead + (K,), dtype=torch.float32, device=x1.device)
+        score = torch.empty(lead + (K,), dtype=f32, device=x1.device)
+        weight = torch.empty(lead + (K,), dtype=f32, device=x1.device)
     else:
         idx, score, weight = out
-    sp = score.data_ptr() if score is not None else None
-    _check(lib().sdm_select(_dev(x1, torch.float32, "x1"), _dev(x2, torch.float32, "x2"), units,
-                            n, K, _dev(idx, torch.int32, "idx"), sp,
-                            _dev(weight, torch.float32, "weight"), _stream(stream)))
+    p1, p2, pi, ps, pw = _gpu(
+        _arg(x1, f32, shape, "x1"), _arg(x2, f32, shape, "x2"),
+        _arg(idx, torch.int32, lead + (K,), "idx"),
+        None if score is None else _arg(score, f32, lead + (K,), "score"),
+        _arg(weight, f32, lead + (K,), "weight"))
+    _check(lib().sdm_select(p1, p2, _units(lead), n, K, pi, ps, pw, _stream(stream)))
     return idx, score, weight
 
 
 def state_init(M0, B: int, dtype=None, out=None, stream=None):
-    """M [B,H,N,d_v] = M0 [H,N,d_v] for every b (fp32, bf16 or fp8 E4M3 state)."""
+    """M [B,H,N,d_v] = M0 [H,N,d_v] for every b (fp32, bf16 or fp8 E4M3 state).
+    out = an existing state tensor to fill (its dtype is the state type)."""
     import torch
 
-    dtype = torch.float32 if dtype is None else dtype
+    if M0.dim() != 3:
+        raise ValueError(f"M0 must be [H, N, d_v], got {tuple(M0.shape)}")
     H, N, d_v = M0.shape
-    M = torch.empty((B, H, N, d_v), dtype=dtype, device=M0.device) if out is None else out
-    _check(lib().sdm_state_init(M.data_ptr(), _state_dtype(M), _dev(M0, torch.float32, "M0", 3),
-                                B, H, N, d_v, _stream(stream)))
+    a0 = _arg(M0, torch.float32, (H, N, d_v), "M0")
+    if out is None:
+        dtype = torch.float32 if dtype is None else dtype
+        M = torch.empty((B, H, N, d_v), dtype=dtype, device=M0.device)
+    else:
+        M = out
+    p0, pm = _gpu(a0, _arg(M, _state_types(), (B, H, N, d_v), "M"))
+    _check(lib().sdm_state_init(pm, _state_dtype(M), p0, B, H, N, d_v, _stream(stream)))
     return M
+
+
+def _scan_shapes(M, widx, ridx):
+    if M.dim() != 4:
+        raise ValueError(f"the state must be [B, H, N, d_v], got {tuple(M.shape)}")
+    if widx.dim() != 4 or ridx.dim() != 4:
+        raise ValueError("widx and ridx must be [B, H, T, W] and [B, H, T, R]")
+    B, H, N, d_v = M.shape
+    T, W = widx.shape[2], widx.shape[3]
+    R = ridx.shape[3]
+    return B, H, N, d_v, T, W, R
+
+
+def _scan_args(B, H, T, W, R, d_v, widx, wk, ridx, rw, v, alpha, beta):
+    import torch
+
+    f32 = torch.float32
+    return [_arg(widx, torch.int32, (B, H, T, W), "widx"), _arg(wk, f32, (B, H, T, W), "wk"),
+            _arg(ridx, torch.int32, (B, H, T, R), "ridx"), _arg(rw, f32, (B, H, T, R), "rw"),
+            _arg(v, f32, (B, H, T, d_v), "v"), _arg(alpha, f32, (B, H, T), "alpha"),
+            _arg(beta, f32, (B, H, T), "beta")]
 
 
 def scan(M, widx, wk, ridx, rw, v, alpha, beta, out=None, stream=None):
@@ -169,26 +241,13 @@ def scan(M, widx, wk, ridx, rw, v, alpha, beta, out=None, stream=None):
     Returns out [B,H,T,d_v] fp32."""
     import torch
 
-    B, H, N, d_v = M.shape
-    if not M.is_contiguous():
-        raise ValueError("M must be contiguous")
-    T, W = widx.shape[2], widx.shape[3]
-    R = ridx.shape[3]
-    if tuple(v.shape) != (B, H, T, d_v):
-        raise ValueError(f"v must be {(B, H, T, d_v)}, got {tuple(v.shape)}")
-    for name, t, shp in (("widx", widx, (B, H, T, W)), ("wk", wk, (B, H, T, W)),
-                         ("ridx", ridx, (B, H, T, R)), ("rw", rw, (B, H, T, R)),
-                         ("alpha", alpha, (B, H, T)), ("beta", beta, (B, H, T))):
-        if tuple(t.shape) != shp:
-            raise ValueError(f"{name} must be {shp}, got {tuple(t.shape)}")
+    B, H, N, d_v, T, W, R = _scan_shapes(M, widx, ridx)
+    am = _arg(M, _state_types(), (B, H, N, d_v), "M")
+    ins = _scan_args(B, H, T, W, R, d_v, widx, wk, ridx, rw, v, alpha, beta)
     if out is None:
         out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
-    _check(lib().sdm_scan(M.data_ptr(), _state_dtype(M), B, H, N, d_v, T, W, R,
-                          _dev(widx, torch.int32, "widx"), _dev(wk, torch.float32, "wk"),
-                          _dev(ridx, torch.int32, "ridx"), _dev(rw, torch.float32, "rw"),
-                          _dev(v, torch.float32, "v"), _dev(alpha, torch.float32, "alpha"),
-                          _dev(beta, torch.float32, "beta"), _dev(out, torch.float32, "out"),
-                          _stream(stream)))
+    pm, *ptrs = _gpu(am, *ins, _arg(out, torch.float32, (B, H, T, d_v), "out"))
+    _check(lib().sdm_scan(pm, _state_dtype(M), B, H, N, d_v, T, W, R, *ptrs, _stream(stream)))
     return out
 
 
@@ -198,51 +257,31 @@ def step_decode(M, s1, s2, q1, q2, v, alpha, beta, W: int, R: int, out=None, wan
     v [B,H,d_v]; alpha, beta [B,H].  Returns (out [B,H,d_v], widx, ridx)."""
     import torch
 
+    if M.dim() != 4:
+        raise ValueError(f"the state must be [B, H, N, d_v], got {tuple(M.shape)}")
     B, H, N, d_v = M.shape
     n = s1.shape[-1]
     if n * n != N:
         raise ValueError(f"M has {N} rows but the halves give n*n = {n * n}")
+    f32 = torch.float32
+    ins = [_arg(M, _state_types(), (B, H, N, d_v), "M")]
+    ins += [_arg(t, f32, (B, H, n), nm) for nm, t in
+            (("s1", s1), ("s2", s2), ("q1", q1), ("q2", q2))]
+    ins += [_arg(v, f32, (B, H, d_v), "v"), _arg(alpha, f32, (B, H), "alpha"),
+            _arg(beta, f32, (B, H), "beta")]
     if out is None:
-        out = torch.empty((B, H, d_v), dtype=torch.float32, device=M.device)
+        out = torch.empty((B, H, d_v), dtype=f32, device=M.device)
+    ins.append(_arg(out, f32, (B, H, d_v), "out"))
     widx = ridx = None
     if want_idx:
         widx = torch.empty((B, H, W), dtype=torch.int32, device=M.device)
         ridx = torch.empty((B, H, R), dtype=torch.int32, device=M.device)
-    ptrs = [_dev(t, torch.float32, nm) for nm, t in
-            (("s1", s1), ("s2", s2), ("q1", q1), ("q2", q2), ("v", v), ("alpha", alpha),
-             ("beta", beta), ("out", out))]
-    _check(lib().sdm_step_decode(M.data_ptr(), _state_dtype(M), B, H, n, d_v, W, R, *ptrs,
+    pm, *ptrs = _gpu(*ins)
+    _check(lib().sdm_step_decode(pm, _state_dtype(M), B, H, n, d_v, W, R, *ptrs,
                                  widx.data_ptr() if widx is not None else None,
                                  ridx.data_ptr() if ridx is not None else None,
                                  _stream(stream)))
     return out, widx, ridx
-
-
-def _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta):
-    B, H, N, d_v = M.shape
-    T, W = widx.shape[2], widx.shape[3]
-    R = ridx.shape[3]
-    for name, t, shp in (("widx", widx, (B, H, T, W)), ("wk", wk, (B, H, T, W)),
-                         ("ridx", ridx, (B, H, T, R)), ("rw", rw, (B, H, T, R)),
-                         ("v", v, (B, H, T, d_v)), ("alpha", alpha, (B, H, T)),
-                         ("beta", beta, (B, H, T))):
-        if tuple(t.shape) != shp:
-            raise ValueError(f"{name} must be {shp}, got {tuple(t.shape)}")
-    return B, H, N, d_v, T, W, R
-
-
-def _tape_shape(tape, shp):
-    if tuple(tape.shape) != shp:
-        raise ValueError(f"tape must be {shp}, got {tuple(tape.shape)}")
-
-
-def _scan_ptrs(widx, wk, ridx, rw, v, alpha, beta):
-    import torch
-
-    return (_dev(widx, torch.int32, "widx"), _dev(wk, torch.float32, "wk"),
-            _dev(ridx, torch.int32, "ridx"), _dev(rw, torch.float32, "rw"),
-            _dev(v, torch.float32, "v"), _dev(alpha, torch.float32, "alpha"),
-            _dev(beta, torch.float32, "beta"))
 
 
 def scan_train(M, widx, wk, ridx, rw, v, alpha, beta, out=None, tape=None, stream=None):
@@ -251,16 +290,17 @@ def scan_train(M, widx, wk, ridx, rw, v, alpha, beta, out=None, tape=None, strea
     tape [B,H,T,W+R,d_v])."""
     import torch
 
-    B, H, N, d_v, T, W, R = _scan_shapes(M, widx, wk, ridx, rw, v, alpha, beta)
+    f32 = torch.float32
+    B, H, N, d_v, T, W, R = _scan_shapes(M, widx, ridx)
+    am = _arg(M, f32, (B, H, N, d_v), "M")
+    ins = _scan_args(B, H, T, W, R, d_v, widx, wk, ridx, rw, v, alpha, beta)
     if out is None:
-        out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
+        out = torch.empty((B, H, T, d_v), dtype=f32, device=M.device)
     if tape is None:
-        tape = torch.empty((B, H, T, W + R, d_v), dtype=torch.float32, device=M.device)
-    _tape_shape(tape, (B, H, T, W + R, d_v))
-    _check(lib().sdm_scan_train(_dev(M, torch.float32, "M", 4), B, H, N, d_v, T, W, R,
-                                *_scan_ptrs(widx, wk, ridx, rw, v, alpha, beta),
-                                _dev(out, torch.float32, "out"),
-                                _dev(tape, torch.float32, "tape"), _stream(stream)))
+        tape = torch.empty((B, H, T, W + R, d_v), dtype=f32, device=M.device)
+    pm, *ptrs = _gpu(am, *ins, _arg(out, f32, (B, H, T, d_v), "out"),
+                     _arg(tape, f32, (B, H, T, W + R, d_v), "tape"))
+    _check(lib().sdm_scan_train(pm, B, H, N, d_v, T, W, R, *ptrs, _stream(stream)))
     return out, tape
 
 
@@ -274,30 +314,27 @@ def scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=N
     dalpha, dbeta [B,H,T]."""
     import torch
 
-    B, H, N, d_v, T, W, R = _scan_shapes(G, widx, wk, ridx, rw, v, alpha, beta)
-    _tape_shape(tape, (B, H, T, W + R, d_v))
-    if first is not None and tuple(first.shape) != (B, H, T, 2):
-        raise ValueError(f"first must be {(B, H, T, 2)}, got {tuple(first.shape)}")
-    dev = G.device
     f32 = torch.float32
+    B, H, N, d_v, T, W, R = _scan_shapes(G, widx, ridx)
+    ins = _scan_args(B, H, T, W, R, d_v, widx, wk, ridx, rw, v, alpha, beta)
+    ins += [_arg(tape, f32, (B, H, T, W + R, d_v), "tape"),
+            _arg(dout, f32, (B, H, T, d_v), "dout"), _arg(G, f32, (B, H, N, d_v), "G")]
+    af = None if first is None else _arg(first, torch.int64, (B, H, T, 2), "first")
+    aw = None if workspace is None else _arg(workspace, None, None, "workspace")
+    dev = G.device
     o = {"dv": torch.empty((B, H, T, d_v), dtype=f32, device=dev),
          "dwk": torch.empty((B, H, T, W), dtype=f32, device=dev),
          "drw": torch.empty((B, H, T, R), dtype=f32, device=dev),
          "dalpha": torch.empty((B, H, T), dtype=f32, device=dev),
          "dbeta": torch.empty((B, H, T), dtype=f32, device=dev)}
+    ptrs = _gpu(*ins, *(_arg(o[k], f32, None, k) for k in ("dv", "dwk", "drw", "dalpha", "dbeta")),
+                af, aw)
     need = int(lib().sdm_scan_backward_workspace_size(B, H, d_v, T, W, R))
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=f32, device=dev)
+        ptrs[-1] = workspace.data_ptr()
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().sdm_scan_backward(B, H, N, d_v, T, W, R,
-                                   *_scan_ptrs(widx, wk, ridx, rw, v, alpha, beta),
-                                   _dev(tape, f32, "tape"), _dev(dout, f32, "dout"),
-                                   _dev(G, f32, "G", 4), o["dv"].data_ptr(), o["dwk"].data_ptr(),
-                                   o["drw"].data_ptr(), o["dalpha"].data_ptr(),
-                                   o["dbeta"].data_ptr(),
-                                   None if first is None else _dev(first, torch.int64, "first"),
-                                   _dev(workspace, workspace.dtype, "workspace"),
-                                   nbytes, _stream(stream)))
+    _check(lib().sdm_scan_backward(B, H, N, d_v, T, W, R, *ptrs, nbytes, _stream(stream)))
     return o
 
 
@@ -308,19 +345,19 @@ def touch_prepare(widx, ridx, N: int, seen=None, first=None, stream=None):
     selected for the last time at that step).  N <= 2^20."""
     import torch
 
+    if widx.dim() != 4 or ridx.dim() != 4:
+        raise ValueError("widx and ridx must be [B, H, T, W] and [B, H, T, R]")
     B, H, T, W = widx.shape
     R = ridx.shape[3]
-    if tuple(ridx.shape) != (B, H, T, R):
-        raise ValueError(f"ridx must be {(B, H, T, R)}, got {tuple(ridx.shape)}")
-    dev = widx.device
+    ins = [_arg(widx, torch.int32, (B, H, T, W), "widx"),
+           _arg(ridx, torch.int32, (B, H, T, R), "ridx")]
     if seen is None:
-        seen = torch.empty((B, H, (N + 31) // 32), dtype=torch.int32, device=dev)
+        seen = torch.empty((B, H, (N + 31) // 32), dtype=torch.int32, device=widx.device)
     if first is None:
-        first = torch.empty((B, H, T, 2), dtype=torch.int64, device=dev)
-    _check(lib().sdm_touch_prepare(B, H, N, T, W, R, _dev(widx, torch.int32, "widx"),
-                                   _dev(ridx, torch.int32, "ridx"),
-                                   _dev(seen, torch.int32, "seen", 3),
-                                   _dev(first, torch.int64, "first", 4), _stream(stream)))
+        first = torch.empty((B, H, T, 2), dtype=torch.int64, device=widx.device)
+    ptrs = _gpu(*ins, _arg(seen, torch.int32, (B, H, (N + 31) // 32), "seen"),
+                _arg(first, torch.int64, (B, H, T, 2), "first"))
+    _check(lib().sdm_touch_prepare(B, H, N, T, W, R, *ptrs, _stream(stream)))
     return seen, first
 
 
@@ -338,17 +375,18 @@ def select_backward(idx, weight, dweight, n: int, stream=None):
     dweight [..., K] -> (dx1, dx2) [..., n] fp32."""
     import torch
 
-    K = idx.shape[-1]
-    lead = tuple(idx.shape[:-1])
-    units = 1
-    for s in lead:
-        units *= s
-    dx1 = torch.empty(lead + (n,), dtype=torch.float32, device=idx.device)
-    dx2 = torch.empty(lead + (n,), dtype=torch.float32, device=idx.device)
-    _check(lib().sdm_select_backward(_dev(idx, torch.int32, "idx"),
-                                     _dev(weight, torch.float32, "weight"),
-                                     _dev(dweight, torch.float32, "dweight"), units, n, K,
-                                     dx1.data_ptr(), dx2.data_ptr(), _stream(stream)))
+    f32 = torch.float32
+    shape = tuple(idx.shape)
+    if len(shape) < 1:
+        raise ValueError("idx must have a last dimension K")
+    K, lead = shape[-1], shape[:-1]
+    ins = [_arg(idx, torch.int32, shape, "idx"), _arg(weight, f32, shape, "weight"),
+           _arg(dweight, f32, shape, "dweight")]
+    dx1 = torch.empty(lead + (n,), dtype=f32, device=idx.device)
+    dx2 = torch.empty(lead + (n,), dtype=f32, device=idx.device)
+    ptrs = _gpu(*ins, _arg(dx1, f32, None, "dx1"), _arg(dx2, f32, None, "dx2"))
+    _check(lib().sdm_select_backward(ptrs[0], ptrs[1], ptrs[2], _units(lead), n, K, ptrs[3],
+                                     ptrs[4], _stream(stream)))
     return dx1, dx2
 
 
@@ -357,11 +395,13 @@ def state_init_backward(G, out=None, seen=None, stream=None):
     touch_prepare) only the rows each sequence selected count."""
     import torch
 
+    f32 = torch.float32
+    if G.dim() != 4:
+        raise ValueError(f"G must be [B, H, N, d_v], got {tuple(G.shape)}")
     B, H, N, d_v = G.shape
-    dM0 = torch.empty((H, N, d_v), dtype=torch.float32, device=G.device) if out is None else out
-    if seen is not None and tuple(seen.shape) != (B, H, (N + 31) // 32):
-        raise ValueError(f"seen must be {(B, H, (N + 31) // 32)}, got {tuple(seen.shape)}")
-    _check(lib().sdm_state_init_backward(_dev(G, torch.float32, "G", 4), B, H, N, d_v,
-                                         None if seen is None else _dev(seen, torch.int32, "seen"),
-                                         _dev(dM0, torch.float32, "dM0", 3), _stream(stream)))
+    ag = _arg(G, f32, (B, H, N, d_v), "G")
+    as_ = None if seen is None else _arg(seen, torch.int32, (B, H, (N + 31) // 32), "seen")
+    dM0 = torch.empty((H, N, d_v), dtype=f32, device=G.device) if out is None else out
+    pg, ps, po = _gpu(ag, as_, _arg(dM0, f32, (H, N, d_v), "dM0"))
+    _check(lib().sdm_state_init_backward(pg, B, H, N, d_v, ps, po, _stream(stream)))
     return dM0

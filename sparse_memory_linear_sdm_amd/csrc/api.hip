@@ -108,7 +108,9 @@ int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, in
   if (units == 0) return finish("sdm_select", hipSuccess, (hipStream_t)stream);  // arrays may be NULL
   if ((rc = check_scores(x1, n, "x1")) || (rc = check_scores(x2, n, "x2"))) return rc;
   if (!idx || !weight) return fail(SDM_ERR_INVALID, "idx and weight must not be NULL");
-  if (units > ((int64_t)1 << 32)) return fail(SDM_ERR_INVALID, "units above 2^32");
+  if (units > sdm::kMaxWaveUnits)
+    return fail(SDM_ERR_UNSUPPORTED, "units must be at most 2^26 - 4 per call (got %lld)",
+                (long long)units);
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_select", sdm::launch_select(x1, x2, units, n, K, idx, score, weight, s), s);
 }
@@ -144,8 +146,8 @@ int check_scan_args(const void* M, int dtype, int B, int H, int64_t N, int d_v, 
       !aligned(alpha, 4) || !aligned(beta, 4))
     return fail(SDM_ERR_INVALID, "index, weight and gate arrays must be 4-byte aligned");
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
-  if ((int64_t)B * H > (1 << 24)) return fail(SDM_ERR_INVALID, "B*H too large");
-  if (T < 0) return fail(SDM_ERR_INVALID, "T must be >= 0");
+  if ((int64_t)B * H > sdm::kMaxMemories)
+    return fail(SDM_ERR_UNSUPPORTED, "B*H must be at most 2^20 memories per call");
   if (W < 1 || R < 1) return fail(SDM_ERR_INVALID, "W and R must be >= 1");
   if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W and R above 64 are not compiled");
   if (W > N || R > N) return fail(SDM_ERR_INVALID, "W and R must not exceed N");
@@ -216,8 +218,9 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
     return fail(SDM_ERR_INVALID, "dwk, drw, dalpha and dbeta must be 4-byte aligned");
   if (!aligned(first, 8)) return fail(SDM_ERR_INVALID, "first must be 8-byte aligned");
   if (T >= ((int64_t)1 << 26)) return fail(SDM_ERR_UNSUPPORTED, "T must be below 2^26");
-  if ((int64_t)B * H * T >= ((int64_t)1 << 33))
-    return fail(SDM_ERR_UNSUPPORTED, "B*H*T must be below 2^33 (one finishing wave per step)");
+  if ((int64_t)B * H * T > sdm::kMaxWaveUnits)
+    return fail(SDM_ERR_UNSUPPORTED,
+                "B*H*T must be at most 2^26 - 4 (one finishing wavefront per memory and step)");
   if (T * (W + R) * d_v * 4 >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*(W+R)*d_v*4 bytes) must be below 2 GiB; "
                 "split the sequence into consecutive calls");
@@ -245,9 +248,9 @@ int sdm_select_backward(const int32_t* idx, const float* weight, const float* dw
   if (!aligned(idx, 4) || !aligned(weight, 4) || !aligned(dweight, 4) || !aligned(dx1, 4) ||
       !aligned(dx2, 4))
     return fail(SDM_ERR_INVALID, "selection-gradient arrays must be 4-byte aligned");
-  if (units < 0) return fail(SDM_ERR_INVALID, "units must be >= 0");
-  if ((rc = check_n_k(n, K, "K"))) return rc;
-  if (units > ((int64_t)1 << 32)) return fail(SDM_ERR_INVALID, "units above 2^32");
+  if (units > sdm::kMaxWaveUnits)
+    return fail(SDM_ERR_UNSUPPORTED, "units must be at most 2^26 - 4 per call (got %lld)",
+                (long long)units);
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_select_backward",
                 sdm::launch_select_backward(idx, weight, dweight, units, n, K, dx1, dx2, s), s);
@@ -269,6 +272,8 @@ int sdm_state_init_backward(const float* G, int B, int H, int64_t N, int d_v,
 int sdm_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R, const int32_t* widx,
                       const int32_t* ridx, uint32_t* seen, uint64_t* first, void* stream) {
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  if ((int64_t)B * H > sdm::kMaxMemories)
+    return fail(SDM_ERR_UNSUPPORTED, "B*H must be at most 2^20 memories per call");
   if (N < 1) return fail(SDM_ERR_INVALID, "N must be >= 1");
   if (N > sdm::kTouchMaxN)
     return fail(SDM_ERR_UNSUPPORTED, "N must be at most 2^20 (one N-bit table per memory in LDS)");
@@ -306,7 +311,8 @@ int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int
   if ((widx && !aligned(widx, 4)) || (ridx && !aligned(ridx, 4)))
     return fail(SDM_ERR_INVALID, "widx and ridx must be 4-byte aligned");
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
-  if ((int64_t)B * H > 0x7FFFFFFF) return fail(SDM_ERR_INVALID, "B*H too large");
+  if ((int64_t)B * H > sdm::kMaxMemories)
+    return fail(SDM_ERR_UNSUPPORTED, "B*H must be at most 2^20 memories per call");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_step_decode",
                 sdm::launch_step_decode(M, dtype, B, H, n, d_v, W, R, s1, s2, q1, q2, v, alpha,

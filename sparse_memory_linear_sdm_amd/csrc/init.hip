@@ -81,7 +81,7 @@ hipError_t launch_state_init(void* M, int dtype, const float* M0, int B, int H, 
   const int64_t per4 = N * d_v / 4;
   const int64_t total = (int64_t)H * per4 / (dtype == 2 ? 4 : (dtype == 1 ? 2 : 1));
   int64_t blocks = (total + 256 * kU - 1) / (256 * kU);
-  if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;  // beyond that the loop strides over the rest
+  if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;  // the loop strides over the rest
   if (dtype == 2)
     hipLaunchKernelGGL(init_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, M,
                        reinterpret_cast<const f32x4*>(M0), B, H, per4);

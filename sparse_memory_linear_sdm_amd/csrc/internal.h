@@ -6,6 +6,21 @@
 
 namespace sdm {
 
+// A kernel dispatch counts its grid in work-items in a 32-bit field, so no
+// launch may hold 2^32 or more of them.  The C-ABI layer keeps every call
+// within these bounds before it launches anything:
+//   one 64-lane wavefront per unit, four per 256-thread block (selection,
+//   selection gradient, the reverse scan's finishing pass over memories x
+//   steps): at most 2^26 - 4 units, so ceil(units / 4) * 256 < 2^32;
+constexpr int64_t kMaxWaveUnits = ((int64_t)1 << 26) - 4;
+//   one or a few workgroups per memory and column tile (scan, reverse scan,
+//   decode, bookkeeping): at most 2^20 memories, so blocks * threads stays
+//   below 2^31 for every tile width and shard count the launchers pick.
+constexpr int64_t kMaxMemories = (int64_t)1 << 20;
+//   grid-stride kernels (state init) cap their grid at this many blocks of
+//   256 threads and loop over the rest.
+constexpr int64_t kMaxStrideBlocks = ((int64_t)1 << 24) - 1;
+
 hipError_t launch_select(const float* x1, const float* x2, int64_t units, int n, int K,
                          int32_t* idx, float* score, float* weight, hipStream_t stream);
 

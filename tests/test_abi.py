@@ -149,8 +149,12 @@ def test_training_calls_validation():
     assert L.sdm_scan_backward(*a) == 1
     a = list(ok); a[4] = 1 << 26
     assert L.sdm_scan_backward(*a) == 2
-    a = list(ok); a[0] = 1 << 12; a[1] = 1 << 12; a[4] = 1 << 10
-    assert L.sdm_scan_backward(*a) == 2 and "2^33" in _err()
+    # one finishing wavefront per memory and step: B*H*T of 2^26 would need
+    # 2^32 work-items in one launch
+    a = list(ok); a[0] = 1 << 8; a[1] = 1 << 8; a[4] = 1 << 10
+    assert L.sdm_scan_backward(*a) == 2 and "2^26 - 4" in _err()
+    a = list(ok); a[0] = 1 << 11; a[1] = 1 << 10  # 2^21 memories
+    assert L.sdm_scan_backward(*a) == 2 and "2^20" in _err()
     a = list(ok); a[3] = 24
     assert L.sdm_scan_backward(*a) == 2
     a = list(ok); a[3] = 128; a[4] = 40000; a[5] = 64; a[6] = 64
@@ -178,6 +182,28 @@ def test_training_calls_validation():
     assert L.sdm_touch_prepare(*a) == 2 and "2 GiB" in _err()
     a = list(ok); a[6] = None
     assert L.sdm_touch_prepare(*a) == 1  # widx NULL with T > 0
+    a = list(ok); a[0] = 1 << 11; a[1] = 1 << 10
+    assert L.sdm_touch_prepare(*a) == 2 and "2^20" in _err()
+    # sdm_select_backward: units at the launch limit (ceil(units/4) blocks of 256 threads)
+    assert L.sdm_select_backward(FAKE, FAKE, FAKE, (1 << 26) - 3, 64, 8, FAKE, FAKE, None) == 2
+
+
+def test_launch_size_limits():
+    """Every call that launches one wavefront per unit, or walks memories,
+    rejects sizes whose grid would need 2^32 work-items, before any launch."""
+    L = sdm.lib()
+    # select: (units + 3) / 4 blocks of 256 threads; 2^26 - 4 units is the largest grid
+    assert L.sdm_select(FAKE, FAKE, (1 << 26) - 3, 64, 8, FAKE, FAKE, FAKE, None) == 2
+    assert "2^26 - 4" in _err()
+    assert L.sdm_select(FAKE, FAKE, 1 << 32, 64, 8, FAKE, FAKE, FAKE, None) == 2
+    # scan / scan_train: at most 2^20 memories
+    assert L.sdm_scan(FAKE, 0, 1 << 11, 1 << 10, 4096, 16, 8, 8, 8, *[FAKE] * 9, None) == 2
+    assert "2^20" in _err()
+    assert L.sdm_scan_train(FAKE, 1 << 11, 1 << 10, 4096, 16, 8, 8, 8, *[FAKE] * 9,
+                            FAKE, None) == 2
+    # decode
+    ok = [FAKE, 1, 1 << 11, 1 << 10, 64, 128, 8, 8] + [FAKE] * 8 + [None, None, None]
+    assert L.sdm_step_decode(*ok) == 2 and "2^20" in _err()
 
 
 def test_fp8_state_validation():

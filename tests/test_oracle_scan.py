@@ -204,7 +204,7 @@ def test_column_range_equals_full():
     assert np.array_equal(r1["out"][:, 3:11], r2["out"][:, 3:11])
 
 
-@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("dtype", [F32, BF16, oracle.FP8])
 def test_decode_steps_equal_scan(dtype):
     cfg = S.CONFIGS["tiny"].with_(B=2, H=3, T=40)
     names = ("s1", "s2", "q1", "q2", "v", "alpha", "beta")
@@ -247,9 +247,28 @@ def test_bf16_round_to_nearest_even():
 
 # ------------------------------------------------ independent numpy model
 
+def bf16_rne_f64(u):
+    """float64 values -> the nearest bf16 values (ties to even), as float32.
+    Integer rounding of the float64 bit pattern: bf16 keeps the sign, the
+    exponent and the top 7 of the 52 fraction bits, so the low 45 bits are
+    rounded away (a carry into the exponent is the correct round-up).  Valid
+    for zero and for magnitudes in binary32's normal range, which the callers
+    assert."""
+    u = np.asarray(u, np.float64)
+    a = np.abs(u)
+    assert np.all((a == 0) | ((a >= 2.0 ** -126) & (a < 2.0 ** 128))), "outside the normal range"
+    b = u.view(np.uint64)
+    one = np.uint64(1)
+    r = ((b + np.uint64((1 << 44) - 1) + ((b >> np.uint64(45)) & one)) >> np.uint64(45)) \
+        << np.uint64(45)
+    return r.view(np.float64).astype(np.float32)  # exact: 8 significant bits
+
+
 def numpy_model(g, W, R, dtype=F32):
     """Whole sequence with brute-force global selection over all N sums and
-    the update written elementwise; no code shared with the oracle."""
+    the update written elementwise; no code shared with the oracle.  bf16
+    state: M0 and every stored row are rounded to bf16 (nearest even), the
+    update itself is taken in float64 from the stored values."""
     n = g["s1"].shape[1]
     M = g["M0"][0].astype(np.float32).copy()
     if dtype == BF16:
@@ -271,7 +290,7 @@ def numpy_model(g, W, R, dtype=F32):
         m = M[wi].astype(np.float64)
         mt = float(g["alpha"][t]) * m
         u = mt + float(g["beta"][t]) * wk[:, None] * (g["v"][t].astype(np.float64) - mt)
-        M[wi] = u.astype(np.float32)
+        M[wi] = bf16_rne_f64(u) if dtype == BF16 else u.astype(np.float32)
         out[t] = (rw[:, None] * M[ri].astype(np.float64)).sum(0).astype(np.float32)
     return M, out
 
@@ -284,6 +303,36 @@ def test_numpy_model_tiny_config():
     Mn, outn = numpy_model(g1, cfg.W, cfg.R)
     np.testing.assert_allclose(M, Mn, rtol=0, atol=2e-7)
     np.testing.assert_allclose(r["out"], outn, rtol=0, atol=2e-7)
+
+
+def test_numpy_model_tiny_config_bf16():
+    """bf16 state: the oracle's stored rows equal, bit for bit, an elementwise
+    float64 update rounded once per store to bf16 by integer rounding of the
+    float64 bits (the oracle rounds with frexp and nearbyint instead)."""
+    cfg, g = tiny_inputs()
+    M, r = run_oracle(cfg, g, dtype=BF16)
+    Mn, outn = numpy_model(g, cfg.W, cfg.R, dtype=BF16)
+    got = oracle.bf16_bits_to_f32(M)
+    assert np.array_equal(got.view(np.uint32), Mn.view(np.uint32))
+    np.testing.assert_allclose(r["out"], outn, rtol=0, atol=2e-7)
+    # the rows really were rewritten (and rounded) many times
+    assert np.count_nonzero(got != oracle.bf16_bits_to_f32(
+        oracle.state_init(g["M0"], 1, BF16)[0, 0])) > 1000
+
+
+def test_bf16_rne_f64_pins():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -40, -2.0,
+                  1 + 255 * 2 ** -8 + 2 ** -9, 0.0, 3.0e38])
+    want = np.array([1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -2.0, 2.0, 0.0, 3.0e38], np.float64)
+    want[-1] = float(np.float32(np.uint32(0x7F620000).view(np.float32)))
+    got = bf16_rne_f64(x)
+    assert np.array_equal(got.astype(np.float64), want), got
+    # agrees with the oracle's rounding on random float64 values
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal(3000) * np.exp(rng.uniform(-20, 20, 3000))
+    ref = np.array([oracle.bf16_from_double(float(v)) for v in y], np.uint16)
+    assert np.array_equal(oracle.bf16_bits_to_f32(ref).view(np.uint32),
+                          bf16_rne_f64(y).view(np.uint32))
 
 
 def test_rejects_repeated_write_row():

@@ -52,7 +52,8 @@
  *   - Size limits per call (a kernel launch counts its work-items in 32 bits):
  *     at most 2^20 memories (B*H) for every call that walks memories, and at
  *     most 2^26 - 4 selection units (sdm_select, sdm_select_backward) or
- *     memory-steps B*H*T (sdm_scan_backward); larger work is split by the
+ *     memory-steps B*H*T (sdm_scan_backward), and for the scans at most 2^32
+ *     steps T and 2^40 memory-steps B*H*T; larger work is split by the
  *     caller into several calls.  Beyond them a call returns
  *     SDM_ERR_UNSUPPORTED before launching anything.
  *   - Calls on different streams are independent as long as they do not

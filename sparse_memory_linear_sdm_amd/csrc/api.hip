@@ -7,6 +7,7 @@
 
 #include "../../include/sdm.h"
 #include "internal.h"
+#include "ranges.h"
 
 namespace {
 
@@ -148,11 +149,17 @@ int check_scan_args(const void* M, int dtype, int B, int H, int64_t N, int d_v, 
   if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
   if ((int64_t)B * H > sdm::kMaxMemories)
     return fail(SDM_ERR_UNSUPPORTED, "B*H must be at most 2^20 memories per call");
+  // bounds every size product the call and its launchers form from T (e.g.
+  // B*H*T*d_v*4 bytes of output, T*(W+R)*d_v*4 bytes of tape) well inside 63 bits
+  if (T > sdm::kMaxSteps || (int64_t)B * H * T > sdm::kMaxMemorySteps)
+    return fail(SDM_ERR_UNSUPPORTED, "T must be at most 2^32 and B*H*T at most 2^40 per call");
   if (W < 1 || R < 1) return fail(SDM_ERR_INVALID, "W and R must be >= 1");
   if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W and R above 64 are not compiled");
   if (W > N || R > N) return fail(SDM_ERR_INVALID, "W and R must not exceed N");
   if (N * d_v * elem_bytes(dtype) >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's table must be below 2 GiB for sdm_scan");
+  if (!sdm::ranges::scan_ok(N, d_v, (int)elem_bytes(dtype), T, W, R, false))
+    return fail(SDM_ERR_UNSUPPORTED, "a state tile's buffer range does not fit 31 bits");
   return SDM_OK;
 }
 
@@ -187,6 +194,8 @@ int sdm_scan_train(void* M, int B, int H, int64_t N, int d_v, int64_t T, int W, 
   if (T * (W + R) * d_v * 4 >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*(W+R)*d_v*4 bytes) must be below 2 GiB; "
                 "split the sequence into consecutive calls");
+  if (!sdm::ranges::scan_ok(N, d_v, 4, T, W, R, true))
+    return fail(SDM_ERR_UNSUPPORTED, "a state or tape tile's buffer range does not fit 31 bits");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_scan_train",
                 sdm::launch_scan(M, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
@@ -224,6 +233,8 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
   if (T * (W + R) * d_v * 4 >= ((int64_t)1 << 31))
     return fail(SDM_ERR_UNSUPPORTED, "one memory's tape (T*(W+R)*d_v*4 bytes) must be below 2 GiB; "
                 "split the sequence into consecutive calls");
+  if (!sdm::ranges::scan_backward_ok(N, d_v, T, W, R))
+    return fail(SDM_ERR_UNSUPPORTED, "a gradient or tape tile's buffer range does not fit 31 bits");
   const size_t need = sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
   if (workspace_bytes < need)
     return fail(SDM_ERR_INVALID, "workspace of %zu bytes is below the %zu required",
@@ -287,6 +298,8 @@ int sdm_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R, const in
     return fail(SDM_ERR_INVALID, "widx, ridx and first must not be NULL");
   if (!aligned(seen, 4) || !aligned(widx, 4) || !aligned(ridx, 4) || !aligned(first, 8))
     return fail(SDM_ERR_INVALID, "index arrays and seen must be 4-byte, first 8-byte aligned");
+  if (!sdm::ranges::touch_ok(T, W, R))
+    return fail(SDM_ERR_UNSUPPORTED, "an index or mask buffer range does not fit 31 bits");
   hipStream_t s = (hipStream_t)stream;
   return finish("sdm_touch_prepare",
                 sdm::launch_touch_prepare(B, H, N, T, W, R, widx, ridx, seen, first, s), s);

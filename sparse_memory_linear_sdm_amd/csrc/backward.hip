@@ -37,12 +37,13 @@
 // sequence selects.  Nothing here is a dense contraction: no MFMA.
 #include "device_common.h"
 #include "internal.h"
+#include "ranges.h"
 
 namespace sdm {
 namespace {
 
 constexpr int kBufWord3 = 0x00020000;  // raw buffer access, gfx9 family
-constexpr uint32_t kOffNone = 0x80000000u;  // outside every range: loads 0, stores dropped
+constexpr uint32_t kOffNone = ranges::kOffNone;  // outside every range: loads 0, stores dropped
 constexpr int kHashBits = 12;
 
 struct BwdArgs {
@@ -126,15 +127,15 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(BwdArgs A) {
   const int64_t T = A.T, N = A.N;
   for (int i = lane; i < (1 << kHashBits); i += kWave) tab[i] = ~0ull;
 
+  // descriptor ranges from ranges.h (checked on the host before the launch)
   const int64_t mem_elems = N * d_v;
-  const int tile_bytes = tile * COLS * 4;
   const __amdgpu_buffer_rsrc_t gres = __builtin_amdgcn_make_buffer_rsrc(
-      A.G + (int64_t)mem * mem_elems + tile * COLS, 0, (int)(mem_elems * 4 - tile_bytes),
-      kBufWord3);
-  const int64_t tape_elems = T * (W + R) * d_v;  // per step: W pre-write rows, R read rows
+      A.G + (int64_t)mem * mem_elems + tile * COLS, 0,
+      (int)ranges::table_range(N, (int64_t)d_v * 4, tile, COLS * 4), kBufWord3);
+  const int64_t tape_rows = T * (W + R);  // per step: W pre-write rows, R read rows
   const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(A.tape) + (int64_t)mem * tape_elems + tile * COLS, 0,
-      (int)(tape_elems * 4 - tile_bytes), kBufWord3);
+      const_cast<float*>(A.tape) + (int64_t)mem * tape_rows * d_v + tile * COLS, 0,
+      (int)ranges::table_range(tape_rows, (int64_t)d_v * 4, tile, COLS * 4), kBufWord3);
   const uint32_t row_bytes = (uint32_t)d_v * 4u;
   const uint32_t lane_off = (uint32_t)lc * 16u;
 
@@ -515,12 +516,15 @@ __global__ __launch_bounds__(kWave) void touch_kernel(const int32_t* __restrict_
   // Buffer loads and stores with out-of-range offsets instead of branches,
   // so the compiler's wait counts stay exact and the index prefetch stays
   // in flight while a chunk is walked.
+  // descriptor ranges from ranges.h (touch_ok, checked on the host)
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(widx) + mem * T * W, 0, (int)(T * W * 4), kBufWord3);
+      const_cast<int32_t*>(widx) + mem * T * W, 0, (int)ranges::table_range(T * W, 4, 0, 4),
+      kBufWord3);
   const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(ridx) + mem * T * R, 0, (int)(T * R * 4), kBufWord3);
-  const __amdgpu_buffer_rsrc_t fres =
-      __builtin_amdgcn_make_buffer_rsrc(first + mem * T * 2, 0, (int)(T * 16), kBufWord3);
+      const_cast<int32_t*>(ridx) + mem * T * R, 0, (int)ranges::table_range(T * R, 4, 0, 4),
+      kBufWord3);
+  const __amdgpu_buffer_rsrc_t fres = __builtin_amdgcn_make_buffer_rsrc(
+      first + mem * T * 2, 0, (int)ranges::table_range(T, 16, 0, 16), kBufWord3);
   const bool ow = lane < W, orr = lane < R;
   uint32_t cw[kTouchChunk], cr[kTouchChunk], nw[kTouchChunk], nr[kTouchChunk];
   auto load = [&](uint32_t (&w)[kTouchChunk], uint32_t (&r)[kTouchChunk], int64_t c0)

@@ -17,6 +17,11 @@ constexpr int64_t kMaxWaveUnits = ((int64_t)1 << 26) - 4;
 //   decode, bookkeeping): at most 2^20 memories, so blocks * threads stays
 //   below 2^31 for every tile width and shard count the launchers pick.
 constexpr int64_t kMaxMemories = (int64_t)1 << 20;
+//   steps per call: at most 2^32, and at most 2^40 memory-steps (B*H*T), so
+//   that byte counts such as B*H*T*d_v*4 and T*(W+R)*d_v*4 stay far inside
+//   63 bits;
+constexpr int64_t kMaxSteps = (int64_t)1 << 32;
+constexpr int64_t kMaxMemorySteps = (int64_t)1 << 40;
 //   grid-stride kernels (state init) cap their grid at this many blocks of
 //   256 threads and loop over the rest.
 constexpr int64_t kMaxStrideBlocks = ((int64_t)1 << 24) - 1;

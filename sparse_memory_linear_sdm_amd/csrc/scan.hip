@@ -58,6 +58,7 @@
 // The two waves meet at one workgroup barrier per chunk.
 #include "device_common.h"
 #include "internal.h"
+#include "ranges.h"
 
 namespace sdm {
 namespace {
@@ -69,9 +70,9 @@ constexpr int kBmWords = (1 << kBmBits) / 32;
 constexpr int kBmSlots = 2 * kChunk;  // bitmaps of the last two chunks' steps, slot = u % 16
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family GPUs.
 constexpr int kBufWord3 = 0x00020000;
-// Byte offset outside every buffer range the kernel builds (one memory slice
-// is below 2^31 bytes): loads there return zero and stores are dropped.
-constexpr uint32_t kOffNone = 0x80000000u;
+// Byte offset outside every buffer range the kernel builds (ranges.h: every
+// range is below 2^31 bytes): loads there return zero and stores are dropped.
+constexpr uint32_t kOffNone = ranges::kOffNone;
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
@@ -676,19 +677,19 @@ __global__ __launch_bounds__(2 * kWave) void scan_kernel(DT* __restrict__ M, Sca
   Consumer<DT, COLS, D, SAVE> cs;
   cs.lane_off = (uint32_t)(lc * 16);
   cs.accumulate = A.shards > 1;
+  // descriptor ranges from ranges.h (checked on the host before the launch)
+  const int64_t row_bytes = (int64_t)d_v * (int64_t)sizeof(DT);
   if constexpr (SAVE) {
-    const int64_t tape_mem = T * (A.W + A.R) * d_v;  // elements of one memory's tape
-    cs.tape_step = (uint32_t)((A.W + A.R) * d_v * (int)sizeof(DT));
-    cs.read_base = (uint32_t)(A.W * d_v * (int)sizeof(DT));
-    cs.row_bytes = (uint32_t)(d_v * (int)sizeof(DT));
+    const int64_t tape_rows = T * (A.W + A.R);  // rows of one memory's tape
+    cs.tape_step = (uint32_t)((A.W + A.R) * row_bytes);
+    cs.read_base = (uint32_t)(A.W * row_bytes);
+    cs.row_bytes = (uint32_t)row_bytes;
     cs.tres = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<DT*>(A.tape) + (int64_t)mem * tape_mem + (int64_t)tile * COLS, 0,
-        (int)(tape_mem * (int64_t)sizeof(DT) - (int64_t)tile * COLS * (int64_t)sizeof(DT)),
-        kBufWord3);
+        reinterpret_cast<DT*>(A.tape) + (int64_t)mem * tape_rows * d_v + (int64_t)tile * COLS, 0,
+        (int)ranges::table_range(tape_rows, row_bytes, tile, TL::TB), kBufWord3);
   }
   cs.mres = __builtin_amdgcn_make_buffer_rsrc(
-      Mm + (int64_t)tile * COLS, 0,
-      (int)(A.N * d_v * (int64_t)sizeof(DT) - (int64_t)tile * COLS * (int64_t)sizeof(DT)),
+      Mm + (int64_t)tile * COLS, 0, (int)ranges::table_range(A.N, row_bytes, tile, TL::TB),
       kBufWord3);
   __syncthreads();
   cs.template prologue<0>(sh, lr, T);
@@ -708,6 +709,8 @@ hipError_t launch(void* M, ScanArgs A, hipStream_t stream) {
   static_assert((SAVE ? 5 : 3) * Tile<DT, COLS>::NI * D <= 63,
                 "outstanding vector memory operations");
   A.ntiles = A.d_v / COLS;
+  if (!ranges::scan_tiles_ok(A.N, A.d_v, (int)sizeof(DT), A.T, A.W, A.R, COLS, SAVE))
+    return hipErrorInvalidValue;  // never taken: the C-ABI layer checked every tile width
   const int groups = (A.n_mem + 7) / 8;
   const int64_t blocks = (int64_t)groups * A.shards * A.ntiles * 8;
   if (A.shards > 1) {  // the shards add into out

@@ -350,16 +350,22 @@ def test_decode_config_full_size():
 def test_long_config_full_size():
     """16 memories of 2^20 x 128 fp32, T = 2^20 streamed in chunks of 16384
     steps (the state persists across calls).  Head 7 is checked over the whole
-    stream: every selection bit-exact, and columns 0..3 of the outputs and the
-    final state (column 0 carries the planted recall pattern) against the
-    oracle.  Other heads' selections are sampled."""
+    stream: every selection bit-exact, and the outputs and the final state in
+    columns 0..3 (column 0 carries the planted recall pattern) and in one
+    column of every other 16-column tile, each at a different lane and
+    element position, against the oracle (each column's recurrence involves
+    that column alone, so the oracle computes just these).  Other heads'
+    selections are sampled."""
     import torch
 
     import sparse_memory_linear_sdm_amd as sdm
 
     cfg = S.CONFIGS["long"]
     C = 16384
-    hc, cols = 7, (0, 4)
+    hc = 7
+    # column ranges: [0, 4) in tile 0, then column 16k + (5k mod 16) of tile k
+    ranges = [(0, 4)] + [(16 * k + (5 * k) % 16, 16 * k + (5 * k) % 16 + 1) for k in range(1, 8)]
+    colsel = np.concatenate([np.arange(a, b) for a, b in ranges])
     M0 = torch.empty((cfg.H, cfg.N, cfg.d_v), dtype=torch.float32, device="cuda")
     S.device_block(cfg, "M0", M0)
     M = sdm.state_init(M0, cfg.B)
@@ -379,16 +385,18 @@ def test_long_config_full_size():
         torch.cuda.synchronize()
         gd = {"widx": widx, "wscore": wsc, "wk": wk, "ridx": ridx, "rscore": rsc, "rw": rw}
         g = {k: v[0, hc].cpu().numpy() for k, v in gd.items()}
-        gout = out[0, hc, :, cols[0]:cols[1]].cpu().numpy()
+        gout = out[0, hc][:, torch.from_numpy(colsel).cuda()].cpu().numpy()
         host = host_inputs(cfg, 0, 1, hc, 1, t0, C)
         wi, ws, wkk = oracle.select(host["s1"][0, 0], host["s2"][0, 0], cfg.W, threads=16)
         ri, rs, rwk = oracle.select(host["q1"][0, 0], host["q2"][0, 0], cfg.R, threads=16)
         tag = f"long h={hc} chunk {c}"
         check_selection(g["widx"], g["wscore"], g["wk"], wi, ws, wkk, tag + " write")
         check_selection(g["ridx"], g["rscore"], g["rw"], ri, rs, rwk, tag + " read")
-        oo = oracle.scan(Mo, F32, wi, wkk, ri, rwk, host["v"][0, 0], host["alpha"][0, 0],
-                         host["beta"][0, 0], cols=cols)
-        check_values(gout, oo[:, cols[0]:cols[1]], F32, tag + " out")
+        oo = np.zeros((C, cfg.d_v), np.float32)
+        for cr in ranges:  # each call computes (and writes back) its columns only
+            oracle.scan(Mo, F32, wi, wkk, ri, rwk, host["v"][0, 0], host["alpha"][0, 0],
+                        host["beta"][0, 0], cols=cr, out=oo)
+        check_values(gout, oo[:, colsel], F32, tag + " out")
         if t0 <= S.PLANT_WRITE_T < t0 + C:
             assert wi[S.PLANT_WRITE_T - t0, 0] == f_star, "planted slot not written"
         if c == cfg.T // C - 1:
@@ -403,8 +411,8 @@ def test_long_config_full_size():
         del d, widx, wsc, wk, ridx, rsc, rw, out
         if c % 16 == 15:
             print(f"long: {c + 1} of {cfg.T // C} chunks checked", flush=True)
-    gm = M[0, hc, :, cols[0]:cols[1]].cpu().numpy()
-    check_values(gm, Mo[:, cols[0]:cols[1]], F32, "long final M")
+    gm = M[0, hc][:, torch.from_numpy(colsel).cuda()].cpu().numpy()
+    check_values(gm, Mo[:, colsel], F32, "long final M")
     print(f"long: planted recall amplitude at t=T-1, column 0: {recall:.4f}", flush=True)
     del M
     _free()

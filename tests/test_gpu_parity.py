@@ -131,14 +131,14 @@ def test_tiny_config_parity():
     _full_parity(S.CONFIGS["tiny"])
 
 
-@pytest.mark.skip(reason="kept off the GPU for now: it faulted twice under a scan producer whose "
-                         "metadata buffer descriptors got a negative range (chunks past the end, "
-                         "column tiles > 0), so loads past the arrays were not range-checked; that "
-                         "load path is removed and the per-lane loads it replaced are back")
 def test_small_config_parity_subset():
     # The small workload's shapes (n=256, d_v=64, W=R=32) on 2 of its 16
     # memories and its first 512 steps; the full config runs in the
-    # full-size tests.
+    # full-size tests.  (An earlier scan producer faulted here: its per-chunk
+    # value descriptor had a negative range past the end of the sequence for
+    # column tiles > 0.  That loader is gone; every descriptor the kernels
+    # build now comes from ranges.h, checked on the host before each launch
+    # and for this shape by tests/test_buffer_ranges.py.)
     cfg = S.CONFIGS["small"].with_(B=1, H=2, T=512)
     _full_parity(cfg)
 
@@ -233,6 +233,73 @@ def test_scan_row_shards_crowded_steps(dtype):
         om = Mo if dtype == F32 else oracle.bf16_bits_to_f32(Mo)
         check_values(gm, om, dtype, f"crowded shards h={h} M")
         check_values(gout[0, h], oo, dtype, f"crowded shards h={h} out")
+
+
+@pytest.mark.parametrize("B,H,d_v", [(1, 3, 32), (2, 48, 64)])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_scan_skips_out_of_range_rows(B, H, d_v, dtype):
+    """Row indices outside [0, N) given to sdm_scan are skipped: a write slot
+    with such a row touches nothing, a read slot contributes 0.  Hand-built
+    index lists hold -1, N, N + k, 2^31 - 1 and -2^31 among valid rows drawn
+    from a small pool (so rows recur inside the prefetch window and are read
+    in the step that writes them).  The oracle, which accepts valid rows only,
+    runs the same steps on a table extended past N: each invalid write slot j
+    writes sink row N + j (never compared), each invalid read slot reads row
+    N + W, which nothing writes and stays zero.  (3 memories take the
+    two-shard narrow-tile path, 96 memories the wide-tile path.)"""
+    torch = _torch()
+    import sparse_memory_linear_sdm_amd as sdm
+
+    cfg = S.CONFIGS["tiny"].with_(B=B, H=H, n=32, d_v=d_v, T=60, W=16, R=16,
+                                  state="f32" if dtype == F32 else "bf16", seed=995 + H)
+    T, N, W, R = cfg.T, cfg.N, cfg.W, cfg.R
+    rng = np.random.default_rng(995 + H + d_v)
+    pool = rng.choice(N, 40, replace=False)
+    bad_vals = np.array([-1, N, N + 7, N + 1000, 2 ** 31 - 1, -2 ** 31], np.int64)
+
+    def lists(K):
+        idx = np.empty((B, H, T, K), np.int32)
+        for b in range(B):
+            for h in range(H):
+                for t in range(T):
+                    row = rng.choice(pool, K, replace=False).astype(np.int64)
+                    bad = rng.random(K) < 0.3
+                    row[bad] = rng.choice(bad_vals, int(bad.sum()))
+                    idx[b, h, t] = row.astype(np.int32)
+        return idx
+
+    widx, ridx = lists(W), lists(R)
+    assert (widx < 0).any() and (widx >= N).any() and (ridx < 0).any() and (ridx >= N).any()
+    wk = rng.uniform(0.0, 0.3, widx.shape).astype(np.float32)
+    rw = rng.uniform(0.0, 0.3, ridx.shape).astype(np.float32)
+    v = rng.standard_normal((B, H, T, d_v)).astype(np.float32)
+    alpha = rng.uniform(0.9, 1.0, (B, H, T)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (B, H, T)).astype(np.float32)
+    M0 = S.host_block(cfg, "M0")
+    tdt = torch.float32 if dtype == F32 else torch.bfloat16
+    M = sdm.state_init(torch.from_numpy(M0).cuda(), B, tdt)
+    out = sdm.scan(M, *(torch.from_numpy(a).cuda() for a in (widx, wk, ridx, rw, v, alpha, beta)))
+    torch.cuda.synchronize()
+    gout, Mh = out.cpu().numpy(), state_to_host(M)
+    slot = np.arange(W, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            wi = widx[b, h].copy()
+            ri = ridx[b, h].copy()
+            wbad = (wi < 0) | (wi >= N)
+            wi[wbad] = (N + np.broadcast_to(slot, wi.shape))[wbad]
+            ri[(ri < 0) | (ri >= N)] = N + W
+            ext = np.zeros((N + W + 1, d_v), np.float32)
+            ext[:N] = M0[h]
+            Mo = oracle.state_init(ext[None], 1, dtype)[0, 0].copy()
+            oo = oracle.scan(Mo, dtype, wi, wk[b, h].astype(np.float64), ri,
+                             rw[b, h].astype(np.float64), v[b, h], alpha[b, h], beta[b, h])
+            assert not Mo[N + W].any()
+            tag = f"invalid rows b={b} h={h}"
+            gm = Mh[b, h] if dtype == F32 else oracle.bf16_bits_to_f32(Mh[b, h])
+            om = Mo[:N] if dtype == F32 else oracle.bf16_bits_to_f32(Mo[:N])
+            check_values(gm, om, dtype, tag + " M")
+            check_values(gout[b, h], oo, dtype, tag + " out")
 
 
 def test_hazard_same_rows_every_step():

@@ -205,6 +205,27 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                       float* drw, float* dalpha, float* dbeta, const uint64_t* first,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* sdm_scan_backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same reverse pass, with its per-tile partial sums kept in
+ * a scratch buffer the library holds on each GPU instead of a caller
+ * workspace.  That buffer is 64 MiB (aligned to 256 bytes), set up on a GPU
+ * at the first call there and held until the process ends; this call never
+ * allocates or frees memory.  Sizes whose workspace
+ * (sdm_scan_backward_workspace_size) is above 64 MiB return
+ * SDM_ERR_UNSUPPORTED before any launch (use sdm_scan_backward then).  Every
+ * call on one GPU uses that GPU's one buffer, whose contents on entry do not
+ * matter: calls that overlap in time on one GPU (on different streams or
+ * from different threads) race on it and give undefined results, so the
+ * caller must order them.  Arguments, outputs and results are otherwise
+ * those of sdm_scan_backward, bit for bit. */
+int sdm_scan_backward_noalloc(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                              const int32_t* widx, const float* wk, const int32_t* ridx,
+                              const float* rw, const float* v, const float* alpha,
+                              const float* beta, const float* tape, const float* dout, float* G,
+                              float* dv, float* dwk, float* drw, float* dalpha, float* dbeta,
+                              const uint64_t* first, void* stream);
+
 /* Gradient of the selection weights back to the halves ("Meccanismo Core",
  * item 2: slot f = a*n + b scores x1[a] + x2[b]), selections held fixed.
  *   idx, weight  [units, K] from sdm_select;  dweight [units, K] fp32 in.

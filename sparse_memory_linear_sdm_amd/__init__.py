@@ -15,6 +15,7 @@ Calls (same names as the C ABI without the "sdm_" prefix):
 Training (fp32 state; selections held fixed):
   scan_train(M, widx, wk, ridx, rw, v, alpha, beta) -> (out, tape)
   scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G) -> dict
+  scan_backward_noalloc(..., G, out) -> out   (no workspace, no allocation)
   touch_prepare(widx, ridx, N) -> (seen, first)
   select_backward(idx, weight, dweight, n) -> (dx1, dx2)
   state_init_backward(G) -> dM0
@@ -26,7 +27,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdm.so")
-ABI_VERSION = 3  # the library's sdm_abi_version() this binding is written for
+ABI_VERSION = 4  # the library's sdm_abi_version() this binding is written for
 
 SDM_F32 = 0
 SDM_BF16 = 1
@@ -35,7 +36,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_INVALID", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_E
 
 # Every symbol include/sdm.h declares.
 EXPORTS = ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_scan_train",
-           "sdm_scan_backward_workspace_size", "sdm_scan_backward", "sdm_select_backward",
+           "sdm_scan_backward_workspace_size", "sdm_scan_backward", "sdm_scan_backward_noalloc",
+           "sdm_select_backward",
            "sdm_state_init_backward", "sdm_touch_prepare", "sdm_status_string", "sdm_last_error",
            "sdm_abi_version")
 
@@ -66,11 +68,13 @@ def lib():
         L.sdm_scan_backward_workspace_size.restype = ctypes.c_size_t
         L.sdm_scan_backward.argtypes = ([i32, i32, i64, i32, i64, i32, i32] + [p] * 17 +
                                         [ctypes.c_size_t, p])
+        L.sdm_scan_backward_noalloc.argtypes = [i32, i32, i64, i32, i64, i32, i32] + [p] * 17
         L.sdm_touch_prepare.argtypes = [i32, i32, i64, i64, i32, i32, p, p, p, p, p]
         L.sdm_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p, p]
         L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p, p]
         for f in ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode",
                   "sdm_abi_version", "sdm_scan_train", "sdm_scan_backward",
+                  "sdm_scan_backward_noalloc",
                   "sdm_select_backward", "sdm_state_init_backward", "sdm_touch_prepare"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i32]
@@ -336,6 +340,29 @@ def scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, workspace=N
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().sdm_scan_backward(B, H, N, d_v, T, W, R, *ptrs, nbytes, _stream(stream)))
     return o
+
+
+def scan_backward_noalloc(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G, out, first=None,
+                          stream=None):
+    """scan_backward() without a workspace and without any allocation: the
+    library's per-GPU static scratch buffer (64 MiB) holds the partial sums,
+    and out is a dict of caller tensors dv [B,H,T,d_v], dwk [B,H,T,W],
+    drw [B,H,T,R], dalpha, dbeta [B,H,T] (fp32).  Calls on one GPU share the
+    buffer and must not overlap in time.  Returns out."""
+    import torch
+
+    f32 = torch.float32
+    B, H, N, d_v, T, W, R = _scan_shapes(G, widx, ridx)
+    ins = _scan_args(B, H, T, W, R, d_v, widx, wk, ridx, rw, v, alpha, beta)
+    ins += [_arg(tape, f32, (B, H, T, W + R, d_v), "tape"),
+            _arg(dout, f32, (B, H, T, d_v), "dout"), _arg(G, f32, (B, H, N, d_v), "G")]
+    shapes = {"dv": (B, H, T, d_v), "dwk": (B, H, T, W), "drw": (B, H, T, R),
+              "dalpha": (B, H, T), "dbeta": (B, H, T)}
+    ins += [_arg(out[k], f32, shp, k) for k, shp in shapes.items()]
+    af = None if first is None else _arg(first, torch.int64, (B, H, T, 2), "first")
+    ptrs = _gpu(*ins, af)
+    _check(lib().sdm_scan_backward_noalloc(B, H, N, d_v, T, W, R, *ptrs, _stream(stream)))
+    return out
 
 
 def touch_prepare(widx, ridx, N: int, seen=None, first=None, stream=None):

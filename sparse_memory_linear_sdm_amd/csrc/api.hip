@@ -87,7 +87,7 @@ int64_t elem_bytes(int dtype) { return dtype == SDM_F32 ? 4 : (dtype == SDM_BF16
 
 extern "C" {
 
-int sdm_abi_version(void) { return 3; }
+int sdm_abi_version(void) { return 4; }
 
 const char* sdm_status_string(int status) {
   switch (status) {
@@ -208,21 +208,27 @@ size_t sdm_scan_backward_workspace_size(int B, int H, int d_v, int64_t T, int W,
   return sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
 }
 
-int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
-                      const int32_t* widx, const float* wk, const int32_t* ridx,
-                      const float* rw, const float* v, const float* alpha, const float* beta,
-                      const float* tape, const float* dout, float* G, float* dv, float* dwk,
-                      float* drw, float* dalpha, float* dbeta, const uint64_t* first,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by sdm_scan_backward and sdm_scan_backward_noalloc; on
+// success *need is the workspace the reverse pass uses, in bytes.
+int check_backward_args(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                        const int32_t* widx, const float* wk, const int32_t* ridx,
+                        const float* rw, const float* v, const float* alpha, const float* beta,
+                        const float* tape, const float* dout, float* G, float* dv, float* dwk,
+                        float* drw, float* dalpha, float* dbeta, const uint64_t* first,
+                        size_t* need) {
   int rc;
   // G has the state's shape and type: it stands for the state in the shared checks
   if ((rc = check_scan_args(G, SDM_F32, B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
                             beta, dv)))
     return rc;
-  if (T > 0 && (!tape || !dout || !dwk || !drw || !dalpha || !dbeta || !workspace))
+  if (T > 0 && (!tape || !dout || !dwk || !drw || !dalpha || !dbeta))
     return fail(SDM_ERR_INVALID, "a backward input or output pointer is NULL");
-  if (!aligned(tape, 16) || !aligned(dout, 16) || !aligned(G, 16) || !aligned(workspace, 16))
-    return fail(SDM_ERR_INVALID, "tape, dout, G and workspace must be 16-byte aligned");
+  if (!aligned(tape, 16) || !aligned(dout, 16) || !aligned(G, 16))
+    return fail(SDM_ERR_INVALID, "tape, dout and G must be 16-byte aligned");
   if (!aligned(dwk, 4) || !aligned(drw, 4) || !aligned(dalpha, 4) || !aligned(dbeta, 4))
     return fail(SDM_ERR_INVALID, "dwk, drw, dalpha and dbeta must be 4-byte aligned");
   if (!aligned(first, 8)) return fail(SDM_ERR_INVALID, "first must be 8-byte aligned");
@@ -235,7 +241,27 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                 "split the sequence into consecutive calls");
   if (!sdm::ranges::scan_backward_ok(N, d_v, T, W, R))
     return fail(SDM_ERR_UNSUPPORTED, "a gradient or tape tile's buffer range does not fit 31 bits");
-  const size_t need = sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
+  *need = sdm::scan_backward_workspace_bytes(B * H, d_v, T, W, R);
+  return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                      const int32_t* widx, const float* wk, const int32_t* ridx,
+                      const float* rw, const float* v, const float* alpha, const float* beta,
+                      const float* tape, const float* dout, float* G, float* dv, float* dwk,
+                      float* drw, float* dalpha, float* dbeta, const uint64_t* first,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  size_t need = 0;
+  if ((rc = check_backward_args(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, tape,
+                                dout, G, dv, dwk, drw, dalpha, dbeta, first, &need)))
+    return rc;
+  if (T > 0 && !workspace) return fail(SDM_ERR_INVALID, "workspace is NULL");
+  if (!aligned(workspace, 16)) return fail(SDM_ERR_INVALID, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(SDM_ERR_INVALID, "workspace of %zu bytes is below the %zu required",
                 workspace_bytes, need);
@@ -244,6 +270,36 @@ int sdm_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                 sdm::launch_scan_backward(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
                                           beta, tape, dout, G, dv, dwk, drw, dalpha, dbeta, first,
                                           reinterpret_cast<float*>(workspace), s),
+                s);
+}
+
+int sdm_scan_backward_noalloc(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                              const int32_t* widx, const float* wk, const int32_t* ridx,
+                              const float* rw, const float* v, const float* alpha,
+                              const float* beta, const float* tape, const float* dout, float* G,
+                              float* dv, float* dwk, float* drw, float* dalpha, float* dbeta,
+                              const uint64_t* first, void* stream) {
+  int rc;
+  size_t need = 0;
+  if ((rc = check_backward_args(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha, beta, tape,
+                                dout, G, dv, dwk, drw, dalpha, dbeta, first, &need)))
+    return rc;
+  if (need > sdm::kStaticScratchBytes)
+    return fail(SDM_ERR_UNSUPPORTED,
+                "the reverse pass needs %zu bytes of workspace, above the library's %zu-byte "
+                "static buffer; use sdm_scan_backward with a caller workspace",
+                need, sdm::kStaticScratchBytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) return finish("sdm_scan_backward_noalloc", hipSuccess, s);
+  void* ws = nullptr;
+  const hipError_t e = sdm::static_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(SDM_ERR_HIP, "sdm_scan_backward_noalloc: device scratch lookup failed: %s",
+                hipGetErrorString(e));
+  return finish("sdm_scan_backward_noalloc",
+                sdm::launch_scan_backward(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, v, alpha,
+                                          beta, tape, dout, G, dv, dwk, drw, dalpha, dbeta, first,
+                                          reinterpret_cast<float*>(ws), s),
                 s);
 }
 

@@ -53,6 +53,14 @@ hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int
                                 float* dalpha, float* dbeta, const uint64_t* first, float* ws,
                                 hipStream_t stream);
 
+// The library's per-GPU scratch buffer (scratch.hip), for callers that cannot
+// allocate: kStaticScratchBytes of device memory, aligned to 256 bytes, held
+// by every GPU the library runs on until the process ends and shared by every
+// call on that GPU.  static_scratch() returns its address on the current
+// device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_select_backward(const int32_t* idx, const float* w, const float* dw,
                                   int64_t units, int n, int K, float* dx1, float* dx2,
                                   hipStream_t stream);

@@ -82,6 +82,11 @@ hipError_t launch_scan_backward(int B, int H, int64_t N, int d_v, int64_t T, int
                                 const uint64_t* first, float*, hipStream_t) {
   return record(B, H, N, d_v, T, W, R, first != nullptr);
 }
+hipError_t static_scratch(void** ptr) {
+  static float fake[4] __attribute__((aligned(256)));
+  *ptr = fake;
+  return hipSuccess;
+}
 hipError_t launch_select_backward(const int32_t*, const float*, const float*, int64_t units,
                                   int n, int K, float*, float*, hipStream_t) {
   return record(units, n, K);
@@ -203,6 +208,18 @@ int main() {
   CHECK(sdm_scan_backward(1 << 8, 1 << 8, 4096, 16, 1 << 10, 8, 8, I, F, I, F, F, F, F, F, F,
                           F, F, F, F, F, F, nullptr, V, (size_t)-1, nullptr) ==
         SDM_ERR_UNSUPPORTED);
+  CHECK(g_launches == n0 + 1);
+  // the allocation-free variant: same checks, its 64 MiB static workspace bound
+  n0 = g_launches;
+  CHECK(sdm_scan_backward_noalloc(2, 2, 4096, 64, 100, 32, 16, I, F, I, F, F, F, F, F, F, F, F,
+                                  F, F, F, F, U, nullptr) == SDM_OK);
+  CHECK(g_launches == n0 + 1 && g_last[4] == 100 && g_last[7] == 1);
+  // 64 memories x 4096 steps x 8 tiles x 129 sums x 4 bytes = 1.08 GB: too large
+  CHECK(sdm_scan_backward_noalloc(8, 8, 4096, 128, 4096, 64, 64, I, F, I, F, F, F, F, F, F, F,
+                                  F, F, F, F, F, nullptr, nullptr) == SDM_ERR_UNSUPPORTED);
+  CHECK(std::strstr(sdm_last_error(), "static buffer") != nullptr);
+  CHECK(sdm_scan_backward_noalloc(1, 1, 4096, 16, 8, 8, 8, I, F, I, F, F, F, F, F, nullptr, F,
+                                  F, F, F, F, F, nullptr, nullptr) == SDM_ERR_INVALID);
   CHECK(g_launches == n0 + 1);
 
   // ---- selection gradient, M0 gradient, bookkeeping

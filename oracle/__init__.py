@@ -47,6 +47,10 @@ def _L():
         lib.oracle_step_decode.argtypes = [p, i32, i32, i32, i32, i32, i32, i32] + [p] * 10
         lib.oracle_scan_backward.argtypes = [p, i64, i32, i64, i32, i32] + [p] * 17
         lib.oracle_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p]
+        lib.oracle_project.argtypes = [p, p, i64, i32, i32, i32, p, p]
+        lib.oracle_project.restype = ctypes.c_int
+        lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+        lib.oracle_sigmoid.restype = ctypes.c_double
         lib.oracle_last_error.restype = ctypes.c_char_p
         lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         lib.oracle_bf16_from_double.restype = ctypes.c_uint16
@@ -270,3 +274,40 @@ def run_memory(M, dtype, s1, s2, q1, q2, v, alpha, beta, W, R, cols=None, thread
     out = scan(M, dtype, widx, wk, ridx, rw, v, alpha, beta, cols=cols)
     return {"widx": widx, "wscore": wsc, "wk": wk, "ridx": ridx, "rscore": rsc, "rw": rw,
             "out": out}
+
+
+def project(X_bits, Wt_bits, H: int, threads: int = 1):
+    """Linear projections of the tokens (bf16 bits): X [M, d_model], Wt
+    [H, P, d_model] -> (y, yabs), each [M, H, P] float64: the exact dot
+    products and the sums of |x_k w_k| (see sdm_oracle.c).  `threads` > 1
+    splits the tokens over several calls."""
+    X = _c(X_bits, np.uint16)
+    Wt = _c(Wt_bits, np.uint16)
+    M, d_model = X.shape
+    Hw, P, d2 = Wt.shape
+    assert Hw == H and d2 == d_model
+    y = np.empty((M, H, P), np.float64)
+    ya = np.empty((M, H, P), np.float64)
+    L = _L()
+    if threads <= 1 or M < 2 * threads:
+        _check(L.oracle_project(_ptr(X), _ptr(Wt), M, d_model, H, P, _ptr(y), _ptr(ya)))
+        return y, ya
+    step = (M + threads - 1) // threads
+    spans = [(s, min(M, s + step)) for s in range(0, M, step)]
+
+    def run(sp):
+        a, b = sp
+        return L.oracle_project(_ptr(X[a:b]), _ptr(Wt), b - a, d_model, H, P, _ptr(y[a:b]),
+                                _ptr(ya[a:b]))
+
+    with ThreadPoolExecutor(threads) as ex:
+        for rc in ex.map(run, spans):
+            _check(rc)
+    return y, ya
+
+
+def sigmoid(y):
+    """The gates' logistic function, elementwise, float64 (the oracle's exp)."""
+    L = _L()
+    f = np.vectorize(lambda t: L.oracle_sigmoid(float(t)), otypes=[np.float64])
+    return f(np.asarray(y, np.float64))

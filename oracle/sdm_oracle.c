@@ -348,6 +348,50 @@ int oracle_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, 
   return rc;
 }
 
+/* ------------------------------------------------------------ projections
+ *
+ * The step's inputs come from linear projections of each token ("Riepilogo
+ * Tecnico: Sparse Delta Memory (SDM)", section "Meccanismo Core", item 2: the
+ * projected keys and queries are split in two halves; section "Design
+ * IsoFLOP": the projections are sized like the baseline's).  Per token x
+ * (d_model values, bf16) and head h, y = W_h x with W_h [P, d_model] bf16,
+ * P = 4n + d_v + 2, rows in this order: the key halves s1, s2, the query
+ * halves q1, q2 (n each), v (d_v), then the two gate pre-activations.  The
+ * pages name the gates alpha_t, beta_t but not how they are formed; here
+ * alpha = sigma(y_alpha), beta = sigma(y_beta) with the logistic sigma, which
+ * keeps both in (0, 1).
+ *
+ * X [M, d_model] and Wt [H, P, d_model] are bf16 bits.  Outputs, for token
+ * m (= b*T + t): y [M, H, P] double (the exact dot products: every product of
+ * two bf16 values is exact in double, and the sum is taken in order), and
+ * yabs [M, H, P] double, the sum of |x_k w_k| (for the rounding bound of a
+ * binary32 accumulation).  The gates are not applied here; oracle_sigmoid()
+ * gives them. */
+static double bf16_bits_to_double(uint16_t h) { return bf16_to_double(h); }
+
+int oracle_project(const uint16_t* X, const uint16_t* Wt, int64_t M, int d_model, int H, int P,
+                   double* y, double* yabs) {
+  if (!X || !Wt || !y || !yabs) return fail("null pointer");
+  if (M < 0 || d_model < 1 || H < 1 || P < 1) return fail("bad sizes");
+  for (int64_t m = 0; m < M; ++m)
+    for (int h = 0; h < H; ++h)
+      for (int p = 0; p < P; ++p) {
+        const uint16_t* w = Wt + ((int64_t)h * P + p) * d_model;
+        const uint16_t* x = X + m * d_model;
+        double acc = 0.0, aabs = 0.0;
+        for (int k = 0; k < d_model; ++k) {
+          double prod = bf16_bits_to_double(x[k]) * bf16_bits_to_double(w[k]);
+          acc += prod;
+          aabs += fabs(prod);
+        }
+        y[(m * H + h) * P + p] = acc;
+        yabs[(m * H + h) * P + p] = aabs;
+      }
+  return 0;
+}
+
+double oracle_sigmoid(double y) { return 1.0 / (1.0 + exp(-y)); }
+
 /* ------------------------------------------------------------- backward
  *
  * Gradients of the step for training.  The pages train the whole layer end to

@@ -3,6 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config mid]
                     [--no-cpu-baseline] [--train [--train-dense]]
+                    [--front [--d-model 4096]]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: the learned-state copy M[b,h] = M0[h] (sdm_state_init),
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SDM scan tokens/sec + slot-traffic HBM GB/s (% of peak), N=2^20, d_v=128"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_traffic.json")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_bwd_mid_traffic.json")
 LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_traffic.json")
@@ -556,6 +558,105 @@ def run_decode(cfg, args, torch, S, sdm):
                           extra)
 
 
+def cpu_baseline_front(cfg, d_model: int, n_tokens: int = 48):
+    """The oracle's projections and selections for the first n_tokens tokens
+    of sequence 0, all heads; the tokens split over the threads."""
+    import numpy as np
+
+    import oracle
+    import sdm_inputs as S
+
+    H, n, d_v = cfg.H, cfg.n, cfg.d_v
+    P = 4 * n + d_v + 2
+    Xb, Wb = S.projection_inputs(1, n_tokens, d_model, H, P, seed=11)
+    Pw = min(workers(), n_tokens)
+    t0 = time.perf_counter()
+    y, _ = oracle.project(Xb[0], Wb, H, threads=Pw)
+    halves = y[:, :, :4 * n].astype(np.float32)  # the binary32 values the selection takes
+    oracle.select(halves[..., :n], halves[..., n:2 * n], cfg.W, threads=Pw)
+    oracle.select(halves[..., 2 * n:3 * n], halves[..., 3 * n:], cfg.R, threads=Pw)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": Pw, "kind": "oracle",
+            "sample": f"{n_tokens} tokens x {H} heads, d_model {d_model}: projections "
+                      f"(float64 dot products) + write and read selections; {dt:.1f} s wall "
+                      f"on {Pw} threads", "seconds": dt}
+
+
+def run_front(cfg, args, torch, S, sdm):
+    """One step = the front end over the whole [B, T] batch: the token
+    projections (sdm_project, one MFMA GEMM of B*T x d_model by d_model x
+    H*(4n + d_v + 2)) and the write and read selections on its halves."""
+    dev = torch.device("cuda:0")
+    B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
+    d_model = args.d_model
+    P = 4 * n + d_v + 2
+    print(f"[bench] front end {cfg.name}: B{B} T{T} d_model{d_model} -> H{H} x P{P} "
+          f"(n{n} d_v{d_v}), selections W{W} R{R}; generating inputs on the host",
+          file=sys.stderr, flush=True)
+    Xb, Wb = S.projection_inputs(B, T, d_model, H, P, seed=2024)
+    X = torch.from_numpy(Xb.view("int16")).to(dev).view(torch.bfloat16)
+    Wt = torch.from_numpy(Wb.view("int16")).to(dev).view(torch.bfloat16)
+    del Xb, Wb
+    f32 = torch.float32
+    outs = tuple(torch.empty(sh, dtype=f32, device=dev) for sh in
+                 [(B, H, T, n)] * 4 + [(B, H, T, d_v), (B, H, T), (B, H, T)])
+    widx = torch.empty((B, H, T, W), dtype=torch.int32, device=dev)
+    wk = torch.empty((B, H, T, W), dtype=f32, device=dev)
+    ridx = torch.empty((B, H, T, R), dtype=torch.int32, device=dev)
+    rw = torch.empty((B, H, T, R), dtype=f32, device=dev)
+    torch.cuda.synchronize()
+    calibration_copy(args, torch, dev)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(record=None):
+        e = [ev() for _ in range(3)]
+        e[0].record(stream)
+        sdm.project(X, Wt, n, out=outs, stream=stream)
+        e[1].record(stream)
+        sdm.select(outs[0], outs[1], W, out=(widx, None, wk), stream=stream)
+        sdm.select(outs[2], outs[3], R, out=(ridx, None, rw), stream=stream)
+        e[2].record(stream)
+        if record is not None:
+            record.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    g0, g1 = ev(), ev()
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(recs)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = g0.elapsed_time(g1) / args.steps
+    proj_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / args.steps
+    sel_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
+    flops = 2.0 * B * T * d_model * H * P  # algorithmic, one projection launch
+    tflops = flops / (proj_ms * 1e-3) / 1e12
+    workload = (f"front end of {cfg.name}: B{B} T{T} d_model{d_model} -> H{H} (n{n}, N={N}, "
+                f"d_v{d_v}), bf16 projections + selections W={W} R={R}")
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "project_kernel", "algorithmic_flops_per_launch": flops}
+    extra = {"breakdown_ms": {"project": proj_ms, "select_write_read": sel_ms},
+             "d_model": d_model, "wall_s": wall}
+    rec = _common_record(cfg, args, B * T / (ms_step * 1e-3), "tokens/s", ms_step,
+                         "bf16 in, f32 accumulate", workload, roofline, extra)
+    rec["config"]["d_model"] = d_model
+    rec["data"] = ("synthetic (seeded PCG64 bf16 tokens and random projection weights, "
+                   "generated on the host)")
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_front(cfg, d_model)
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
 def run_long(cfg, args, torch, S, sdm):
     """One step = the whole T = 2^20 stream in chunks of 16384 steps.  The
     inputs of each chunk are generated on the GPU outside the timed spans.
@@ -685,6 +786,11 @@ def main():
     ap.add_argument("--train-dense", action="store_true",
                     help="with --train: zero the gradient table and sum all of it (dense mode)"
                          " instead of the sparse-mode bookkeeping")
+    ap.add_argument("--front", action="store_true",
+                    help="time the front end instead: token projections (bf16 MFMA GEMM) + "
+                         "the two selections")
+    ap.add_argument("--d-model", type=int, default=4096,
+                    help="with --front: model width feeding the projections")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the step's kernels back to back on one stream")
     ap.add_argument("--pipeline", action="store_true",
@@ -712,7 +818,9 @@ def main():
     cfg = S.CONFIGS[args.config]
     if args.state is None:
         args.state = cfg.state
-    if args.train:
+    if args.front:
+        rec = run_front(cfg, args, torch, S, sdm)
+    elif args.train:
         rec = run_train(cfg, args, torch, S, sdm)
     elif cfg.decode:
         rec = run_decode(cfg, args, torch, S, sdm)

@@ -72,6 +72,29 @@ extern "C" {
 enum { SDM_OK = 0, SDM_ERR_INVALID = 1, SDM_ERR_UNSUPPORTED = 2, SDM_ERR_HIP = 3 };
 enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8 = 2 };
 
+/* Token projections in front of the step ("Meccanismo Core", item 2: the
+ * projected key k' and query q' are each split in two halves; section
+ * "Design IsoFLOP": the projections are sized like the baseline's).  For
+ * token m = b*T + t and head h, y = Wt[h] x_m (P = 4n + d_v + 2 rows per
+ * head), on the matrix cores: bf16 inputs, fp32 accumulation.
+ *   X      [B*T, d_model] bf16 bits in (row-major, 16-byte aligned).
+ *   Wt     [H, P, d_model] bf16 bits in (16-byte aligned): per head the rows
+ *          giving, in order, s1 (n rows), s2 (n), q1 (n), q2 (n), v (d_v),
+ *          the alpha pre-activation and the beta pre-activation.
+ *   s1, s2, q1, q2  [B, H, T, n] fp32 out: the write key halves and the
+ *          read query halves (the layout sdm_select takes, units = B*H*T).
+ *   v      [B, H, T, d_v] fp32 out.
+ *   alpha, beta  [B, H, T] fp32 out: 1 / (1 + exp(-y)) of the two gate rows.
+ * Each y is a binary32 sum of the d_model exact bf16 products, in an
+ * unspecified order: |y - exact| <= d_model * 2^-24 * sum |x_i w_i| (plus
+ * the gates' expf error).  Sizes: d_model a multiple of 64 in [64, 65536];
+ * n, d_v >= 1; H*P < 2^31; at most 2^24 - 1 tiles of 128 tokens x 128
+ * columns per call.  B*T = 0 is a valid no-op (every array may then be
+ * NULL).  Output pointers must be 4-byte aligned. */
+int sdm_project(const uint16_t* X, const uint16_t* Wt, int B, int T, int d_model, int H, int n,
+                int d_v, float* s1, float* s2, float* q1, float* q2, float* v, float* alpha,
+                float* beta, void* stream);
+
 /* Product-key top-K selection with softmax weights ("Meccanismo Core",
  * item 2), for `units` independent (key or query) half pairs.
  *   x1, x2  [units, n] fp32 half sub-scores (all values finite, and every

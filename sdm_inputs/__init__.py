@@ -329,3 +329,26 @@ def device_block(cfg: Config, name: str, dst, b0: int = 0, h0: int = 0, t0: int 
                 view[:, :, t - t0, 0] = 1.0
             else:
                 view[:, :, t - t0, col] = val
+
+
+def _bf16_bits_rne(a: np.ndarray) -> np.ndarray:
+    """float32 array (finite) -> bf16 bit patterns (uint16), round to nearest
+    even: add 0x7FFF plus the lowest kept bit, then drop the low 16 bits."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    return ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >>
+            np.uint32(16)).astype(np.uint16)
+
+
+def projection_inputs(B: int, T: int, d_model: int, H: int, P: int, seed: int = 0):
+    """Seeded inputs of the token projections, as bf16 bit patterns (uint16):
+    X [B, T, d_model] ~ N(0, 1) and Wt [H, P, d_model] ~ N(0, 1/d_model), so
+    that each projected value is about N(0, 1), the distribution the
+    workloads above give the sub-scores and values.  float32 draws from
+    numpy's PCG64 seeded with `seed` (X first, then Wt), each rounded once to
+    bf16 to nearest even.  The pages train these weights; random ones of the
+    same shape stand in for them."""
+    rng = np.random.default_rng(seed)
+    X = _bf16_bits_rne(rng.standard_normal((B, T, d_model), dtype=np.float32))
+    w = rng.standard_normal((H, P, d_model), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(d_model))
+    return X, _bf16_bits_rne(w)

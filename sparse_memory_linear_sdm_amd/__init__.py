@@ -8,6 +8,7 @@ fallback -- importing works without the library, but every call raises if
 libsdm.so is not built.  PyTorch is used only for device memory and streams.
 
 Calls (same names as the C ABI without the "sdm_" prefix):
+  project(X, Wt, n)                      -> (s1, s2, q1, q2, v, alpha, beta)
   select(x1, x2, K)                      -> (idx, score, weight)
   state_init(M0, B, dtype)               -> M
   scan(M, widx, wk, ridx, rw, v, alpha, beta) -> out      (M updated in place)
@@ -27,7 +28,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdm.so")
-ABI_VERSION = 4  # the library's sdm_abi_version() this binding is written for
+ABI_VERSION = 5  # the library's sdm_abi_version() this binding is written for
 
 SDM_F32 = 0
 SDM_BF16 = 1
@@ -35,7 +36,7 @@ SDM_FP8 = 2
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_INVALID", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_HIP"}
 
 # Every symbol include/sdm.h declares.
-EXPORTS = ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_scan_train",
+EXPORTS = ("sdm_project", "sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_scan_train",
            "sdm_scan_backward_workspace_size", "sdm_scan_backward", "sdm_scan_backward_noalloc",
            "sdm_select_backward",
            "sdm_state_init_backward", "sdm_touch_prepare", "sdm_status_string", "sdm_last_error",
@@ -59,6 +60,7 @@ def lib():
                 f"{LIB_PATH} is not built; run `python -m sparse_memory_linear_sdm_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.sdm_project.argtypes = [p, p, i32, i32, i32, i32, i32, i32] + [p] * 8
         L.sdm_select.argtypes = [p, p, i64, i32, i32, p, p, p, p]
         L.sdm_state_init.argtypes = [p, i32, p, i32, i32, i64, i32, p]
         L.sdm_scan.argtypes = [p, i32, i32, i32, i64, i32, i64, i32, i32] + [p] * 9
@@ -72,7 +74,7 @@ def lib():
         L.sdm_touch_prepare.argtypes = [i32, i32, i64, i64, i32, i32, p, p, p, p, p]
         L.sdm_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p, p]
         L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p, p]
-        for f in ("sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode",
+        for f in ("sdm_project", "sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode",
                   "sdm_abi_version", "sdm_scan_train", "sdm_scan_backward",
                   "sdm_scan_backward_noalloc",
                   "sdm_select_backward", "sdm_state_init_backward", "sdm_touch_prepare"):
@@ -170,6 +172,35 @@ def _units(lead):
     for s in lead:
         units *= s
     return units
+
+
+def project(X, Wt, n: int, out=None, stream=None):
+    """Token projections on the matrix cores: X [B, T, d_model] bfloat16,
+    Wt [H, P, d_model] bfloat16 with P = 4n + d_v + 2 (rows s1, s2, q1, q2,
+    v, alpha, beta of each head).  Returns fp32 (s1, s2, q1, q2) [B, H, T, n],
+    v [B, H, T, d_v], alpha, beta [B, H, T] (the gates through the logistic
+    function).  out = that 7-tuple writes into caller tensors."""
+    import torch
+
+    bf16, f32 = torch.bfloat16, torch.float32
+    if X.dim() != 3 or Wt.dim() != 3:
+        raise ValueError("X must be [B, T, d_model] and Wt [H, P, d_model]")
+    B, T, d_model = X.shape
+    H, P = Wt.shape[0], Wt.shape[1]
+    d_v = P - 4 * n - 2
+    if n < 1 or d_v < 1:
+        raise ValueError(f"Wt has P={P} rows per head: too few for n={n} (P = 4n + d_v + 2)")
+    shapes = [(B, H, T, n)] * 4 + [(B, H, T, d_v), (B, H, T), (B, H, T)]
+    names = ("s1", "s2", "q1", "q2", "v", "alpha", "beta")
+    if out is None:
+        out = tuple(torch.empty(sh, dtype=f32, device=X.device) for sh in shapes)
+    if len(out) != 7:
+        raise ValueError("out must hold 7 tensors (s1, s2, q1, q2, v, alpha, beta)")
+    ptrs = _gpu(_arg(X, bf16, (B, T, d_model), "X"), _arg(Wt, bf16, (H, P, d_model), "Wt"),
+                *(_arg(t, f32, sh, nm) for t, sh, nm in zip(out, shapes, names)))
+    _check(lib().sdm_project(ptrs[0], ptrs[1], B, T, d_model, H, n, d_v, *ptrs[2:],
+                             _stream(stream)))
+    return tuple(out)
 
 
 def select(x1, x2, K: int, out=None, stream=None):

@@ -87,7 +87,7 @@ int64_t elem_bytes(int dtype) { return dtype == SDM_F32 ? 4 : (dtype == SDM_BF16
 
 extern "C" {
 
-int sdm_abi_version(void) { return 4; }
+int sdm_abi_version(void) { return 5; }
 
 const char* sdm_status_string(int status) {
   switch (status) {
@@ -100,6 +100,37 @@ const char* sdm_status_string(int status) {
 }
 
 const char* sdm_last_error(void) { return g_err; }
+
+int sdm_project(const uint16_t* X, const uint16_t* Wt, int B, int T, int d_model, int H, int n,
+                int d_v, float* s1, float* s2, float* q1, float* q2, float* v, float* alpha,
+                float* beta, void* stream) {
+  if (B < 0 || T < 0) return fail(SDM_ERR_INVALID, "B and T must be >= 0 (got %d, %d)", B, T);
+  if (H < 1 || n < 1 || d_v < 1)
+    return fail(SDM_ERR_INVALID, "H, n and d_v must be >= 1 (got %d, %d, %d)", H, n, d_v);
+  if (d_model < 64 || d_model > 65536 || d_model % 64 != 0)
+    return fail(SDM_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in [64, 65536] (got %d)",
+                d_model);
+  const int64_t P = 4 * (int64_t)n + d_v + 2, cols = (int64_t)H * P, M = (int64_t)B * T;
+  if (cols >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "H*(4n + d_v + 2) must be below 2^31 (got %lld)",
+                (long long)cols);
+  if (M == 0) return finish("sdm_project", hipSuccess, (hipStream_t)stream);  // arrays may be NULL
+  if (sdm::project_blocks(M, cols) > sdm::kMaxStrideBlocks)
+    return fail(SDM_ERR_UNSUPPORTED, "more than 2^24 - 1 output tiles of 128 x 128 (B*T=%lld, "
+                "H*P=%lld); split the tokens over several calls", (long long)M, (long long)cols);
+  if (!X || !Wt) return fail(SDM_ERR_INVALID, "X and Wt must not be NULL");
+  if (!aligned(X, 16) || !aligned(Wt, 16))
+    return fail(SDM_ERR_INVALID, "X and Wt must be 16-byte aligned");
+  float* outs[7] = {s1, s2, q1, q2, v, alpha, beta};
+  const char* names[7] = {"s1", "s2", "q1", "q2", "v", "alpha", "beta"};
+  for (int i = 0; i < 7; ++i) {
+    if (!outs[i]) return fail(SDM_ERR_INVALID, "%s is NULL", names[i]);
+    if (!aligned(outs[i], 4)) return fail(SDM_ERR_INVALID, "%s must be 4-byte aligned", names[i]);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_project", sdm::launch_project(X, Wt, B, T, d_model, H, n, d_v, s1, s2, q1, q2,
+                                                   v, alpha, beta, s), s);
+}
 
 int sdm_select(const float* x1, const float* x2, int64_t units, int n, int K, int32_t* idx,
                float* score, float* weight, void* stream) {

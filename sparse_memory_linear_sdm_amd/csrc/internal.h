@@ -29,6 +29,16 @@ constexpr int64_t kMaxStrideBlocks = ((int64_t)1 << 24) - 1;
 hipError_t launch_select(const float* x1, const float* x2, int64_t units, int n, int K,
                          int32_t* idx, float* score, float* weight, hipStream_t stream);
 
+// Token projections (project.hip): one workgroup per kProjTile x kProjTile
+// tile of the [tokens, H*P] output, d_model a multiple of 64.
+constexpr int kProjTile = 128;
+inline int64_t project_blocks(int64_t M, int64_t Ncols) {
+  return ((M + kProjTile - 1) / kProjTile) * ((Ncols + kProjTile - 1) / kProjTile);
+}
+hipError_t launch_project(const uint16_t* X, const uint16_t* Wt, int B, int T, int d_model, int H,
+                          int n, int d_v, float* s1, float* s2, float* q1, float* q2, float* v,
+                          float* alpha, float* beta, hipStream_t stream);
+
 hipError_t launch_state_init(void* M, int dtype, const float* M0, int B, int H, int64_t N,
                              int d_v, hipStream_t stream);
 

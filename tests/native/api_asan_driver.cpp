@@ -52,6 +52,11 @@ hipError_t hipStreamSynchronize(hipStream_t) {
 }
 
 namespace sdm {
+hipError_t launch_project(const uint16_t*, const uint16_t*, int B, int T, int d_model, int H,
+                          int n, int d_v, float*, float*, float*, float*, float*, float*, float*,
+                          hipStream_t) {
+  return record(B, T, d_model, H, n, d_v);
+}
 hipError_t launch_select(const float*, const float*, int64_t units, int n, int K, int32_t*,
                          float*, float*, hipStream_t) {
   return record(units, n, K);
@@ -129,6 +134,32 @@ int main() {
   CHECK(g_launches == n0);
   CHECK(sdm_select(nullptr, nullptr, 0, 64, 8, nullptr, nullptr, nullptr, nullptr) == SDM_OK);
   CHECK(g_launches == n0);  // units = 0: nothing to launch
+
+  // ---- sdm_project
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(buf);
+  n0 = g_launches;
+  CHECK(sdm_project(X, X, 8, 4096, 4096, 8, 1024, 128, F, F, F, F, F, F, F, nullptr) == SDM_OK);
+  CHECK(g_launches == n0 + 1 && g_last[0] == 8 && g_last[1] == 4096 && g_last[2] == 4096 &&
+        g_last[3] == 8 && g_last[4] == 1024 && g_last[5] == 128);
+  n0 = g_launches;
+  CHECK(sdm_project(X, X, 1, 10, 96, 1, 4, 4, F, F, F, F, F, F, F, nullptr) ==
+        SDM_ERR_UNSUPPORTED);
+  CHECK(std::strstr(sdm_last_error(), "multiple of 64") != nullptr);
+  CHECK(sdm_project(X, X, 1, 10, 64, 1 << 20, 1 << 20, 4, F, F, F, F, F, F, F, nullptr) ==
+        SDM_ERR_UNSUPPORTED);  // H*P beyond 2^31
+  CHECK(sdm_project(X, X, 1 << 30, 1 << 30, 64, 1, 4, 4, F, F, F, F, F, F, F, nullptr) ==
+        SDM_ERR_UNSUPPORTED);  // too many tiles
+  CHECK(sdm_project(X, X, 1, 10, 64, 1, 4, 4, F, F, F, nullptr, F, F, F, nullptr) ==
+        SDM_ERR_INVALID);
+  CHECK(std::strstr(sdm_last_error(), "q2") != nullptr);
+  CHECK(sdm_project(X + 1, X, 1, 10, 64, 1, 4, 4, F, F, F, F, F, F, F, nullptr) ==
+        SDM_ERR_INVALID);
+  CHECK(sdm_project(X, X, -1, 10, 64, 1, 4, 4, F, F, F, F, F, F, F, nullptr) == SDM_ERR_INVALID);
+  CHECK(sdm_project(X, X, 1, 10, 64, 1, 0, 4, F, F, F, F, F, F, F, nullptr) == SDM_ERR_INVALID);
+  CHECK(g_launches == n0);
+  CHECK(sdm_project(nullptr, nullptr, 0, 10, 64, 1, 4, 4, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, nullptr, nullptr, nullptr) == SDM_OK);
+  CHECK(g_launches == n0);  // no tokens: nothing to launch
 
   // ---- launch and kernel errors
   g_launch_rc = hipErrorInvalidValue;

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = sdm.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.sdm_abi_version() == 4
+    assert L.sdm_abi_version() == 5
     assert L.sdm_status_string(0) == b"SDM_OK"
     assert L.sdm_status_string(2) == b"SDM_ERR_UNSUPPORTED"
 
@@ -56,6 +56,29 @@ def test_select_validation():
         rc = L.sdm_select(*args)
         assert rc == status, (args, rc, _err())
         assert word in _err()
+
+
+def test_project_validation():
+    L = sdm.lib()
+    ok = (FAKE, FAKE, 2, 100, 256, 2, 64, 16) + (FAKE,) * 7 + (None,)
+    bad = [
+        ((None,) + ok[1:], 1, "NULL"),
+        (ok[:4] + (96,) + ok[5:], 2, "multiple of 64"),
+        (ok[:4] + (0,) + ok[5:], 2, "multiple of 64"),
+        (ok[:4] + (65600,) + ok[5:], 2, "multiple of 64"),
+        (ok[:2] + (-1,) + ok[3:], 1, "B and T"),
+        (ok[:6] + (0,) + ok[7:], 1, "n and d_v"),
+        (ok[:5] + (1 << 20, 1 << 20) + ok[7:], 2, "2^31"),
+        (ok[:2] + (1 << 30, 1 << 30) + ok[4:], 2, "tiles"),
+        (ok[:12] + (None,) + ok[13:], 1, "v is NULL"),
+        (ok[:8] + (FAKE + 2,) + ok[9:], 1, "s1 must be 4-byte aligned"),
+        ((FAKE + 8,) + ok[1:], 1, "16-byte aligned"),
+    ]
+    for args, status, word in bad:
+        rc = L.sdm_project(*args)
+        assert rc == status, (args, rc, _err())
+        assert word in _err(), _err()
+    assert L.sdm_project(None, None, 0, 100, 256, 2, 64, 16, *([None] * 7), None) == 0
 
 
 def test_state_init_validation():

@@ -125,3 +125,23 @@ def test_training_helpers_reject_bad_tensors():
     G = z(B, H, N, d_v)
     expect("dM0", sdm.state_init_backward, G, out=z(H, N, d_v - 1))
     expect("seen", sdm.state_init_backward, G, seen=z(B, H, N // 32 - 1, dtype=i32))
+
+
+def test_project_rejects_bad_inputs_and_outputs():
+    bf = torch.bfloat16
+    d_model, P = 64, 4 * n + d_v + 2
+    X, Wt = z(B, T, d_model, dtype=bf), z(H, P, d_model, dtype=bf)
+    expect("on the GPU", sdm.project, X, Wt, n)
+    expect("X must be", sdm.project, z(B, T, d_model), Wt, n)          # fp32 X
+    expect("X must be", sdm.project, z(B * T, d_model, dtype=bf), Wt, n)
+    expect("too few", sdm.project, X, Wt, P)                            # n too large for P
+    expect("Wt must have shape", sdm.project, X, z(H, P, d_model + 64, dtype=bf), n)
+    outs = [z(B, H, T, n)] * 4 + [z(B, H, T, d_v), z(B, H, T), z(B, H, T)]
+    expect("on the GPU", sdm.project, X, Wt, n, out=tuple(outs))
+    bad = list(outs)
+    bad[4] = z(B, H, T, d_v + 1)
+    expect("v must have shape", sdm.project, X, Wt, n, out=tuple(bad))
+    bad = list(outs)
+    bad[6] = z(B, T, H)
+    expect("beta", sdm.project, X, Wt, n, out=tuple(bad))
+    expect("7 tensors", sdm.project, X, Wt, n, out=tuple(outs[:6]))

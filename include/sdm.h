@@ -86,9 +86,10 @@ enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8 = 2 };
  *   v      [B, H, T, d_v] fp32 out.
  *   alpha, beta  [B, H, T] fp32 out: 1 / (1 + exp(-y)) of the two gate rows.
  * Each y is a binary32 sum of the d_model exact bf16 products, in an
- * unspecified order: |y - exact| <= d_model * 2^-24 * sum |x_i w_i| (plus
- * the gates' expf error).  Sizes: d_model a multiple of 64 in [64, 65536];
- * n, d_v >= 1; H*P < 2^31; at most 2^24 - 1 tiles of 128 tokens x 128
+ * unspecified order: |y - exact| <= (d_model - 1) * 2^-23 * sum |x_i w_i|
+ * (unit roundoff 2^-23 covers any rounding of the additions inside the
+ * matrix unit), plus a few ulps of expf and division for the gates.  Sizes: d_model a multiple of 64 in [64, 65536];
+ * n, d_v >= 1; H*P < 2^31; at most 2^24 - 1 tiles of 256 tokens x 256
  * columns per call.  B*T = 0 is a valid no-op (every array may then be
  * NULL).  Output pointers must be 4-byte aligned. */
 int sdm_project(const uint16_t* X, const uint16_t* Wt, int B, int T, int d_model, int H, int n,

@@ -116,7 +116,7 @@ int sdm_project(const uint16_t* X, const uint16_t* Wt, int B, int T, int d_model
                 (long long)cols);
   if (M == 0) return finish("sdm_project", hipSuccess, (hipStream_t)stream);  // arrays may be NULL
   if (sdm::project_blocks(M, cols) > sdm::kMaxStrideBlocks)
-    return fail(SDM_ERR_UNSUPPORTED, "more than 2^24 - 1 output tiles of 128 x 128 (B*T=%lld, "
+    return fail(SDM_ERR_UNSUPPORTED, "more than 2^24 - 1 output tiles of 256 x 256 (B*T=%lld, "
                 "H*P=%lld); split the tokens over several calls", (long long)M, (long long)cols);
   if (!X || !Wt) return fail(SDM_ERR_INVALID, "X and Wt must not be NULL");
   if (!aligned(X, 16) || !aligned(Wt, 16))

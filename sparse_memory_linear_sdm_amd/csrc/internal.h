@@ -31,7 +31,7 @@ hipError_t launch_select(const float* x1, const float* x2, int64_t units, int n,
 
 // Token projections (project.hip): one workgroup per kProjTile x kProjTile
 // tile of the [tokens, H*P] output, d_model a multiple of 64.
-constexpr int kProjTile = 128;
+constexpr int kProjTile = 256;
 inline int64_t project_blocks(int64_t M, int64_t Ncols) {
   return ((M + kProjTile - 1) / kProjTile) * ((Ncols + kProjTile - 1) / kProjTile);
 }

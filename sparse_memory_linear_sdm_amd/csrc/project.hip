@@ -8,13 +8,19 @@
 //
 // This is the one dense contraction of the path, so it runs on the matrix
 // cores: C = X * Wt^T, X [M, K] and Wt [Ncols, K] bf16 (both K-contiguous),
-// fp32 accumulation with v_mfma_f32_32x32x16_bf16.  Per 256-thread workgroup
-// a 128 x 128 tile of C (2 x 2 wavefronts of 64 x 64, each 2 x 2 MFMA blocks
-// of 32 x 32); K is consumed 64 at a time through double-buffered LDS tiles
-// (rows padded by 16 bytes), the next tiles' global loads in flight while
-// the current ones feed the MFMAs.  Tiles are numbered so that each XCD gets
-// a contiguous range, grouped 8 tiles deep along M, so the workgroups that
-// run together on an XCD share their X rows and W columns in its L2.
+// fp32 accumulation with v_mfma_f32_32x32x16_bf16.  Per 512-thread workgroup
+// a 256 x 256 tile of C: 2 x 4 wavefronts of 128 x 64, each 4 x 2 MFMA
+// blocks of 32 x 32.  K is consumed 32 at a time through a 4-deep ring of
+// LDS stages filled by direct global-to-LDS loads (no staging registers, no
+// LDS store instructions), issued three stages ahead of the MFMAs that read
+// them; one barrier per stage.  Within a stage each operand row is 64 bytes
+// (four 16-byte segments), and segment s of row r sits at position
+// s ^ ((r >> 2) & 3): with that placement the fragment reads (32 rows x one
+// segment per half-wave) measured free of bank conflicts on gfx950, while
+// the unswizzled rows conflict four ways.  Tiles are numbered so that each
+// XCD gets a contiguous range, grouped 8 tiles deep along M, so the
+// workgroups that run together on an XCD share their X rows and W columns in
+// its L2.
 //
 // The epilogue writes each value straight to where the selection and the
 // scan read it: s1, s2, q1, q2 [B, H, T, n], v [B, H, T, d_v], alpha, beta
@@ -28,9 +34,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPBM = kProjTile, kPBN = kProjTile, kPBK = 64, kPPad = 8;  // tile sizes, bf16 elements
-constexpr int kPThreads = 256;
+constexpr int kPBM = kProjTile, kPBN = kProjTile;  // output tile
+constexpr int kPBK = 32;                            // K per stage (bf16 elements)
+constexpr int kPStages = 4;
+constexpr int kPThreads = 512;                      // 8 wavefronts
+constexpr int kPWavesM = 2;                         // wavefront grid 2 (M) x 4 (N)
+constexpr int kPTM = 4, kPTN = 2;                   // 32 x 32 MFMA blocks per wavefront
+constexpr int kPSegs = kPBK / 8;                    // 16-byte segments per row
+constexpr int kPStage = (kPBM + kPBN) * kPBK;       // bf16 elements per stage
+constexpr int kPLoads = kPBM * kPSegs / kPThreads;  // direct loads per thread, operand, stage
 constexpr int kPGroupM = 8;
+static_assert(kPBM == 256 && kPBN == 256, "the wavefront grid covers 256 x 256");
+static_assert(kPLoads == 2 && kPSegs == 4, "the slot numbering assumes 2 loads of 4 segments");
 
 struct ProjArgs {
   const uint16_t* X;   // [M, K] bf16
@@ -43,16 +58,28 @@ struct ProjArgs {
   int nbm, nbn;
 };
 
-struct ProjShared {
-  uint16_t a[2][kPBM][kPBK + kPPad];
-  uint16_t b[2][kPBN][kPBK + kPPad];
-};
-
 __device__ __forceinline__ float sigmoidf_(float y) { return 1.0f / (1.0f + expf(-y)); }
 
+// position of 16-byte segment `seg` in row `row` of a stage
+__device__ __forceinline__ int seg_pos(int row, int seg) { return seg ^ ((row >> 2) & 3); }
+
+// s_waitcnt with only the vector-memory count limited (expcnt and lgkmcnt at
+// their maxima): vmcnt(n) for n < 16
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
+
+// a workgroup barrier without a memory fence (the direct loads are waited for
+// by count just before it); the empty asm keeps the compiler from moving LDS
+// accesses across it
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
-  __shared__ __align__(16) ProjShared sh;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  __shared__ __align__(16) uint16_t lds[kPStages * kPStage];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // tile of this workgroup
   const int64_t nblocks = (int64_t)A.nbm * A.nbn;
@@ -65,71 +92,93 @@ __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
   const int64_t pn = (pid % per_group) / gsz;
   const int64_t m0 = pm * kPBM, n0 = pn * kPBN;
 
-  // global -> LDS: 1024 16-byte segments per operand tile, 4 per thread
-  uint4 ra[4], rb[4];
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  // Direct loads: per operand and stage, load q of wavefront w fills the 64
+  // consecutive 16-byte slots (q * 8 + w) * 64 + lane; slot s is position
+  // s % 4 of row s / 4, so it takes segment seg_pos(row, s % 4) of that row.
+  // Rows past the matrix read its last row (their products land only in
+  // outputs that are never stored).
+  const uint16_t* srcA[kPLoads];
+  const uint16_t* srcB[kPLoads];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + kPThreads * q, row = c >> 3, seg = c & 7;
-      const int64_t gm = m0 + row, gn = n0 + row;
-      const bool vm = gm < A.M, vn = gn < A.Ncols;
-      const uint4 xa = *reinterpret_cast<const uint4*>(A.X + (vm ? gm : A.M - 1) * A.K + k0 + seg * 8);
-      const uint4 xb = *reinterpret_cast<const uint4*>(A.Wt + (vn ? gn : A.Ncols - 1) * A.K + k0 + seg * 8);
-      ra[q] = vm ? xa : make_uint4(0, 0, 0, 0);
-      rb[q] = vn ? xb : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) __attribute__((always_inline)) {
+  for (int q = 0; q < kPLoads; ++q) {
+    const int s = (q * 8 + w) * kWave + lane, row = s / kPSegs, seg = seg_pos(row, s % kPSegs);
+    const int64_t gm = m0 + row < A.M ? m0 + row : A.M - 1;
+    const int64_t gn = n0 + row < A.Ncols ? n0 + row : A.Ncols - 1;
+    srcA[q] = A.X + gm * A.K + seg * 8;
+    srcB[q] = A.Wt + gn * A.K + seg * 8;
+  }
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    uint16_t* base = lds + buf * kPStage;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + kPThreads * q, row = c >> 3, seg = c & 7;
-      *reinterpret_cast<uint4*>(&sh.a[buf][row][seg * 8]) = ra[q];
-      *reinterpret_cast<uint4*>(&sh.b[buf][row][seg * 8]) = rb[q];
+    for (int q = 0; q < kPLoads; ++q) {
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + kt * kPBK),
+                                       (void*)(base + (q * 8 + w) * kWave * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + kt * kPBK),
+                                       (void*)(base + kPBM * kPBK + (q * 8 + w) * kWave * 8), 16,
+                                       0, 0);
     }
   };
 
-  const int wm = w & 1, wn = w >> 1;  // this wavefront's 64 x 64 quarter of the tile
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  f32x16 acc[2][2];
+  const int wm = w % kPWavesM, wn = w / kPWavesM;  // this wavefront's 128 x 64 part of the tile
+  const int lr = lane & 31, lh = lane >> 5;
+  // LDS offsets (elements, within a stage) of this lane's fragments for the
+  // first 16 of the stage's 32 k; the second 16 are segments 2, 3 = offset ^ 16
+  int offA[kPTM], offB[kPTN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kPTM; ++i) {
+    const int row = (wm * kPTM + i) * 32 + lr;
+    offA[i] = row * kPBK + seg_pos(row, lh) * 8;
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kPTN; ++j) {
+    const int row = (wn * kPTN + j) * 32 + lr;
+    offB[j] = kPBM * kPBK + row * kPBK + seg_pos(row, lh) * 8;
+  }
+  f32x16 acc[kPTM][kPTN];
+#pragma unroll
+  for (int i = 0; i < kPTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kPTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = A.K / kPBK;
-  load(0);
-  store(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kPStages - 1; ++s)
+    if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kPBK);  // in flight during the MFMAs
+    // stage kt has landed once at most the loads of the stages issued after
+    // it (2 per operand each) are still outstanding
+    const int after = nk - 1 - kt;
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kPLoads));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPLoads));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    stage_barrier();  // every wavefront's part of stage kt is in; stage kt-1 is read
+    if (kt + kPStages - 1 < nk) issue(kt + kPStages - 1, (kt + kPStages - 1) % kPStages);
+    const uint16_t* base = lds + (kt % kPStages) * kPStage;
 #pragma unroll
-    for (int kk = 0; kk < kPBK; kk += 16) {
-      bf16x8 a[2], b[2];
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 a[kPTM], b[kPTN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&sh.a[buf][wm * 64 + i * 32 + lr][kk + lk]);
+      for (int i = 0; i < kPTM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(base + (offA[i] ^ (kk * 16)));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&sh.b[buf][wn * 64 + j * 32 + lr][kk + lk]);
+      for (int j = 0; j < kPTN; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(base + (offB[j] ^ (kk * 16)));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kPTM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kPTN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(buf ^ 1);  // that buffer was last read before the previous barrier
-    __syncthreads();
   }
 
   // epilogue: lane l, accumulator r of block (i, j) holds C[row][col] with
   // row = 8*(r/4) + 4*(l/32) + r%4 and col = l%32 within the 32 x 32 block
   const int64_t HT = (int64_t)A.H * A.T;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t col = n0 + wn * 64 + j * 32 + lr;
+  for (int j = 0; j < kPTN; ++j) {
+    const int64_t col = n0 + (wn * kPTN + j) * 32 + lr;
     if (col >= A.Ncols) continue;
     const int h = (int)(col / A.P), p = (int)(col % A.P);
     float* dst;
@@ -152,10 +201,10 @@ __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
       gate = true;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kPTM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = m0 + (wm * kPTM + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
         if (row >= A.M) continue;
         const int64_t b = row / A.T, t = row - b * A.T;
         const int64_t tok = b * HT + (int64_t)h * A.T + t;  // ((b*H + h)*T + t)

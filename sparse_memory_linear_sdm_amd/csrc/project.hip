@@ -202,12 +202,23 @@ __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
     }
 #pragma unroll
     for (int i = 0; i < kPTM; ++i) {
+      // this lane's rows in block i: rb + 8*(r/4) + r%4, r = 0..15; the
+      // token (b, t) of rb by one division (tokens < 2^32), then stepped
+      const int64_t rb = m0 + (wm * kPTM + i) * 32 + 4 * lh;
+      if (rb >= A.M) continue;
+      uint32_t b = (uint32_t)rb / (uint32_t)A.T, t = (uint32_t)rb - b * (uint32_t)A.T;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + (wm * kPTM + i) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row >= A.M) continue;
-        const int64_t b = row / A.T, t = row - b * A.T;
-        const int64_t tok = b * HT + (int64_t)h * A.T + t;  // ((b*H + h)*T + t)
+        if (r > 0) {
+          t += (r & 3) ? 1 : 5;  // the row offsets run 0,1,2,3, 8,9,10,11, 16,...
+          while (t >= (uint32_t)A.T) {
+            t -= (uint32_t)A.T;
+            ++b;
+          }
+        }
+        const int64_t row = rb + 8 * (r >> 2) + (r & 3);
+        if (row >= A.M) break;
+        const int64_t tok = (int64_t)b * HT + (int64_t)h * A.T + t;  // ((b*H + h)*T + t)
         const float y = acc[i][j][r];
         dst[tok * stride + off] = gate ? sigmoidf_(y) : y;
       }

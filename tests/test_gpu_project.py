@@ -71,6 +71,9 @@ def _check(Xb, Wb, got, B, T, H, n, d_v, tokens=None, threads=8):
     (1, 129, 64, 1, 1, 1),       # P = 7: one partial column tile; one k step
     (3, 64, 128, 2, 37, 32),     # odd n: parts cross tile edges mid-row
     (1, 300, 512, 2, 256, 64),   # several full column tiles per head
+    (300, 1, 128, 1, 8, 16),     # T = 1: every row of a tile is another sequence
+    (37, 3, 64, 2, 16, 16),      # T = 3: sequences change inside each lane's rows
+    (2, 700, 1024, 1, 128, 128), # row tiles of 256 with a ragged last one; 16 k stages
 ])
 def test_project_parity(B, T, d_model, H, n, d_v):
     Xb, Wb, got, _ = _run(B, T, d_model, H, n, d_v, seed=B * 1000 + T + n)
@@ -140,6 +143,6 @@ def test_project_front_full_size_sampled():
     oracle on every head and every column."""
     B, T, d_model, H, n, d_v = 8, 4096, 4096, 8, 1024, 128
     Xb, Wb, got, _ = _run(B, T, d_model, H, n, d_v, seed=2024)
-    toks = [0, 1, 127, 128, T - 1, T, 5 * T + 777, B * T - 129, B * T - 1]
+    toks = [0, 1, 255, 256, T - 1, T, 5 * T + 777, B * T - 257, B * T - 1]
     worst = _check(Xb, Wb, got, B, T, H, n, d_v, tokens=toks, threads=16)
     print(f"worst |err| / bound = {worst:.3e}")

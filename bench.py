@@ -41,9 +41,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_traffic.json")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_bwd_mid_traffic.json")
 LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_traffic.json")
+PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_front_traffic.json")
 _CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
 SCAN_SOURCES = [os.path.join(_CSRC, f) for f in ("scan.hip", "device_common.h")]
 BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "device_common.h")]
+PROJ_SOURCES = [os.path.join(_CSRC, f) for f in ("project.hip", "device_common.h", "internal.h")]
 
 
 def _code_only(text: str) -> str:
@@ -639,8 +641,12 @@ def run_front(cfg, args, torch, S, sdm):
     tflops = flops / (proj_ms * 1e-3) / 1e12
     workload = (f"front end of {cfg.name}: B{B} T{T} d_model{d_model} -> H{H} (n{n}, N={N}, "
                 f"d_v{d_v}), bf16 projections + selections W={W} R={R}")
+    # traffic: HBM bytes per launch from the committed counter summary (null
+    # once the kernel's sources differ from the ones it was taken on)
+    traffic = measured_traffic(flops, path=PROJ_TRAFFIC_FILE, sources=PROJ_SOURCES) \
+        if (B, T, H, n, d_v, d_model) == (8, 4096, 8, 1024, 128, 4096) else None
     roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "project_kernel", "algorithmic_flops_per_launch": flops}
     extra = {"breakdown_ms": {"project": proj_ms, "select_write_read": sel_ms},
              "d_model": d_model, "wall_s": wall}

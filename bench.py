@@ -560,7 +560,7 @@ def run_decode(cfg, args, torch, S, sdm):
                           extra)
 
 
-def cpu_baseline_front(cfg, d_model: int, n_tokens: int = 48):
+def cpu_baseline_front(cfg, d_model: int, n_tokens: int = 512):
     """The oracle's projections and selections for the first n_tokens tokens
     of sequence 0, all heads; the tokens split over the threads."""
     import numpy as np
@@ -590,7 +590,7 @@ def run_front(cfg, args, torch, S, sdm):
     H*(4n + d_v + 2)) and the write and read selections on its halves."""
     dev = torch.device("cuda:0")
     B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
-    d_model = args.d_model
+    d_model = args.d_model or 2 * n * H
     P = 4 * n + d_v + 2
     print(f"[bench] front end {cfg.name}: B{B} T{T} d_model{d_model} -> H{H} x P{P} "
           f"(n{n} d_v{d_v}), selections W{W} R{R}; generating inputs on the host",
@@ -644,7 +644,7 @@ def run_front(cfg, args, torch, S, sdm):
     # traffic: HBM bytes per launch from the committed counter summary (null
     # once the kernel's sources differ from the ones it was taken on)
     traffic = measured_traffic(flops, path=PROJ_TRAFFIC_FILE, sources=PROJ_SOURCES) \
-        if (B, T, H, n, d_v, d_model) == (8, 4096, 8, 1024, 128, 4096) else None
+        if (B, T, H, n, d_v, d_model) == (8, 4096, 8, 1024, 128, 16384) else None
     roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "project_kernel", "algorithmic_flops_per_launch": flops}
@@ -795,8 +795,9 @@ def main():
     ap.add_argument("--front", action="store_true",
                     help="time the front end instead: token projections (bf16 MFMA GEMM) + "
                          "the two selections")
-    ap.add_argument("--d-model", type=int, default=4096,
-                    help="with --front: model width feeding the projections")
+    ap.add_argument("--d-model", type=int, default=0,
+                    help="with --front: model width feeding the projections (default 2*n*H: "
+                         "the key projection as wide as the model, as in the baseline)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the step's kernels back to back on one stream")
     ap.add_argument("--pipeline", action="store_true",

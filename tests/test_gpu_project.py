@@ -138,10 +138,10 @@ def test_project_empty_and_errors():
 @pytest.mark.slow
 def test_project_front_full_size_sampled():
     """The front end at the mid workload's size (B=8, T=4096, H=8, n=1024,
-    d_v=128, d_model=4096), in the launch the bench times: sampled tokens
-    (first, last, both ends of a row tile and of a sequence) against the
-    oracle on every head and every column."""
-    B, T, d_model, H, n, d_v = 8, 4096, 4096, 8, 1024, 128
+    d_v=128, d_model = 2nH = 16384), in the launch the bench times: sampled
+    tokens (first, last, both ends of a row tile and of a sequence) against
+    the oracle on every head and every column."""
+    B, T, d_model, H, n, d_v = 8, 4096, 16384, 8, 1024, 128
     Xb, Wb, got, _ = _run(B, T, d_model, H, n, d_v, seed=2024)
     toks = [0, 1, 255, 256, T - 1, T, 5 * T + 777, B * T - 257, B * T - 1]
     worst = _check(Xb, Wb, got, B, T, H, n, d_v, tokens=toks, threads=16)

@@ -85,3 +85,22 @@ def test_planted_pattern():
     assert np.all(S.host_block(cfg, "alpha", 0, 1, 0, 2, 1000, 1) == 1.0)
     q1 = S.host_block(cfg, "q1", 0, 1, 0, 2, cfg.T - 1, 1)
     assert np.all(q1[..., i_s] == 16.0)
+
+
+def test_projection_inputs_bf16_rounding_and_scale():
+    """The projection inputs: float32 draws rounded once to bf16 to nearest
+    even (against torch's conversion, ties included), seeded, with the
+    weights scaled by 1/sqrt(d_model)."""
+    import torch
+
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -130,
+                     3.0e38, -0.0], np.float32)  # halfway cases round to the even neighbour
+    want = torch.from_numpy(ties).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(S._bf16_bits_rne(ties), want)
+    X1, W1 = S.projection_inputs(2, 5, 256, 3, 11, seed=9)
+    X2, W2 = S.projection_inputs(2, 5, 256, 3, 11, seed=9)
+    X3, _ = S.projection_inputs(2, 5, 256, 3, 11, seed=10)
+    assert np.array_equal(X1, X2) and np.array_equal(W1, W2) and not np.array_equal(X1, X3)
+    assert X1.shape == (2, 5, 256) and W1.shape == (3, 11, 256) and X1.dtype == np.uint16
+    w = torch.from_numpy(W1.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert abs(float(w.std()) * 16.0 - 1.0) < 0.05  # N(0, 1/256)

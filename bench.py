@@ -42,9 +42,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_traffic.json")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_bwd_mid_traffic.json")
 LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_traffic.json")
 PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_front_traffic.json")
+BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_bf16_traffic.json")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_fp8_traffic.json")
 _CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
-SCAN_SOURCES = [os.path.join(_CSRC, f) for f in ("scan.hip", "device_common.h")]
-BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "device_common.h")]
+SCAN_SOURCES = [os.path.join(_CSRC, f)
+                for f in ("scan.hip", "scan_rows.h", "ranges.h", "device_common.h")]
+BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "ranges.h", "device_common.h")]
 PROJ_SOURCES = [os.path.join(_CSRC, f) for f in ("project.hip", "device_common.h", "internal.h")]
 
 
@@ -287,7 +290,8 @@ def run_prefill(cfg, args, torch, S, sdm):
     scan_gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
     kname = {4: "scan_kernel<float,32,1,false>", 2: "scan_kernel<uint16_t(bf16),32,1,false>",
              1: "scan_kernel<fp8e4m3,32,1,false>"}[es]
-    traffic = measured_traffic(slot_bytes) if (cfg.name == "mid" and es == 4) else None
+    traffic_file = {4: TRAFFIC_FILE, 2: BF16_TRAFFIC_FILE, 1: FP8_TRAFFIC_FILE}[es]
+    traffic = measured_traffic(slot_bytes, traffic_file) if cfg.name == "mid" else None
     workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} "
                 f"{args.state} state")
     roofline = {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -308,7 +312,7 @@ def run_prefill(cfg, args, torch, S, sdm):
                          workload, roofline, extra)
     if not args.no_cpu_baseline and es == 4:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg)
+        rec["cpu_baseline"] = cpu_baseline(cfg, n_heads=cfg.H)  # the whole batch
     else:
         rec["cpu_baseline"] = None
     return rec

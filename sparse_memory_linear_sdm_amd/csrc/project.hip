@@ -10,14 +10,16 @@
 // cores: C = X * Wt^T, X [M, K] and Wt [Ncols, K] bf16 (both K-contiguous),
 // fp32 accumulation with v_mfma_f32_32x32x16_bf16.  Per 512-thread workgroup
 // a 256 x 256 tile of C: 2 x 4 wavefronts of 128 x 64, each 4 x 2 MFMA
-// blocks of 32 x 32.  K is consumed 32 at a time through a 4-deep ring of
-// LDS stages filled by direct global-to-LDS loads (no staging registers, no
-// LDS store instructions), issued three stages ahead of the MFMAs that read
-// them; one barrier per stage.  Within a stage each operand row is 64 bytes
-// (four 16-byte segments), and segment s of row r sits at position
-// s ^ ((r >> 2) & 3): with that placement the fragment reads (32 rows x one
-// segment per half-wave) measured free of bank conflicts on gfx950, while
-// the unswizzled rows conflict four ways.  Tiles are numbered so that each
+// blocks of 32 x 32.  K is consumed 64 at a time through two LDS stages
+// (128 KiB) filled by direct global-to-LDS loads (no staging registers, no
+// LDS store instructions): the loads of stage k+1 are issued right after the
+// barrier of stage k and land while stage k feeds the MFMAs; one barrier per
+// stage (measured: 64-deep stages, two of them, beat 32-deep ones in a ring
+// of 2 to 5 by 10%: half the barriers).  Within a stage each operand row is
+// 128 bytes (eight 16-byte segments), and segment s of row r sits at
+// position s ^ ((r >> 1) & 7): with that placement the fragment reads (32
+// rows x one segment per half-wave) measured free of bank conflicts on
+// gfx950, while unswizzled rows conflict.  Tiles are numbered so that each
 // XCD gets a contiguous range, grouped 8 tiles deep along M, so the
 // workgroups that run together on an XCD share their X rows and W columns in
 // its L2.
@@ -35,8 +37,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPBM = kProjTile, kPBN = kProjTile;  // output tile
-constexpr int kPBK = 32;                            // K per stage (bf16 elements)
-constexpr int kPStages = 4;
+constexpr int kPBK = 64;                            // K per stage (bf16 elements)
+constexpr int kPStages = 2;
 constexpr int kPThreads = 512;                      // 8 wavefronts
 constexpr int kPWavesM = 2;                         // wavefront grid 2 (M) x 4 (N)
 constexpr int kPTM = 4, kPTN = 2;                   // 32 x 32 MFMA blocks per wavefront
@@ -45,7 +47,7 @@ constexpr int kPStage = (kPBM + kPBN) * kPBK;       // bf16 elements per stage
 constexpr int kPLoads = kPBM * kPSegs / kPThreads;  // direct loads per thread, operand, stage
 constexpr int kPGroupM = 8;
 static_assert(kPBM == 256 && kPBN == 256, "the wavefront grid covers 256 x 256");
-static_assert(kPLoads == 2 && kPSegs == 4, "the slot numbering assumes 2 loads of 4 segments");
+static_assert(kPLoads == 4 && kPSegs == 8, "the slot numbering assumes 4 loads of 8 segments");
 
 struct ProjArgs {
   const uint16_t* X;   // [M, K] bf16
@@ -61,7 +63,7 @@ struct ProjArgs {
 __device__ __forceinline__ float sigmoidf_(float y) { return 1.0f / (1.0f + expf(-y)); }
 
 // position of 16-byte segment `seg` in row `row` of a stage
-__device__ __forceinline__ int seg_pos(int row, int seg) { return seg ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int seg_pos(int row, int seg) { return seg ^ ((row >> 1) & 7); }
 
 // s_waitcnt with only the vector-memory count limited (expcnt and lgkmcnt at
 // their maxima): vmcnt(n) for n < 16
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
 
   // Direct loads: per operand and stage, load q of wavefront w fills the 64
   // consecutive 16-byte slots (q * 8 + w) * 64 + lane; slot s is position
-  // s % 4 of row s / 4, so it takes segment seg_pos(row, s % 4) of that row.
+  // s % 8 of row s / 8, so it takes segment seg_pos(row, s % 8) of that row.
   // Rows past the matrix read its last row (their products land only in
   // outputs that are never stored).
   const uint16_t* srcA[kPLoads];
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
   const int wm = w % kPWavesM, wn = w / kPWavesM;  // this wavefront's 128 x 64 part of the tile
   const int lr = lane & 31, lh = lane >> 5;
   // LDS offsets (elements, within a stage) of this lane's fragments for the
-  // first 16 of the stage's 32 k; the second 16 are segments 2, 3 = offset ^ 16
+  // first 16 of the stage's 64 k; the k-th 16 are segments 2k, 2k + 1, at
+  // offset ^ 16k
   int offA[kPTM], offB[kPTN];
 #pragma unroll
   for (int i = 0; i < kPTM; ++i) {
@@ -147,17 +150,14 @@ __global__ __launch_bounds__(kPThreads) void project_kernel(ProjArgs A) {
   for (int s = 0; s < kPStages - 1; ++s)
     if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the loads of the stages issued after
-    // it (2 per operand each) are still outstanding
-    const int after = nk - 1 - kt;
-    if (after >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kPLoads));
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPLoads));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // stage kt has landed once this wavefront's loads are in (they are the
+    // only ones outstanding)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     stage_barrier();  // every wavefront's part of stage kt is in; stage kt-1 is read
     if (kt + kPStages - 1 < nk) issue(kt + kPStages - 1, (kt + kPStages - 1) % kPStages);
     const uint16_t* base = lds + (kt % kPStages) * kPStage;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kPBK / 16; ++kk) {
       bf16x8 a[kPTM], b[kPTN];
 #pragma unroll
       for (int i = 0; i < kPTM; ++i)

@@ -376,6 +376,35 @@ def test_step_decode_reads_rows_it_writes(dtype, overlap, d_v):
     _decode_parity(cfg, dtype, host)
 
 
+@pytest.mark.parametrize("n,W,R,d_v,B,H", [
+    (256, 64, 64, 128, 3, 2),   # the rows in one batch of loads per thread
+    (256, 64, 64, 256, 2, 1),   # fp32: the write, then the read after a barrier
+    (512, 17, 40, 64, 2, 2),
+    (1024, 64, 64, 64, 1, 2),
+    (2048, 33, 64, 16, 1, 1),
+    (256, 1, 1, 16, 2, 2),
+])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_step_decode_parity_large_n(dtype, n, W, R, d_v, B, H):
+    # n = 256 .. 2048 (4 to 32 keys per lane in stage 1), random scores,
+    # several consecutive tokens
+    cfg = S.CONFIGS["decode"].with_(B=B, H=H, n=n, T=4, W=W, R=R, d_v=d_v,
+                                    state="f32" if dtype == F32 else "bf16", seed=406 + n + W)
+    _decode_parity(cfg, dtype)
+
+
+@pytest.mark.parametrize("overlap", ["all", "part"])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_step_decode_reads_rows_it_writes_n256(dtype, overlap):
+    cfg = S.CONFIGS["decode"].with_(B=2, H=2, n=256, T=4, W=64, R=64, d_v=128,
+                                    state="f32" if dtype == F32 else "bf16", seed=407)
+    host = host_inputs(cfg)
+    host["q1"] = host["s1"].copy()
+    if overlap == "all":
+        host["q2"] = host["s2"].copy()
+    _decode_parity(cfg, dtype, host)
+
+
 def _decode_parity(cfg, dtype, host=None):
     torch = _torch()
     import sparse_memory_linear_sdm_amd as sdm
@@ -402,12 +431,13 @@ def _decode_parity(cfg, dtype, host=None):
             check_values(gm, om, dtype, f"decode M b={b} h={h}")
 
 
+@pytest.mark.parametrize("n", [32, 256])
 @pytest.mark.parametrize("dtype", [F32, BF16])
-def test_step_decode_equals_scan(dtype):
+def test_step_decode_equals_scan(dtype, n):
     torch = _torch()
     import sparse_memory_linear_sdm_amd as sdm
 
-    cfg = S.CONFIGS["decode"].with_(B=2, H=2, n=32, T=20, W=12, R=12, d_v=64)
+    cfg = S.CONFIGS["decode"].with_(B=2, H=2, n=n, T=20 if n == 32 else 8, W=12, R=12, d_v=64)
     dev = to_dev(host_inputs(cfg))
     M0 = torch.from_numpy(S.host_block(cfg, "M0")).cuda()
     tdt = torch.float32 if dtype == F32 else torch.bfloat16
@@ -427,7 +457,8 @@ def test_step_decode_equals_scan(dtype):
                  "decode vs scan out")
 
 
-@pytest.mark.parametrize("n,W,R", [(64, 16, 64), (256, 64, 37), (1024, 64, 64)])
+@pytest.mark.parametrize("n,W,R", [(64, 16, 64), (256, 64, 37), (1024, 64, 64), (512, 1, 5),
+                                   (2048, 64, 64)])
 def test_step_decode_selection_ties(n, W, R):
     # The fused decode step runs its own search variant; its write and read
     # indices must equal the oracle's selection bit for bit on inputs full of

@@ -44,11 +44,14 @@ LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_traffic.json")
 PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_front_traffic.json")
 BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_bf16_traffic.json")
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_fp8_traffic.json")
+LONG_PLANNED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_planned_traffic.json")
 _CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
 SCAN_SOURCES = [os.path.join(_CSRC, f)
                 for f in ("scan.hip", "scan_rows.h", "ranges.h", "device_common.h")]
 BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "ranges.h", "device_common.h")]
 PROJ_SOURCES = [os.path.join(_CSRC, f) for f in ("project.hip", "device_common.h", "internal.h")]
+PLANNED_SOURCES = [os.path.join(_CSRC, f) for f in
+                   ("scan_planned.hip", "planned.h", "scan_rows.h", "ranges.h", "device_common.h")]
 
 
 def _code_only(text: str) -> str:
@@ -698,6 +701,10 @@ def run_long(cfg, args, torch, S, sdm):
                     torch.empty((B, H, C, R), dtype=torch.int32, device=dev),
                     torch.empty((B, H, C, R), dtype=f32, device=dev)))
     out = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
+    planned = args.planned
+    if planned:  # one plan workspace per chunk buffer
+        wsb = sdm.scan_plan_workspace_size(B, H, d_v, C)
+        plans = [torch.empty((wsb,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
     torch.cuda.synchronize()
     calibration_copy(args, torch, dev)
     stream = torch.cuda.current_stream()
@@ -712,10 +719,16 @@ def run_long(cfg, args, torch, S, sdm):
         x, (wi, wkk, ri, rww) = inp[c % nbuf], sel[c % nbuf]
         sdm.select(x["s1"], x["s2"], W, out=(wi, None, wkk), stream=s)
         sdm.select(x["q1"], x["q2"], R, out=(ri, None, rww), stream=s)
+        if planned:  # the planned scan's lists for this chunk, beside the previous scan too
+            sdm.scan_plan(wi, wkk, ri, rww, N, d_v, workspace=plans[c % nbuf], stream=s)
 
     def scan(c):
         x, (wi, wkk, ri, rww) = inp[c % nbuf], sel[c % nbuf]
-        sdm.scan(M, wi, wkk, ri, rww, x["v"], x["alpha"], x["beta"], out=out, stream=stream)
+        if planned:
+            sdm.scan_planned(M, x["v"], x["alpha"], x["beta"], plans[c % nbuf], out=out,
+                             stream=stream)
+        else:
+            sdm.scan(M, wi, wkk, ri, rww, x["v"], x["alpha"], x["beta"], out=out, stream=stream)
 
     def timed(fn):
         e0, e1 = ev(), ev()
@@ -767,15 +780,22 @@ def run_long(cfg, args, torch, S, sdm):
     slot_bytes = B * H * T * (2 * W + R) * d_v * 4
     gbps = slot_bytes / (scan_ms * 1e-3) / 1e9
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
+    if planned:
+        workload += ", planned scan"
+        kernel = ("planned_kernel<4,4>, four row shards of 32-column tiles (duration includes "
+                  "the shards' combine kernel of the same call)")
+        traffic = measured_traffic(slot_bytes // nch, LONG_PLANNED_TRAFFIC_FILE, PLANNED_SOURCES)
+    else:
+        kernel = ("scan_kernel<float,16,3,false>, two row shards (duration includes the output "
+                  "zero fill of the same call)")
+        traffic = measured_traffic(slot_bytes // nch, LONG_TRAFFIC_FILE)
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbps / HBM_PEAK_GBPS,
-                "traffic": measured_traffic(slot_bytes // nch, LONG_TRAFFIC_FILE),
-                "kernel": "scan_kernel<float,16,3,false>, two row shards (duration includes the "
-                          "output zero fill of the same call)", "algorithmic_bytes_per_launch":
-                slot_bytes // nch}
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic, "kernel": kernel,
+                "algorithmic_bytes_per_launch": slot_bytes // nch}
+    side_work = "selections and plan" if planned else "selections"
     bd = ({"select_write_read": sel_ms, "scan": scan_ms} if args.no_overlap else
           {"select_chunk0": sel_ms, "spans": span_ms, "scan": scan_ms,
-           "overlap": "selections of chunk c+1 || scan of chunk c"})
+           "overlap": f"{side_work} of chunk c+1 || scan of chunk c"})
     extra = {"breakdown_ms": bd, "wall_s": wall, "cpu_baseline": None}
     return _common_record(cfg, args, B * T / (ms_step * 1e-3), "tokens/s", ms_step, "f32",
                           workload, roofline, extra)
@@ -796,6 +816,9 @@ def main():
     ap.add_argument("--train-dense", action="store_true",
                     help="with --train: zero the gradient table and sum all of it (dense mode)"
                          " instead of the sparse-mode bookkeeping")
+    ap.add_argument("--planned", action="store_true",
+                    help="with --config long: run the chunks with the planned scan "
+                         "(sdm_scan_plan beside the previous chunk, then sdm_scan_planned)")
     ap.add_argument("--front", action="store_true",
                     help="time the front end instead: token projections (bf16 MFMA GEMM) + "
                          "the two selections")

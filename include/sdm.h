@@ -141,6 +141,47 @@ int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, in
              const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
              const float* v, const float* alpha, const float* beta, float* out, void* stream);
 
+/* ---- Planned scan (fp32 state): the steps of sdm_scan ("Meccanismo Core",
+ * items 3 and 4) in two calls, for workloads with few memories (long
+ * sequences on a handful of heads).  The first call turns the step indices
+ * into per-shard compacted row lists in a caller workspace; the second runs
+ * the steps from those lists.  The rows of a memory are split between S row
+ * shards (S = 1, 2 or 8, chosen from B*H and d_v so the workgroups fill the
+ * GPU), each moved in whole 128-byte row pieces (32 columns).
+ *
+ * Results: M equal to sdm_scan's bit for bit (the same fp32 update of the
+ * same rows in the same step order); out equal to it up to the order of
+ * the read's fp32 additions (per shard in list order, then the shards in a
+ * fixed order), so it is deterministic and the same for any split of the
+ * sequence into consecutive calls.  Index, weight and gate semantics are
+ * sdm_scan's (rows outside [0, N) are skipped; repeated write rows within
+ * one step leave those rows unspecified). */
+
+/* Bytes of workspace for these sizes (0 if they are not supported: B, H < 1,
+ * T < 0, d_v not one of 32, 64, 128, 256).  The workspace holds the lists of
+ * every step and, with S > 1, one fp32 partial output per shard; it grows
+ * with B*H*T, so long sequences are planned and run in consecutive calls of
+ * a bounded T (16384 steps of 16 memories at d_v = 128: about 3.8 GB). */
+size_t sdm_scan_plan_workspace_size(int B, int H, int d_v, int64_t T);
+
+/* Plan T steps.
+ *   widx, wk, ridx, rw  as for sdm_scan; W, R in [1, 64].
+ *   workspace  device buffer of at least sdm_scan_plan_workspace_size bytes,
+ *              256-byte aligned, written by this call (no clearing needed).
+ * T = 0 is a no-op (the arrays may then be NULL). */
+int sdm_scan_plan(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                  const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Run the T steps that sdm_scan_plan wrote into workspace, on the fp32
+ * state M [B, H, N, d_v] in place; v, alpha, beta and out as for sdm_scan
+ * (out 16-byte aligned).  B, H, N, d_v and T must be those of the plan call
+ * (rows at or past N are skipped, so a mismatch gives wrong values but never
+ * an access outside M).  The workspace's partial outputs are overwritten. */
+int sdm_scan_planned(void* M, int B, int H, int64_t N, int d_v, int64_t T, const float* v,
+                     const float* alpha, const float* beta, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* One single-token step for every (b,h): both selections, the write and the
  * read, fused in one kernel (the recurrent inference form; page "Riepilogo
  * Tecnico: Sparse Delta Memory (SDM)", section "Significato e

@@ -17,6 +17,9 @@ Training (fp32 state; selections held fixed):
   scan_train(M, widx, wk, ridx, rw, v, alpha, beta) -> (out, tape)
   scan_backward(widx, wk, ridx, rw, v, alpha, beta, tape, dout, G) -> dict
   scan_backward_noalloc(..., G, out) -> out   (no workspace, no allocation)
+Planned scan (fp32 state; few memories, long sequences):
+  scan_plan(widx, wk, ridx, rw, N, d_v) -> workspace
+  scan_planned(M, v, alpha, beta, workspace) -> out       (M updated in place)
   touch_prepare(widx, ridx, N) -> (seen, first)
   select_backward(idx, weight, dweight, n) -> (dx1, dx2)
   state_init_backward(G) -> dM0
@@ -28,7 +31,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdm.so")
-ABI_VERSION = 5  # the library's sdm_abi_version() this binding is written for
+ABI_VERSION = 6  # the library's sdm_abi_version() this binding is written for
 
 SDM_F32 = 0
 SDM_BF16 = 1
@@ -38,8 +41,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_INVALID", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_E
 # Every symbol include/sdm.h declares.
 EXPORTS = ("sdm_project", "sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode", "sdm_scan_train",
            "sdm_scan_backward_workspace_size", "sdm_scan_backward", "sdm_scan_backward_noalloc",
-           "sdm_select_backward",
-           "sdm_state_init_backward", "sdm_touch_prepare", "sdm_status_string", "sdm_last_error",
+           "sdm_select_backward", "sdm_scan_plan_workspace_size", "sdm_scan_plan",
+           "sdm_scan_planned", "sdm_state_init_backward", "sdm_touch_prepare", "sdm_status_string", "sdm_last_error",
            "sdm_abi_version")
 
 _lib = None
@@ -72,12 +75,17 @@ def lib():
                                         [ctypes.c_size_t, p])
         L.sdm_scan_backward_noalloc.argtypes = [i32, i32, i64, i32, i64, i32, i32] + [p] * 17
         L.sdm_touch_prepare.argtypes = [i32, i32, i64, i64, i32, i32, p, p, p, p, p]
+        L.sdm_scan_plan_workspace_size.argtypes = [i32, i32, i32, i64]
+        L.sdm_scan_plan_workspace_size.restype = ctypes.c_size_t
+        L.sdm_scan_plan.argtypes = [i32, i32, i64, i32, i64, i32, i32] + [p] * 5 + [ctypes.c_size_t, p]
+        L.sdm_scan_planned.argtypes = [p, i32, i32, i64, i32, i64] + [p] * 5 + [ctypes.c_size_t, p]
         L.sdm_select_backward.argtypes = [p, p, p, i64, i32, i32, p, p, p]
         L.sdm_state_init_backward.argtypes = [p, i32, i32, i64, i32, p, p, p]
         for f in ("sdm_project", "sdm_select", "sdm_state_init", "sdm_scan", "sdm_step_decode",
                   "sdm_abi_version", "sdm_scan_train", "sdm_scan_backward",
                   "sdm_scan_backward_noalloc",
-                  "sdm_select_backward", "sdm_state_init_backward", "sdm_touch_prepare"):
+                  "sdm_select_backward", "sdm_state_init_backward", "sdm_touch_prepare",
+                  "sdm_scan_plan", "sdm_scan_planned"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i32]
         L.sdm_status_string.restype = ctypes.c_char_p
@@ -463,3 +471,51 @@ def state_init_backward(G, out=None, seen=None, stream=None):
     pg, ps, po = _gpu(ag, as_, _arg(dM0, f32, (H, N, d_v), "dM0"))
     _check(lib().sdm_state_init_backward(pg, B, H, N, d_v, ps, po, _stream(stream)))
     return dM0
+
+
+def scan_plan_workspace_size(B: int, H: int, d_v: int, T: int) -> int:
+    """Bytes of workspace scan_plan / scan_planned need (0: unsupported)."""
+    return int(lib().sdm_scan_plan_workspace_size(B, H, d_v, T))
+
+
+def scan_plan(widx, wk, ridx, rw, N: int, d_v: int, workspace=None, stream=None):
+    """Plan the steps of a planned scan on memories of N rows of d_v fp32
+    columns: widx, wk [B,H,T,W]; ridx, rw [B,H,T,R].  Returns the workspace
+    (a uint8 device tensor, allocated when None) for scan_planned."""
+    import torch
+
+    if widx.dim() != 4 or ridx.dim() != 4:
+        raise ValueError("widx and ridx must be [B, H, T, W] and [B, H, T, R]")
+    B, H, T, W = widx.shape
+    R = ridx.shape[3]
+    f32 = torch.float32
+    ins = [_arg(widx, torch.int32, (B, H, T, W), "widx"), _arg(wk, f32, (B, H, T, W), "wk"),
+           _arg(ridx, torch.int32, (B, H, T, R), "ridx"), _arg(rw, f32, (B, H, T, R), "rw")]
+    need = scan_plan_workspace_size(B, H, d_v, T)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=widx.device)
+    ptrs = _gpu(*ins, _arg(workspace, None, None, "workspace"))
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().sdm_scan_plan(B, H, N, d_v, T, W, R, *ptrs, nbytes, _stream(stream)))
+    return workspace
+
+
+def scan_planned(M, v, alpha, beta, workspace, out=None, stream=None):
+    """Run the steps scan_plan wrote into workspace on the fp32 state M
+    [B,H,N,d_v] in place; v [B,H,T,d_v]; alpha, beta [B,H,T].  Returns out
+    [B,H,T,d_v] fp32."""
+    import torch
+
+    if M.dim() != 4 or v.dim() != 4:
+        raise ValueError("M and v must be [B, H, N, d_v] and [B, H, T, d_v]")
+    B, H, N, d_v = M.shape
+    T = v.shape[2]
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty((B, H, T, d_v), dtype=f32, device=M.device)
+    ptrs = _gpu(_arg(M, f32, (B, H, N, d_v), "M"), _arg(v, f32, (B, H, T, d_v), "v"),
+                _arg(alpha, f32, (B, H, T), "alpha"), _arg(beta, f32, (B, H, T), "beta"),
+                _arg(out, f32, (B, H, T, d_v), "out"), _arg(workspace, None, None, "workspace"))
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().sdm_scan_planned(ptrs[0], B, H, N, d_v, T, *ptrs[1:], nbytes, _stream(stream)))
+    return out

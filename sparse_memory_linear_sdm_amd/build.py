@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsdm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "select.hip", "scan.hip", "init.hip", "decode.hip", "backward.hip",
-           "scratch.hip", "project.hip"]
+           "scratch.hip", "project.hip", "scan_planned.hip"]
 HIPCC = "/opt/rocm/bin/hipcc"
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

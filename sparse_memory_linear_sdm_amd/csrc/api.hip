@@ -7,6 +7,7 @@
 
 #include "../../include/sdm.h"
 #include "internal.h"
+#include "planned.h"
 #include "ranges.h"
 
 namespace {
@@ -87,7 +88,7 @@ int64_t elem_bytes(int dtype) { return dtype == SDM_F32 ? 4 : (dtype == SDM_BF16
 
 extern "C" {
 
-int sdm_abi_version(void) { return 5; }
+int sdm_abi_version(void) { return 6; }
 
 const char* sdm_status_string(int status) {
   switch (status) {
@@ -417,6 +418,91 @@ int sdm_step_decode(void* M, int dtype, int B, int H, int n, int d_v, int W, int
   return finish("sdm_step_decode",
                 sdm::launch_step_decode(M, dtype, B, H, n, d_v, W, R, s1, s2, q1, q2, v, alpha,
                                         beta, out, widx, ridx, s),
+                s);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shapes the planned scan supports; also bounds its grids (the plan pass
+// launches ceil(T/32) 256-thread workgroups per memory).
+int check_plan_shape(int B, int H, int64_t N, int d_v, int64_t T) {
+  if (B < 1 || H < 1) return fail(SDM_ERR_INVALID, "B and H must be >= 1");
+  if ((int64_t)B * H > sdm::kMaxMemories)
+    return fail(SDM_ERR_UNSUPPORTED, "B*H must be at most 2^20 memories per call");
+  if (T < 0) return fail(SDM_ERR_INVALID, "T must be >= 0");
+  if (T > sdm::kMaxSteps || (int64_t)B * H * T > sdm::kMaxMemorySteps)
+    return fail(SDM_ERR_UNSUPPORTED, "T must be at most 2^32 and B*H*T at most 2^40 per call");
+  if ((int64_t)B * H * ((T + sdm::kPlanSteps - 1) / sdm::kPlanSteps) > sdm::kMaxStrideBlocks)
+    return fail(SDM_ERR_UNSUPPORTED, "B*H*ceil(T/32) must be below 2^24; split the sequence");
+  if (N < 1 || N >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_INVALID, "N must be in [1, 2^31) (got %lld)", (long long)N);
+  if (d_v != 32 && d_v != 64 && d_v != 128 && d_v != 256)
+    return fail(SDM_ERR_UNSUPPORTED, "the planned scan needs d_v in {32, 64, 128, 256} (got %d)", d_v);
+  if (N * d_v * 4 >= ((int64_t)1 << 31))
+    return fail(SDM_ERR_UNSUPPORTED, "one memory's table must be below 2 GiB");
+  if (!sdm::ranges::scan_tiles_ok(N, d_v, 4, T, 1, 1, 32, false))
+    return fail(SDM_ERR_UNSUPPORTED, "a state tile's buffer range does not fit 31 bits");
+  return SDM_OK;
+}
+
+int check_workspace(const void* ws, size_t bytes, int B, int H, int d_v, int64_t T) {
+  const int S = sdm::planned_shards(B * H, d_v);
+  const int64_t need = sdm::plan_layout((int64_t)B * H, S, T, d_v).total;
+  if (!ws) return fail(SDM_ERR_INVALID, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(SDM_ERR_INVALID, "workspace must be 256-byte aligned");
+  if ((int64_t)bytes < need)
+    return fail(SDM_ERR_INVALID, "workspace has %zu bytes, %lld needed", bytes, (long long)need);
+  return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdm_scan_plan_workspace_size(int B, int H, int d_v, int64_t T) {
+  if (B < 1 || H < 1 || T < 0 || (int64_t)B * H > sdm::kMaxMemories || T > sdm::kMaxSteps ||
+      (int64_t)B * H * T > sdm::kMaxMemorySteps)
+    return 0;
+  if (d_v != 32 && d_v != 64 && d_v != 128 && d_v != 256) return 0;
+  const int S = sdm::planned_shards(B * H, d_v);
+  return (size_t)sdm::plan_layout((int64_t)B * H, S, T, d_v).total;
+}
+
+int sdm_scan_plan(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                  const int32_t* widx, const float* wk, const int32_t* ridx, const float* rw,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_plan_shape(B, H, N, d_v, T))) return rc;
+  if (W < 1 || R < 1) return fail(SDM_ERR_INVALID, "W and R must be >= 1");
+  if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W and R above 64 are not compiled");
+  if (T == 0) return SDM_OK;
+  if (!widx || !wk || !ridx || !rw) return fail(SDM_ERR_INVALID, "an index or weight pointer is NULL");
+  if (!aligned(widx, 4) || !aligned(wk, 4) || !aligned(ridx, 4) || !aligned(rw, 4))
+    return fail(SDM_ERR_INVALID, "index and weight arrays must be 4-byte aligned");
+  if ((rc = check_workspace(workspace, workspace_bytes, B, H, d_v, T))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_scan_plan",
+                sdm::launch_scan_plan(B, H, N, d_v, T, W, R, widx, wk, ridx, rw, workspace, s), s);
+}
+
+int sdm_scan_planned(void* M, int B, int H, int64_t N, int d_v, int64_t T, const float* v,
+                     const float* alpha, const float* beta, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_plan_shape(B, H, N, d_v, T))) return rc;
+  if (!M) return fail(SDM_ERR_INVALID, "M is NULL");
+  if (!aligned(M, 16)) return fail(SDM_ERR_INVALID, "M must be 16-byte aligned");
+  if (T == 0) return SDM_OK;
+  if (!v || !alpha || !beta || !out) return fail(SDM_ERR_INVALID, "v, alpha, beta and out must not be NULL");
+  if (!aligned(v, 4) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(out, 16))
+    return fail(SDM_ERR_INVALID, "v, alpha, beta must be 4-byte and out 16-byte aligned");
+  if ((rc = check_workspace(workspace, workspace_bytes, B, H, d_v, T))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  return finish("sdm_scan_planned",
+                sdm::launch_scan_planned(reinterpret_cast<float*>(M), B, H, N, d_v, T, v, alpha,
+                                         beta, out, workspace, s),
                 s);
 }
 

@@ -105,6 +105,21 @@ hipError_t launch_touch_prepare(int B, int H, int64_t N, int64_t T, int W, int R
                                 hipStream_t) {
   return record(B, H, N, T, W, R);
 }
+int planned_shards(int n_mem, int d_v) {  // as the library's rule on 256 compute units
+  const int64_t units = (int64_t)n_mem * (d_v / 32);
+  if (units * 2 > 256) return 1;
+  if (units * 4 > 256) return 2;
+  return 8;
+}
+hipError_t launch_scan_plan(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
+                            const int32_t*, const float*, const int32_t*, const float*, void*,
+                            hipStream_t) {
+  return record(B, H, N, d_v, T, W, R, 1);
+}
+hipError_t launch_scan_planned(float*, int B, int H, int64_t N, int d_v, int64_t T, const float*,
+                               const float*, const float*, float*, void*, hipStream_t) {
+  return record(B, H, N, d_v, T, 0, 0, 2);
+}
 }  // namespace sdm
 
 int main() {
@@ -270,6 +285,59 @@ int main() {
   CHECK(sdm_touch_prepare(1 << 30, 1 << 30, 4096, 50, 8, 8, I, I,
                           reinterpret_cast<uint32_t*>(buf), U, nullptr) == SDM_ERR_UNSUPPORTED);
   CHECK(g_launches == n0 + 4);
+
+  // ---- planned scan
+  {
+    static float ws_buf[64] __attribute__((aligned(256)));
+    void* WS = ws_buf;
+    const size_t need = sdm_scan_plan_workspace_size(1, 16, 128, 16384);
+    // 16 memories x 8 shards x 16384 steps of lists, plus 8 partial outputs
+    const size_t lists = (size_t)16 * 8 * 16384 * (4 + 512 + 512 + 128 + 128);
+    CHECK(need == lists + (size_t)8 * 16 * 16384 * 128 * 4);
+    CHECK(sdm_scan_plan_workspace_size(1, 16, 16, 100) == 0);
+    CHECK(sdm_scan_plan_workspace_size(0, 16, 128, 100) == 0);
+    CHECK(sdm_scan_plan_workspace_size(1, 16, 128, -1) == 0);
+    CHECK(sdm_scan_plan_workspace_size(1 << 30, 1 << 30, 128, 100) == 0);
+    CHECK(sdm_scan_plan_workspace_size(64, 4, 128, 100) ==
+          (size_t)256 * 100 * (4 + 512 + 512 + 128 + 128));  // S = 1: no partials
+    n0 = g_launches;
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, 16384, 64, 64, I, F, I, F, WS, need, nullptr) ==
+          SDM_OK);
+    CHECK(g_launches == n0 + 1 && g_last[1] == 16 && g_last[2] == (1 << 20) && g_last[4] == 16384 &&
+          g_last[7] == 1);
+    CHECK(sdm_scan_planned(V, 1, 16, 1 << 20, 128, 16384, F, F, F, F, WS, need, nullptr) == SDM_OK);
+    CHECK(g_launches == n0 + 2 && g_last[3] == 128 && g_last[7] == 2);
+    n0 = g_launches;
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, 16384, 64, 64, I, F, I, F, WS, need - 1, nullptr) ==
+          SDM_ERR_INVALID);
+    CHECK(std::strstr(sdm_last_error(), "needed") != nullptr);
+    CHECK(sdm_scan_planned(V, 1, 16, 1 << 20, 128, 16384, F, F, F, F, WS, need - 1, nullptr) ==
+          SDM_ERR_INVALID);
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, 100, 64, 64, I, F, I, F, F + 1, need, nullptr) ==
+          SDM_ERR_INVALID);  // workspace not 256-byte aligned
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 16, 100, 64, 64, I, F, I, F, WS, need, nullptr) ==
+          SDM_ERR_UNSUPPORTED);  // d_v 16
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, 100, 65, 64, I, F, I, F, WS, need, nullptr) ==
+          SDM_ERR_UNSUPPORTED);
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, 100, 64, 64, nullptr, F, I, F, WS, need, nullptr) ==
+          SDM_ERR_INVALID);
+    CHECK(sdm_scan_plan(1, 16, (int64_t)1 << 31, 128, 100, 64, 64, I, F, I, F, WS, need,
+                        nullptr) == SDM_ERR_INVALID);
+    CHECK(sdm_scan_plan(1, 16, 1 << 23, 128, 100, 64, 64, I, F, I, F, WS, need, nullptr) ==
+          SDM_ERR_UNSUPPORTED);  // 4 GiB table
+    CHECK(sdm_scan_plan(1 << 20, 1, 1 << 10, 32, (int64_t)1 << 20, 8, 8, I, F, I, F, WS, need,
+                        nullptr) == SDM_ERR_UNSUPPORTED);  // plan grid beyond 2^24 blocks
+    CHECK(sdm_scan_planned(nullptr, 1, 16, 1 << 20, 128, 100, F, F, F, F, WS, need, nullptr) ==
+          SDM_ERR_INVALID);
+    CHECK(sdm_scan_planned(V, 1, 16, 1 << 20, 128, 100, F, F, F, F + 1, WS, need, nullptr) ==
+          SDM_ERR_INVALID);  // out not 16-byte aligned
+    CHECK(g_launches == n0);
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, 0, 64, 64, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, 0, nullptr) == SDM_OK);
+    CHECK(sdm_scan_planned(V, 1, 16, 1 << 20, 128, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           0, nullptr) == SDM_OK);
+    CHECK(g_launches == n0);  // T = 0: nothing to launch
+  }
 
   CHECK(std::strcmp(sdm_status_string(SDM_ERR_HIP), "SDM_ERR_HIP") == 0);
   CHECK(std::strcmp(sdm_status_string(42), "unknown status") == 0);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = sdm.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.sdm_abi_version() == 5
+    assert L.sdm_abi_version() == 6
     assert L.sdm_status_string(0) == b"SDM_OK"
     assert L.sdm_status_string(2) == b"SDM_ERR_UNSUPPORTED"
 

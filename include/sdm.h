@@ -164,7 +164,7 @@ int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, in
  * a bounded T (16384 steps of 16 memories at d_v = 128: about 3.8 GB). */
 size_t sdm_scan_plan_workspace_size(int B, int H, int d_v, int64_t T);
 
-/* Plan T steps.
+/* Plan T steps (T <= 2^20 per call).
  *   widx, wk, ridx, rw  as for sdm_scan; W, R in [1, 64].
  *   workspace  device buffer of at least sdm_scan_plan_workspace_size bytes,
  *              256-byte aligned, written by this call (no clearing needed).

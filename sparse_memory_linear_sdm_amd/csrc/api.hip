@@ -436,6 +436,10 @@ int check_plan_shape(int B, int H, int64_t N, int d_v, int64_t T) {
     return fail(SDM_ERR_UNSUPPORTED, "T must be at most 2^32 and B*H*T at most 2^40 per call");
   if ((int64_t)B * H * ((T + sdm::kPlanSteps - 1) / sdm::kPlanSteps) > sdm::kMaxStrideBlocks)
     return fail(SDM_ERR_UNSUPPORTED, "B*H*ceil(T/32) must be below 2^24; split the sequence");
+  // a workgroup's slices of the lists and of v are addressed by 32-bit
+  // buffer offsets: T * 512 and T * d_v * 4 bytes stay below 2^31
+  if (T > sdm::kPlanMaxSteps)
+    return fail(SDM_ERR_UNSUPPORTED, "the planned scan takes at most 2^20 steps per call; split the sequence");
   if (N < 1 || N >= ((int64_t)1 << 31))
     return fail(SDM_ERR_INVALID, "N must be in [1, 2^31) (got %lld)", (long long)N);
   if (d_v != 32 && d_v != 64 && d_v != 128 && d_v != 256)

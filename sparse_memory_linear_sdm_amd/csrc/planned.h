@@ -44,6 +44,8 @@ inline PlanLayout plan_layout(int64_t n_mem, int S, int64_t T, int d_v) {
 int planned_shards(int n_mem, int d_v);
 // Steps per plan workgroup.
 constexpr int kPlanSteps = 32;
+// Steps per planned call (32-bit offsets into a workgroup's slices).
+constexpr int64_t kPlanMaxSteps = (int64_t)1 << 20;
 hipError_t launch_scan_plan(int B, int H, int64_t N, int d_v, int64_t T, int W, int R,
                             const int32_t* widx, const float* wk, const int32_t* ridx,
                             const float* rw, void* ws, hipStream_t stream);

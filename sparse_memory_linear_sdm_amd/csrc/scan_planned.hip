@@ -285,36 +285,61 @@ enum : uint32_t { kFlagSync = 4u };
 // step (loaded whatever the list length, so no load waits for a header;
 // positions past the length are masked when the plan is written).
 struct ChunkRegs {
-  uint32_t h;
-  uint2 we[kChunk], re[kChunk];
+  uint32_t h, al, be;  // lane s < kChunk: step s's header, alpha, beta
+  u32x2 we[kChunk], re[kChunk];
   uint32_t sw[kChunk], sr[kChunk];
-  float vv[kChunk], ab[kChunk];
+  uint32_t vv[kChunk];
 };
 
 // Loader wavefront: the loads of chunk q + 1 are in flight while chunk q is
-// written into the LDS plan (two register sets).
+// written into the LDS plan (two register sets).  Every load is a raw
+// buffer load through a descriptor over this workgroup's slice of an array,
+// so a masked lane is an out-of-range offset rather than a branch.
 template <int D, int NIC>
 struct Loader {
   static constexpr int C = NIC * kRPI;
-  int mem, tile;
-  int64_t ubase;  // (mem * S + shard) * T
+  __amdgpu_buffer_rsrc_t rhdr, rwent, rrent, rsrcw, rsrcr, rv, ralpha, rbeta;
+  uint32_t off_list, off_src, off_v;  // this lane's byte offset within a step (or kOffNone)
+  uint32_t step_v;                            // bytes between steps of v
 
-  // Issue the loads of chunk q; no wait.  Steps past the end load nothing.
+  __device__ __forceinline__ void init(const PScanArgs& A, int mem, int tile, int64_t ubase) {
+    const int lane = lane_id();
+    const int64_t T = A.T;
+    rhdr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(A.hdr + ubase), 0, (int)(T * 4), kBufWord3);
+    rwent = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint2*>(A.went + ubase * 64), 0, (int)(T * 512), kBufWord3);
+    rrent = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint2*>(A.rent + ubase * 64), 0, (int)(T * 512), kBufWord3);
+    rsrcw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A.srcw + ubase * 64), 0, (int)(T * 128), kBufWord3);
+    rsrcr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A.srcr + ubase * 64), 0, (int)(T * 128), kBufWord3);
+    rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(A.v + (int64_t)mem * T * A.d_v + (int64_t)tile * kCols), 0,
+                                           (int)(T * A.d_v * 4 - (int64_t)tile * kCols * 4), kBufWord3);
+    ralpha = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(A.alpha + (int64_t)mem * T), 0, (int)(T * 4), kBufWord3);
+    rbeta = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(A.beta + (int64_t)mem * T), 0, (int)(T * 4), kBufWord3);
+    off_list = lane < C ? (uint32_t)lane * 8u : kOffNone;
+    off_src = lane < C ? (uint32_t)lane * 2u : kOffNone;
+    off_v = lane < kCols ? (uint32_t)lane * 4u : kOffNone;
+    step_v = (uint32_t)A.d_v * 4u;
+  }
+
+  // Issue the loads of chunk q; no wait.  Steps past the end load nothing
+  // (their offsets are out of range).
   __device__ __forceinline__ void load(ChunkRegs& r, const PScanArgs& A, int64_t q) const {
     const int64_t t0 = q * kChunk;
     const int lane = lane_id();
-    r.h = (lane < kChunk && t0 + lane < A.T) ? A.hdr[ubase + t0 + lane] : 0u;
+    const uint32_t th = (lane < kChunk && t0 + lane < A.T) ? (uint32_t)(t0 + lane) * 4u : kOffNone;
+    r.h = __builtin_amdgcn_raw_buffer_load_b32(rhdr, th, 0, 0);
+    r.al = __builtin_amdgcn_raw_buffer_load_b32(ralpha, th, 0, 0);
+    r.be = __builtin_amdgcn_raw_buffer_load_b32(rbeta, th, 0, 0);
 #pragma unroll
     for (int s = 0; s < kChunk; ++s) {
       const bool live = t0 + s < A.T;
-      const int64_t e = (ubase + t0 + s) * 64 + lane;
-      const int64_t st = (int64_t)mem * A.T + t0 + s;
-      r.we[s] = (live && lane < C) ? A.went[e] : make_uint2(kEmpty, 0u);
-      r.re[s] = (live && lane < C) ? A.rent[e] : make_uint2(kEmpty, 0u);
-      r.sw[s] = (live && lane < C) ? (uint32_t)A.srcw[e] : 0u;
-      r.sr[s] = (live && lane < C) ? (uint32_t)A.srcr[e] : 0u;
-      r.vv[s] = (live && lane < kCols) ? A.v[st * A.d_v + (int64_t)tile * kCols + lane] : 0.0f;
-      r.ab[s] = (live && lane < 2) ? (lane == 0 ? A.alpha : A.beta)[st] : 0.0f;
+      const uint32_t t = (uint32_t)(t0 + s);
+      const uint32_t ol = live ? off_list + t * 512u : kOffNone;  // kOffNone + x stays out of range
+      const uint32_t os = live ? off_src + t * 128u : kOffNone;
+      r.we[s] = __builtin_amdgcn_raw_buffer_load_b64(rwent, ol, 0, 0);
+      r.re[s] = __builtin_amdgcn_raw_buffer_load_b64(rrent, ol, 0, 0);
+      r.sw[s] = __builtin_amdgcn_raw_buffer_load_b16(rsrcw, os, 0, 0);
+      r.sr[s] = __builtin_amdgcn_raw_buffer_load_b16(rsrcr, os, 0, 0);
+      r.vv[s] = __builtin_amdgcn_raw_buffer_load_b32(rv, live ? off_v + t * step_v : kOffNone, 0, 0);
     }
   }
 
@@ -344,23 +369,28 @@ struct Loader {
         const uint32_t hs = (uint32_t)__builtin_amdgcn_readlane((int)r.h, s);
         const int nw = (int)(hs & 0xFFu), nr = (int)((hs >> 8) & 0xFFu);
         const bool fwd = ((hs >> 16) & 1u) != 0u;
-        const bool wok = lane < nw && r.we[s].x < Nu;  // rows at or past N: skipped
-        const bool rok = lane < nr && r.re[s].x < Nu;
-        const uint32_t sw = (fwd && lane < nw) ? r.sw[s] : 0u;
-        const uint32_t sr = (fwd && lane < nr) ? r.sr[s] : 0u;
+        const uint32_t wrow = r.we[s].x, rrow = r.re[s].x;
+        const bool wok = lane < nw && wrow < Nu;  // rows at or past N: skipped
+        const bool rok = lane < nr && rrow < Nu;
         if (lane < C) {
-          p.rec[lr][k] = wok ? r.we[s].x * row_bytes : kOffNone;
-          p.rec[lr][NIC + k] = rok ? r.re[s].x * row_bytes : kOffNone;
+          p.rec[lr][k] = wok ? wrow * row_bytes : kOffNone;
+          p.rec[lr][NIC + k] = rok ? rrow * row_bytes : kOffNone;
           p.rec[lr][2 * NIC + k] = r.we[s].y;
           p.rec[lr][3 * NIC + k] = rok ? r.re[s].y : 0u;
-          p.src[lr][k] = sw | (sr << 16);
         }
-        if (lane < kCols) p.v[lane] = r.vv[s];
-        const bool far = __ballot(lane < C && (beyond_ring(sw, 1) || beyond_ring(sr, 0))) != 0ull;
-        const float bta = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(r.ab[s]), 1));
+        if (lane < kCols) p.v[lane] = __uint_as_float(r.vv[s]);
+        bool far = false;
+        if (fwd) {  // rare: the sources of a flagged step
+          const uint32_t sw = lane < nw ? (r.sw[s] & 0xFFFFu) : 0u;
+          const uint32_t sr = lane < nr ? (r.sr[s] & 0xFFFFu) : 0u;
+          if (lane < C) p.src[lr][k] = sw | (sr << 16);
+          far = __ballot(lane < C && (beyond_ring(sw, 1) || beyond_ring(sr, 0))) != 0ull;
+        }
+        const uint32_t al = (uint32_t)__builtin_amdgcn_readlane((int)r.al, s);
+        const uint32_t be = (uint32_t)__builtin_amdgcn_readlane((int)r.be, s);
         if (lane == 0) {
-          p.alpha = r.ab[s];
-          p.beta = bta;
+          p.alpha = __uint_as_float(al);
+          p.beta = __uint_as_float(be);
           p.flags = (fwd ? kFlagFwd : 0u) | ((nw > C || nr > C || far) ? kFlagSync : 0u) |
                     ((uint32_t)nw << 8) | ((uint32_t)nr << 16);
         }
@@ -692,7 +722,8 @@ __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ 
     // loader: chunks 0 and 1 before the consumer starts, then chunk c + 2
     // while the consumer runs chunk c (one barrier per chunk, as the
     // consumer); the loads of chunk c + 3 are in flight meanwhile
-    Loader<D, NIC> ld{mem, tile, ubase};
+    Loader<D, NIC> ld;
+    ld.init(A, mem, tile, ubase);
     ChunkRegs ra, rb;
     ld.load(ra, A, 0);
     ld.load(rb, A, 1);

@@ -409,10 +409,15 @@ struct PConsumer {
   static_assert(NIC % 2 == 0, "offsets of a step are NIC / 2 16-byte reads");
   u32x4v wv[D + 1][NIC];
   u32x4v rv[D + 1][NIC];
-  uint32_t gw[NIC], gr[NIC];  // offsets of the next gathers (read one step ahead)
+  // Plan words read one step ahead, kept exactly as loaded: whatever is
+  // computed from them happens where they are used, a step later, so no
+  // step waits for the LDS read it just issued.
+  uint32_t gw[NIC], gr[NIC];  // row offsets of the next gathers
+  bool glive;                 // those gathers' step is inside the sequence
   uint32_t cw[NIC];           // the next step's write offsets ...
-  float ck[NIC], cr[NIC];     // ... weights ...
-  float cv[4], ca, cb;        // ... v columns and gates ...
+  uint32_t ck[NIC], cr[NIC];  // ... weights (bit patterns) ...
+  float4 cv;                  // ... v columns ...
+  float ca, cb;               // ... gates ...
   uint32_t cf;                // ... and flags
   __amdgpu_buffer_rsrc_t mres;  // this memory's tile column, range = the memory's table
   uint32_t lane_off;            // lc * 16
@@ -428,44 +433,35 @@ struct PConsumer {
 
   __device__ __forceinline__ void read_gather_offsets(const PStep<NIC>& p, bool live) {
     const uint4* r = reinterpret_cast<const uint4*>(p.rec[lr]);
-    uint32_t o[2 * NIC];
 #pragma unroll
     for (int i = 0; i < NIC / 2; ++i) {
       const uint4 x = r[i];
-      o[4 * i] = x.x;
-      o[4 * i + 1] = x.y;
-      o[4 * i + 2] = x.z;
-      o[4 * i + 3] = x.w;
-    }
+      const uint32_t o[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int k = 0; k < NIC; ++k) {
-      gw[k] = live ? o[k] + lane_off : kOffNone;  // kOffNone + lane_off is still out of range
-      gr[k] = live ? o[NIC + k] + lane_off : kOffNone;
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * i + e;
+        if (j < NIC) gw[j] = o[e];
+        else gr[j - NIC] = o[e];
+      }
     }
+    glive = live;
   }
 
   __device__ __forceinline__ void read_step_fields(const PStep<NIC>& p) {
     const uint4* r = reinterpret_cast<const uint4*>(p.rec[lr]);
-    uint32_t o[4 * NIC];
 #pragma unroll
     for (int i = 0; i < NIC; ++i) {
       const uint4 x = r[i];
-      o[4 * i] = x.x;
-      o[4 * i + 1] = x.y;
-      o[4 * i + 2] = x.z;
-      o[4 * i + 3] = x.w;
-    }
+      const uint32_t o[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int k = 0; k < NIC; ++k) {
-      cw[k] = o[k] + lane_off;
-      ck[k] = __uint_as_float(o[2 * NIC + k]);
-      cr[k] = __uint_as_float(o[3 * NIC + k]);
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * i + e;
+        if (j < NIC) cw[j] = o[e];
+        else if (j >= 2 * NIC && j < 3 * NIC) ck[j - 2 * NIC] = o[e];
+        else if (j >= 3 * NIC) cr[j - 3 * NIC] = o[e];
+      }
     }
-    const float4 v4 = *reinterpret_cast<const float4*>(&p.v[lc * 4]);
-    cv[0] = v4.x;
-    cv[1] = v4.y;
-    cv[2] = v4.z;
-    cv[3] = v4.w;
+    cv = *reinterpret_cast<const float4*>(&p.v[lc * 4]);
     ca = p.alpha;
     cb = p.beta;
     cf = p.flags;
@@ -473,12 +469,18 @@ struct PConsumer {
 
   template <int SLOT>
   __device__ __forceinline__ void issue() {
+    uint32_t ow[NIC], orr[NIC];
+#pragma unroll
+    for (int k = 0; k < NIC; ++k) {  // kOffNone + lane_off is still out of range
+      ow[k] = glive ? gw[k] + lane_off : kOffNone;
+      orr[k] = glive ? gr[k] + lane_off : kOffNone;
+    }
 #pragma unroll
     for (int k = 0; k < NIC; ++k)
-      wv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, gw[k], 0, 0);
+      wv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ow[k], 0, 0);
 #pragma unroll
     for (int k = 0; k < NIC; ++k)
-      rv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, gr[k], 0, 0);
+      rv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, orr[k], 0, 0);
   }
 
   // A whole step without the prefetch (rare): wait for every earlier
@@ -557,7 +559,9 @@ struct PConsumer {
   }
 
   // Step s of the chunk starting at t0 (P: its plan, P1: the next chunk's).
-  template <int s>
+  // FULL: this chunk and the next are wholly inside the sequence, so no
+  // step or prefetch needs a bounds check.
+  template <int s, bool FULL>
   __device__ __forceinline__ void step(PShared<D, NIC>& sh, const PStep<NIC>* P,
                                        const PStep<NIC>* P1, int64_t t0, int64_t T) {
     constexpr int SLOT = s % (D + 1);
@@ -567,21 +571,20 @@ struct PConsumer {
     // fields (read during the previous step) and the next step's
     {
       constexpr int g = s + D + 1;
-      read_gather_offsets(g < kChunk ? P[g] : P1[g - kChunk], t0 + g < T);
+      read_gather_offsets(g < kChunk ? P[g] : P1[g - kChunk], FULL || t0 + g < T);
     }
     uint32_t wo[NIC];
-    float wkk[NIC], rwk[NIC], vv[4];
+    float wkk[NIC], rwk[NIC];
 #pragma unroll
     for (int k = 0; k < NIC; ++k) {
-      wo[k] = cw[k];
-      wkk[k] = ck[k];
-      rwk[k] = cr[k];
+      wo[k] = cw[k] + lane_off;  // kOffNone + lane_off is still out of range
+      wkk[k] = __uint_as_float(ck[k]);
+      rwk[k] = __uint_as_float(cr[k]);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = cv[e];
+    const float vv[4] = {cv.x, cv.y, cv.z, cv.w};
     const float a = ca, b = cb;
-    const uint32_t flags = cf;
-    if (u + 1 < T) read_step_fields(s + 1 < kChunk ? P[s + 1] : P1[0]);
+    const uint32_t flags = __builtin_amdgcn_readfirstlane(cf);
+    if (FULL || u + 1 < T) read_step_fields(s + 1 < kChunk ? P[s + 1] : P1[0]);
     const PStep<NIC>& p = P[s];
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (flags & kFlagSync) {
@@ -651,12 +654,12 @@ struct PConsumer {
 
   // A full chunk of kChunk steps, then its outputs and the barrier the
   // loader meets (one per chunk).
-  template <int s>
+  template <int s, bool FULL>
   __device__ __forceinline__ void steps(PShared<D, NIC>& sh, const PStep<NIC>* P,
                                         const PStep<NIC>* P1, int64_t t0, int64_t T) {
     if constexpr (s < kChunk) {
-      step<s>(sh, P, P1, t0, T);
-      steps<s + 1>(sh, P, P1, t0, T);
+      step<s, FULL>(sh, P, P1, t0, T);
+      steps<s + 1, FULL>(sh, P, P1, t0, T);
     }
   }
 
@@ -666,7 +669,7 @@ struct PConsumer {
                                              const PStep<NIC>* P1, int64_t t0, int64_t T) {
     if constexpr (s < kChunk) {
       if (t0 + s < T) {
-        step<s>(sh, P, P1, t0, T);
+        step<s, false>(sh, P, P1, t0, T);
         tail_steps<s + 1>(sh, P, P1, t0, T);
       }
     }
@@ -762,16 +765,28 @@ __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ 
       (int)ranges::table_range(A.N, row_bytes, tile, kTileBytes), kBufWord3);
   __syncthreads();
   cs.template prologue<0>(sh, T);
+  // chunks whose successor is wholly inside the sequence, then the last
+  // whole chunk (its successor may be partial), then the partial one
   const int64_t full = T / kChunk;
-  for (int64_t c = 0; c < full; ++c) {
-    const int64_t t0 = c * kChunk;
-    cs.template steps<0>(sh, sh.plan[c % kNBuf], sh.plan[(c + 1) % kNBuf], t0, T);
-    cs.end_chunk(sh, out_mem, d_v, T, tile, t0);
+  int buf = 0;  // plan buffer of chunk c (c % kNBuf)
+  int64_t c = 0;
+  for (; c + 1 < full; ++c) {
+    const int nxt = buf == kNBuf - 1 ? 0 : buf + 1;
+    cs.template steps<0, true>(sh, sh.plan[buf], sh.plan[nxt], c * kChunk, T);
+    cs.end_chunk(sh, out_mem, d_v, T, tile, c * kChunk);
+    buf = nxt;
   }
-  if (full < nchunks) {
-    const int64_t t0 = full * kChunk;
-    cs.template tail_steps<0>(sh, sh.plan[full % kNBuf], sh.plan[(full + 1) % kNBuf], t0, T);
-    cs.end_chunk(sh, out_mem, d_v, T, tile, t0);
+  if (c < full) {
+    const int nxt = buf == kNBuf - 1 ? 0 : buf + 1;
+    cs.template steps<0, false>(sh, sh.plan[buf], sh.plan[nxt], c * kChunk, T);
+    cs.end_chunk(sh, out_mem, d_v, T, tile, c * kChunk);
+    buf = nxt;
+    ++c;
+  }
+  if (c < nchunks) {
+    const int nxt = buf == kNBuf - 1 ? 0 : buf + 1;
+    cs.template tail_steps<0>(sh, sh.plan[buf], sh.plan[nxt], c * kChunk, T);
+    cs.end_chunk(sh, out_mem, d_v, T, tile, c * kChunk);
   }
 }
 

@@ -102,8 +102,9 @@ struct PlanShared {
   uint8_t rpos[kPlanSteps][64];
   uint32_t cnt[kPlanSteps][8];  // per owned step and shard: write count | read count << 8
   uint32_t hrow[kHashCap];      // hash table: row (kEmpty: free) ...
-  uint32_t hinf[kHashCap];      // ... and window step << 8 | list position
+  uint16_t hinf[kHashCap];      // ... and window step << 8 | list position
 };
+static_assert(kWin <= 255, "window steps fit the high byte of a 16-bit hinf entry");
 
 // Source code of the newest write of `row` in window steps [lo, hi], or 0.
 __device__ __forceinline__ uint32_t newest_writer(const PlanShared& sh, uint32_t row, int lo,
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs A) {
       const uint32_t inf = ((uint32_t)ls << 8) | (uint32_t)pos;
       for (uint32_t p = hash_slot((uint32_t)row);; p = (p + 1) & (kHashCap - 1)) {
         if (atomicCAS(&sh.hrow[p], kEmpty, (uint32_t)row) == kEmpty) {
-          sh.hinf[p] = inf;
+          sh.hinf[p] = (uint16_t)inf;
           break;
         }
       }
@@ -714,6 +715,11 @@ __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ 
   const int shard = (rest / A.ntiles) % A.S;
   const int mem = (rest / A.ntiles / A.S) * 8 + x;
   if (mem >= A.n_mem) return;  // whole workgroup leaves together
+  // Each workgroup is one long chain of dependent steps, so its waves take
+  // the highest issue priority: kernels running beside it (the next
+  // chunk's selections) then fill the cycles the chain leaves idle instead
+  // of stretching it.
+  __builtin_amdgcn_s_setprio(3);
 
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -807,6 +813,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   }
 }
 
+// A device attribute of the current device, read once per device.
+int device_attr(hipDeviceAttribute_t attr, int fallback, int (&cached)[64]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  return device_attr(hipDeviceAttributeMultiprocessorCount, 256, cached);
+}
+
+int lds_per_cu() {
+  static int cached[64] = {0};
+  return device_attr(hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, 160 * 1024, cached);
+}
+
 template <int D, int NIC>
 hipError_t launch_planned(float* M, const PScanArgs& A, hipStream_t stream) {
   // the offsets of step u + D + 1 are read during step u: at most one
@@ -818,26 +846,24 @@ hipError_t launch_planned(float* M, const PScanArgs& A, hipStream_t stream) {
   static_assert(3 * NIC * D <= 63, "outstanding vector memory operations");
   const int groups = (A.n_mem + 7) / 8;
   const int64_t blocks = (int64_t)groups * A.S * A.ntiles * 8;
-  hipLaunchKernelGGL((planned_kernel<D, NIC>), dim3((unsigned)blocks), dim3(2 * kWave), 0, stream,
+  // Each workgroup is one chain of dependent steps over the whole call, so
+  // the call lasts as long as its slowest chain. When the grid fits two
+  // workgroups per CU, each asks for just over a third of the CU's LDS: no
+  // CU can then take a third of them, whatever else is dispatched at the
+  // same time (kernels beside, such as the next chunk's selections and
+  // plan, use the LDS left over).
+  size_t dyn = 0;
+  if (blocks <= 2 * (int64_t)cu_count()) {
+    const size_t third = ((size_t)lds_per_cu() / 3 / 256 + 1) * 256;
+    if (third > sizeof(PShared<D, NIC>) && third <= 64 * 1024) dyn = third - sizeof(PShared<D, NIC>);
+  }
+  hipLaunchKernelGGL((planned_kernel<D, NIC>), dim3((unsigned)blocks), dim3(2 * kWave), dyn, stream,
                      M, A);
   return hipGetLastError();
 }
 
 // Compute units of the current device (cached per device; 256 if the
 // query fails).
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cu = 0;
-    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
-      cu = 256;
-    cached[dev] = cu;
-  }
-  return cached[dev];
-}
-
 }  // namespace
 
 int planned_shards(int n_mem, int d_v) {

@@ -782,7 +782,7 @@ def run_long(cfg, args, torch, S, sdm):
     workload = f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} T{T} W={W} R={R} fp32 state"
     if planned:
         workload += ", planned scan"
-        kernel = ("planned_kernel<7,2>, eight row shards of 32-column tiles (duration includes "
+        kernel = ("planned_kernel<7,2,16>, eight row shards of 32-column tiles (duration includes "
                   "the shards' combine kernel of the same call)")
         traffic = measured_traffic(slot_bytes // nch, LONG_PLANNED_TRAFFIC_FILE, PLANNED_SOURCES)
     else:

@@ -26,8 +26,8 @@
 //            and list position.  Flagged (memory, shard, step) entries get
 //            their source lists written; the rest do not.
 //   scan     (planned_kernel) one workgroup per (memory, 32-column tile,
-//            shard), two wavefronts.  A loader wavefront copies each 8-step
-//            chunk of the shard's lists into an LDS plan (byte offsets and
+//            shard), two wavefronts.  A loader wavefront copies each chunk
+//            (8 or 16 steps) of the shard's lists into an LDS plan (byte offsets and
 //            weights laid out per row group, sources, v columns, gates) two
 //            chunks ahead, with the loads of the next chunk in flight.  The
 //            consumer wavefront runs a chunk per loop iteration with every
@@ -59,7 +59,6 @@ constexpr int kTileBytes = kCols * 4;
 constexpr int kLPR = kTileBytes / 16;  // lanes per row (8)
 constexpr int kRPI = kWave / kLPR;     // rows per wave instruction (8)
 constexpr int kNI = 64 / kRPI;         // instructions for 64 rows (8)
-constexpr int kChunk = 8;              // steps per LDS plan chunk
 constexpr int kNBuf = 3;               // plan chunks resident
 constexpr int kBufWord3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr uint32_t kOffNone = ranges::kOffNone;
@@ -254,7 +253,7 @@ struct PStep {
   uint32_t pad;
 };
 
-template <int D, int NIC>
+template <int D, int NIC, int kChunk>
 struct PShared {
   static constexpr int C = NIC * kRPI;
   PStep<NIC> plan[kNBuf][kChunk];
@@ -285,6 +284,7 @@ enum : uint32_t { kFlagSync = 4u };
 // holds step s's header; every lane j < C holds list position j of each
 // step (loaded whatever the list length, so no load waits for a header;
 // positions past the length are masked when the plan is written).
+template <int kChunk>
 struct ChunkRegs {
   uint32_t h, al, be;  // lane s < kChunk: step s's header, alpha, beta
   u32x2 we[kChunk], re[kChunk];
@@ -296,7 +296,7 @@ struct ChunkRegs {
 // written into the LDS plan (two register sets).  Every load is a raw
 // buffer load through a descriptor over this workgroup's slice of an array,
 // so a masked lane is an out-of-range offset rather than a branch.
-template <int D, int NIC>
+template <int D, int NIC, int kChunk>
 struct Loader {
   static constexpr int C = NIC * kRPI;
   __amdgpu_buffer_rsrc_t rhdr, rwent, rrent, rsrcw, rsrcr, rv, ralpha, rbeta;
@@ -323,7 +323,7 @@ struct Loader {
 
   // Issue the loads of chunk q; no wait.  Steps past the end load nothing
   // (their offsets are out of range).
-  __device__ __forceinline__ void load(ChunkRegs& r, const PScanArgs& A, int64_t q) const {
+  __device__ __forceinline__ void load(ChunkRegs<kChunk>& r, const PScanArgs& A, int64_t q) const {
     const int64_t t0 = q * kChunk;
     const int lane = lane_id();
     const uint32_t th = (lane < kChunk && t0 + lane < A.T) ? (uint32_t)(t0 + lane) * 4u : kOffNone;
@@ -354,7 +354,7 @@ struct Loader {
   // Write chunk q's plan from its loaded data.  Entries past a list's length
   // and the sources of unflagged steps (never written by the plan pass) are
   // masked here.
-  __device__ __forceinline__ void fill(PShared<D, NIC>& sh, const PScanArgs& A, const ChunkRegs& r,
+  __device__ __forceinline__ void fill(PShared<D, NIC, kChunk>& sh, const PScanArgs& A, const ChunkRegs<kChunk>& r,
                                        int64_t q) const {
     const int64_t t0 = q * kChunk;
     if (t0 >= A.T) return;
@@ -403,7 +403,7 @@ struct Loader {
 // Consumer wavefront.  The loop body is one plan chunk of kChunk steps with
 // the step index known at compile time (D + 1 divides kChunk, so a step's
 // ring slot is too); the gathers of step s + D are issued at step s.
-template <int D, int NIC>
+template <int D, int NIC, int kChunk>
 struct PConsumer {
   static constexpr int C = NIC * kRPI;
   static_assert(kChunk % (D + 1) == 0, "ring slots repeat within a chunk");
@@ -490,7 +490,7 @@ struct PConsumer {
   // rows, so every value is current.  Rows at positions < C also go into the
   // ring for the later steps whose gathers are already in flight.
   template <int SLOT>
-  __device__ __forceinline__ void sync_step(PShared<D, NIC>& sh, int64_t u, uint32_t nw,
+  __device__ __forceinline__ void sync_step(PShared<D, NIC, kChunk>& sh, int64_t u, uint32_t nw,
                                             uint32_t nr, float a, float b, const float (&vv)[4],
                                             float (&acc)[4]) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -538,32 +538,35 @@ struct PConsumer {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
-  // Sum a chunk's per-lane partials: lane g handles float4 group g of the
-  // chunk's kChunk x kCols outputs.
-  __device__ __forceinline__ void reduce_chunk(PShared<D, NIC>& sh, float* out_mem, int d_v,
+  // Sum a chunk's per-lane partials: lane g handles float4 groups g,
+  // g + 64, ... of the chunk's kChunk x kCols outputs.
+  __device__ __forceinline__ void reduce_chunk(PShared<D, NIC, kChunk>& sh, float* out_mem, int d_v,
                                                int64_t T, int tile, int64_t t0) {
     constexpr int G4 = kCols / 4;
-    static_assert(kChunk * G4 == kWave, "one float4 group per lane");
-    const int g = lane_id();
-    const int s = g / G4, c4 = g % G4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    static_assert((kChunk * G4) % kWave == 0, "whole float4 groups per lane");
 #pragma unroll
-    for (int r = 0; r < kRPI; ++r) {
-      const float4 x = *reinterpret_cast<const float4*>(&sh.part[s][r][c4 * 4]);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+    for (int q = 0; q < kChunk * G4 / kWave; ++q) {
+      const int g = lane_id() + q * kWave;
+      const int s = g / G4, c4 = g % G4;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int r = 0; r < kRPI; ++r) {
+        const float4 x = *reinterpret_cast<const float4*>(&sh.part[s][r][c4 * 4]);
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
+      if (t0 + s < T)
+        *reinterpret_cast<float4*>(out_mem + (t0 + s) * d_v + tile * kCols + c4 * 4) = acc;
     }
-    if (t0 + s < T)
-      *reinterpret_cast<float4*>(out_mem + (t0 + s) * d_v + tile * kCols + c4 * 4) = acc;
   }
 
   // Step s of the chunk starting at t0 (P: its plan, P1: the next chunk's).
   // FULL: this chunk and the next are wholly inside the sequence, so no
   // step or prefetch needs a bounds check.
   template <int s, bool FULL>
-  __device__ __forceinline__ void step(PShared<D, NIC>& sh, const PStep<NIC>* P,
+  __device__ __forceinline__ void step(PShared<D, NIC, kChunk>& sh, const PStep<NIC>* P,
                                        const PStep<NIC>* P1, int64_t t0, int64_t T) {
     constexpr int SLOT = s % (D + 1);
     const int64_t u = t0 + s;
@@ -656,7 +659,7 @@ struct PConsumer {
   // A full chunk of kChunk steps, then its outputs and the barrier the
   // loader meets (one per chunk).
   template <int s, bool FULL>
-  __device__ __forceinline__ void steps(PShared<D, NIC>& sh, const PStep<NIC>* P,
+  __device__ __forceinline__ void steps(PShared<D, NIC, kChunk>& sh, const PStep<NIC>* P,
                                         const PStep<NIC>* P1, int64_t t0, int64_t T) {
     if constexpr (s < kChunk) {
       step<s, FULL>(sh, P, P1, t0, T);
@@ -666,7 +669,7 @@ struct PConsumer {
 
   // The last, partial chunk: the same steps, each only while t0 + s < T.
   template <int s>
-  __device__ __forceinline__ void tail_steps(PShared<D, NIC>& sh, const PStep<NIC>* P,
+  __device__ __forceinline__ void tail_steps(PShared<D, NIC, kChunk>& sh, const PStep<NIC>* P,
                                              const PStep<NIC>* P1, int64_t t0, int64_t T) {
     if constexpr (s < kChunk) {
       if (t0 + s < T) {
@@ -676,7 +679,7 @@ struct PConsumer {
     }
   }
 
-  __device__ __forceinline__ void end_chunk(PShared<D, NIC>& sh, float* out_mem, int d_v,
+  __device__ __forceinline__ void end_chunk(PShared<D, NIC, kChunk>& sh, float* out_mem, int d_v,
                                             int64_t T, int tile, int64_t t0) {
     wave_sync();
     reduce_chunk(sh, out_mem, d_v, T, tile, t0);
@@ -687,7 +690,7 @@ struct PConsumer {
   // range (dropped), so the memory operations enter the loop in the pattern
   // a step leaves them in (its gathers, then its stores).
   template <int S>
-  __device__ __forceinline__ void prologue(PShared<D, NIC>& sh, int64_t T) {
+  __device__ __forceinline__ void prologue(PShared<D, NIC, kChunk>& sh, int64_t T) {
     if constexpr (S == 0) read_step_fields(sh.plan[0][0]);
     if constexpr (S < D) {
       read_gather_offsets(sh.plan[0][S], S < T);
@@ -703,9 +706,9 @@ struct PConsumer {
   }
 };
 
-template <int D, int NIC>
+template <int D, int NIC, int kChunk>
 __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ M, PScanArgs A) {
-  __shared__ PShared<D, NIC> sh;
+  __shared__ PShared<D, NIC, kChunk> sh;
   // XCD-aware numbering as in the scan kernel: every tile and shard of a
   // memory on one XCD, so the rows its tiles share come from one L2.
   const int bid = blockIdx.x;
@@ -731,9 +734,9 @@ __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ 
     // loader: chunks 0 and 1 before the consumer starts, then chunk c + 2
     // while the consumer runs chunk c (one barrier per chunk, as the
     // consumer); the loads of chunk c + 3 are in flight meanwhile
-    Loader<D, NIC> ld;
+    Loader<D, NIC, kChunk> ld;
     ld.init(A, mem, tile, ubase);
-    ChunkRegs ra, rb;
+    ChunkRegs<kChunk> ra, rb;
     ld.load(ra, A, 0);
     ld.load(rb, A, 1);
     ld.fill(sh, A, ra, 0);
@@ -756,7 +759,7 @@ __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ 
   const int d_v = A.d_v;
   float* const out_mem =
       A.out + ((A.S == 1 ? 0 : (int64_t)shard * A.n_mem) + mem) * T * d_v;
-  PConsumer<D, NIC> cs;
+  PConsumer<D, NIC, kChunk> cs;
   cs.lr = lane / kLPR;
   cs.lc = lane % kLPR;
   cs.lane_off = (uint32_t)(cs.lc * 16);
@@ -835,7 +838,7 @@ int lds_per_cu() {
   return device_attr(hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, 160 * 1024, cached);
 }
 
-template <int D, int NIC>
+template <int D, int NIC, int kChunk>
 hipError_t launch_planned(float* M, const PScanArgs& A, hipStream_t stream) {
   // the offsets of step u + D + 1 are read during step u: at most one
   // chunk ahead of the one the consumer is in (the loader fills two ahead)
@@ -855,9 +858,9 @@ hipError_t launch_planned(float* M, const PScanArgs& A, hipStream_t stream) {
   size_t dyn = 0;
   if (blocks <= 2 * (int64_t)cu_count()) {
     const size_t third = ((size_t)lds_per_cu() / 3 / 256 + 1) * 256;
-    if (third > sizeof(PShared<D, NIC>) && third <= 64 * 1024) dyn = third - sizeof(PShared<D, NIC>);
+    if (third > sizeof(PShared<D, NIC, kChunk>) && third <= 64 * 1024) dyn = third - sizeof(PShared<D, NIC, kChunk>);
   }
-  hipLaunchKernelGGL((planned_kernel<D, NIC>), dim3((unsigned)blocks), dim3(2 * kWave), dyn, stream,
+  hipLaunchKernelGGL((planned_kernel<D, NIC, kChunk>), dim3((unsigned)blocks), dim3(2 * kWave), dyn, stream,
                      M, A);
   return hipGetLastError();
 }
@@ -938,11 +941,13 @@ hipError_t launch_scan_planned(float* M, int B, int H, int64_t N, int d_v, int64
   // Fast-path capacity per list (NIC * 8 rows) and prefetch depth per shard
   // count: a shard's share of 64 random rows exceeds 48 (of 2 shards) about
   // once in 10^5 lists and 16 (of 8) about twice in 10^3; longer lists take
-  // the synchronous path.
+  // the synchronous path.  Chunk length: 16 steps where the LDS allows two
+  // workgroups per CU with it (one barrier and one output pass per 16
+  // steps), else 8.
   hipError_t e;
-  if (S == 1) e = launch_planned<1, 8>(M, A, stream);
-  else if (S == 2) e = launch_planned<3, 6>(M, A, stream);
-  else e = launch_planned<7, 2>(M, A, stream);  // 8 shards
+  if (S == 1) e = launch_planned<1, 8, 8>(M, A, stream);
+  else if (S == 2) e = launch_planned<3, 6, 8>(M, A, stream);
+  else e = launch_planned<7, 2, 16>(M, A, stream);  // 8 shards
   if (e != hipSuccess || S == 1) return e;
   const int64_t n4 = (int64_t)n_mem * T * d_v / 4;
   const int64_t cb = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;

@@ -673,10 +673,13 @@ def run_front(cfg, args, torch, S, sdm):
 def run_long(cfg, args, torch, S, sdm):
     """One step = the whole T = 2^20 stream in chunks of 16384 steps.  The
     inputs of each chunk are generated on the GPU outside the timed spans.
-    Timed: the selections of chunk 0, then per chunk c one span holding the
-    scan of chunk c on the main stream and, beside it on a second stream,
-    the selections of chunk c + 1 (the scan's workgroups leave compute units
-    free).  --no-overlap times selections and scan of each chunk in turn."""
+    Timed: the selections (and plan) of chunk 0, then per chunk c one span
+    holding the scan of chunk c on the main stream and, beside it on a
+    second stream, the selections and plan of chunk c + 1 (the planned
+    scan's workgroups, two per CU, leave LDS and wave slots free).  The scan
+    is the planned scan (sdm_scan_plan + sdm_scan_planned); --sdm-scan runs
+    sdm_scan on the selections instead.  --no-overlap times selections and
+    scan of each chunk in turn."""
     dev = torch.device("cuda:0")
     B, H, T, n, d_v, W, R, N = cfg.B, cfg.H, cfg.T, cfg.n, cfg.d_v, cfg.W, cfg.R, cfg.N
     C = 16384
@@ -701,7 +704,7 @@ def run_long(cfg, args, torch, S, sdm):
                     torch.empty((B, H, C, R), dtype=torch.int32, device=dev),
                     torch.empty((B, H, C, R), dtype=f32, device=dev)))
     out = torch.empty((B, H, C, d_v), dtype=f32, device=dev)
-    planned = args.planned
+    planned = not args.sdm_scan
     if planned:  # one plan workspace per chunk buffer
         wsb = sdm.scan_plan_workspace_size(B, H, d_v, C)
         plans = [torch.empty((wsb,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
@@ -816,9 +819,10 @@ def main():
     ap.add_argument("--train-dense", action="store_true",
                     help="with --train: zero the gradient table and sum all of it (dense mode)"
                          " instead of the sparse-mode bookkeeping")
-    ap.add_argument("--planned", action="store_true",
-                    help="with --config long: run the chunks with the planned scan "
-                         "(sdm_scan_plan beside the previous chunk, then sdm_scan_planned)")
+    ap.add_argument("--sdm-scan", action="store_true",
+                    help="with --config long: run the chunks with sdm_scan on the selections "
+                         "instead of the planned scan (sdm_scan_plan beside the previous "
+                         "chunk, then sdm_scan_planned)")
     ap.add_argument("--front", action="store_true",
                     help="time the front end instead: token projections (bf16 MFMA GEMM) + "
                          "the two selections")

@@ -158,7 +158,7 @@ int sdm_scan(void* M, int dtype, int B, int H, int64_t N, int d_v, int64_t T, in
  * one step leave those rows unspecified). */
 
 /* Bytes of workspace for these sizes (0 if they are not supported: B, H < 1,
- * T < 0, d_v not one of 32, 64, 128, 256).  The workspace holds the lists of
+ * B*H > 2^20, T < 0 or T > 2^20, d_v not one of 32, 64, 128, 256).  The workspace holds the lists of
  * every step and, with S > 1, one fp32 partial output per shard; it grows
  * with B*H*T, so long sequences are planned and run in consecutive calls of
  * a bounded T (16384 steps of 16 memories at d_v = 128: about 3.8 GB). */

@@ -466,8 +466,7 @@ int check_workspace(const void* ws, size_t bytes, int B, int H, int d_v, int64_t
 extern "C" {
 
 size_t sdm_scan_plan_workspace_size(int B, int H, int d_v, int64_t T) {
-  if (B < 1 || H < 1 || T < 0 || (int64_t)B * H > sdm::kMaxMemories || T > sdm::kMaxSteps ||
-      (int64_t)B * H * T > sdm::kMaxMemorySteps)
+  if (B < 1 || H < 1 || T < 0 || (int64_t)B * H > sdm::kMaxMemories || T > sdm::kPlanMaxSteps)
     return 0;
   if (d_v != 32 && d_v != 64 && d_v != 128 && d_v != 256) return 0;
   const int S = sdm::planned_shards(B * H, d_v);

@@ -327,6 +327,15 @@ int main() {
           SDM_ERR_UNSUPPORTED);  // 4 GiB table
     CHECK(sdm_scan_plan(1 << 20, 1, 1 << 10, 32, (int64_t)1 << 20, 8, 8, I, F, I, F, WS, need,
                         nullptr) == SDM_ERR_UNSUPPORTED);  // plan grid beyond 2^24 blocks
+    // at most 2^20 steps per call (the workgroups' list slices are addressed by 31-bit offsets)
+    CHECK(sdm_scan_plan_workspace_size(1, 16, 128, ((int64_t)1 << 20) + 1) == 0);
+    CHECK(sdm_scan_plan_workspace_size(1, 16, 128, (int64_t)1 << 20) > 0);
+    CHECK(sdm_scan_plan(1, 16, 1 << 20, 128, ((int64_t)1 << 20) + 1, 64, 64, I, F, I, F, WS, need,
+                        nullptr) == SDM_ERR_UNSUPPORTED);
+    CHECK(std::strstr(sdm_last_error(), "2^20 steps") != nullptr);
+    CHECK(sdm_scan_planned(V, 1, 16, 1 << 20, 128, ((int64_t)1 << 20) + 1, F, F, F, F, WS, need,
+                           nullptr) == SDM_ERR_UNSUPPORTED);
+    CHECK(std::strstr(sdm_last_error(), "2^20 steps") != nullptr);
     CHECK(sdm_scan_planned(nullptr, 1, 16, 1 << 20, 128, 100, F, F, F, F, WS, need, nullptr) ==
           SDM_ERR_INVALID);
     CHECK(sdm_scan_planned(V, 1, 16, 1 << 20, 128, 100, F, F, F, F + 1, WS, need, nullptr) ==

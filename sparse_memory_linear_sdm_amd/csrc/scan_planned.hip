@@ -557,8 +557,10 @@ struct PConsumer {
         acc.z += x.z;
         acc.w += x.w;
       }
-      if (t0 + s < T)
-        *reinterpret_cast<float4*>(out_mem + (t0 + s) * d_v + tile * kCols + c4 * 4) = acc;
+      if (t0 + s < T) {  // read once, by the combine or the caller: streamed past the caches
+        const f32x4 v = {acc.x, acc.y, acc.z, acc.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_mem + (t0 + s) * d_v + tile * kCols + c4 * 4));
+      }
     }
   }
 
@@ -800,19 +802,20 @@ __global__ __launch_bounds__(2 * kWave) void planned_kernel(float* __restrict__ 
 }
 
 // out = p_0 + p_1 + ... + p_{S-1}, element by element, added in that order.
-__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ part,
-                                                      float4* __restrict__ out, int S, int64_t n4) {
+// Each partial is read once and out written once: non-temporal accesses
+// (streamed past the caches), all S loads of a group in flight together.
+template <int S>
+__global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ part,
+                                                      f32x4* __restrict__ out, int64_t n4) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * 256) {
-    float4 o = part[i];
-    for (int s = 1; s < S; ++s) {
-      const float4 x = part[(int64_t)s * n4 + i];
-      o.x += x.x;
-      o.y += x.y;
-      o.z += x.z;
-      o.w += x.w;
-    }
-    out[i] = o;
+    f32x4 x[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) x[s] = __builtin_nontemporal_load(&part[(int64_t)s * n4 + i]);
+    f32x4 o = x[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) o += x[s];  // p_0 + p_1 + ... in that order
+    __builtin_nontemporal_store(o, &out[i]);
   }
 }
 
@@ -951,9 +954,12 @@ hipError_t launch_scan_planned(float* M, int B, int H, int64_t N, int d_v, int64
   if (e != hipSuccess || S == 1) return e;
   const int64_t n4 = (int64_t)n_mem * T * d_v / 4;
   const int64_t cb = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)cb), dim3(256), 0, stream,
-                     reinterpret_cast<const float4*>(base + L.part), reinterpret_cast<float4*>(out),
-                     S, n4);
+  const f32x4* const part = reinterpret_cast<const f32x4*>(base + L.part);
+  f32x4* const o4 = reinterpret_cast<f32x4*>(out);
+  if (S == 2)
+    hipLaunchKernelGGL(combine_kernel<2>, dim3((unsigned)cb), dim3(256), 0, stream, part, o4, n4);
+  else
+    hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)cb), dim3(256), 0, stream, part, o4, n4);
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ namespace sdm {
 namespace {
 
 constexpr int kCols = 32;             // fp32 columns per tile: one 128-byte line of a row
+constexpr int kCpolNT = 2;            // buffer instruction cache policy: nt (non-temporal)
 constexpr int kTileBytes = kCols * 4;
 constexpr int kLPR = kTileBytes / 16;  // lanes per row (8)
 constexpr int kRPI = kWave / kLPR;     // rows per wave instruction (8)
@@ -476,12 +477,16 @@ struct PConsumer {
       ow[k] = glive ? gw[k] + lane_off : kOffNone;
       orr[k] = glive ? gr[k] + lane_off : kOffNone;
     }
+    // Row pieces are used once per step and rarely again while a cache
+    // would hold them: the gathers and the stores of the rows are
+    // non-temporal (cache policy nt), which leaves L2 to the plan lists and
+    // v that the workgroups of a memory share.
 #pragma unroll
     for (int k = 0; k < NIC; ++k)
-      wv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ow[k], 0, 0);
+      wv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, ow[k], 0, kCpolNT);
 #pragma unroll
     for (int k = 0; k < NIC; ++k)
-      rv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, orr[k], 0, 0);
+      rv[SLOT][k] = __builtin_amdgcn_raw_buffer_load_b128(mres, orr[k], 0, kCpolNT);
   }
 
   // A whole step without the prefetch (rare): wait for every earlier
@@ -631,7 +636,7 @@ struct PConsumer {
 #pragma unroll
         for (int e = 0; e < 4; ++e) m[e] = write_elem<float>(a, g, vv[e], m[e]);
         wv[SLOT][k] = pack<float>(m);
-        __builtin_amdgcn_raw_buffer_store_b128(wv[SLOT][k], mres, wo[k], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(wv[SLOT][k], mres, wo[k], 0, kCpolNT);
         const u32x4v q = wv[SLOT][k];
         sh.upd[SLOT][(k * kRPI + lr) * kLPR + lc] = make_uint4(q.x, q.y, q.z, q.w);
       }

@@ -95,20 +95,25 @@ struct PlanArgs {
   uint16_t* srcr;
 };
 
+constexpr int kFiltBits = 15;  // bit filter over the window's write rows (4 KiB)
+
 struct PlanShared {
-  int32_t wrow[kWin][64];  // write rows of the window's steps (-1: skipped)
-  uint8_t wpos[kWin][64];  // their positions in their shard's list
-  int32_t rrow[kPlanSteps][64];
-  uint8_t rpos[kPlanSteps][64];
-  uint32_t cnt[kPlanSteps][8];  // per owned step and shard: write count | read count << 8
-  uint32_t hrow[kHashCap];      // hash table: row (kEmpty: free) ...
-  uint16_t hinf[kHashCap];      // ... and window step << 8 | list position
+  uint32_t hrow[kHashCap];  // hash table of the window's write rows: row (kEmpty: free) ...
+  uint16_t hinf[kHashCap];  // ... and window step << 8 | list position
+  uint32_t filt[(1 << kFiltBits) / 32];  // bit filt_bit(row) set for every row in the table
 };
 static_assert(kWin <= 255, "window steps fit the high byte of a 16-bit hinf entry");
 
+__device__ __forceinline__ uint32_t filt_bit(uint32_t row) {
+  return (row * 0x85EBCA77u) >> (32 - kFiltBits);
+}
+
 // Source code of the newest write of `row` in window steps [lo, hi], or 0.
+// Almost every row has none: the filter answers those with one read.
 __device__ __forceinline__ uint32_t newest_writer(const PlanShared& sh, uint32_t row, int lo,
                                                   int hi, int ls) {
+  const uint32_t f = filt_bit(row);
+  if (((sh.filt[f >> 5] >> (f & 31u)) & 1u) == 0u) return 0u;
   int best = -1;
   uint32_t pos = 0;
   for (uint32_t p = hash_slot(row);; p = (p + 1) & (kHashCap - 1)) {
@@ -126,6 +131,23 @@ __device__ __forceinline__ uint32_t newest_writer(const PlanShared& sh, uint32_t
   return best < 0 ? 0u : 1u + (uint32_t)(ls - best) * 64u + pos;
 }
 
+// Lane j's position among the valid lanes of its shard (lanes below j), and
+// for lane s < S the number of valid lanes in shard s: the lanes of a shard
+// are those that agree on each of the sbits shard bits.
+__device__ __forceinline__ void shard_positions(bool valid, uint32_t shard, int sbits, int lane,
+                                                int* pos, int* count) {
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t vm = __ballot(valid);
+  uint64_t mine = vm, lanes_s = vm;
+  for (int b = 0; b < sbits; ++b) {
+    const uint64_t m = __ballot(valid && ((shard >> b) & 1u));
+    mine &= ((shard >> b) & 1u) ? m : ~m;
+    lanes_s &= (((uint32_t)lane >> b) & 1u) ? m : ~m;
+  }
+  *pos = __popcll(mine & below);
+  *count = __popcll(lanes_s);
+}
+
 __global__ __launch_bounds__(256) void plan_kernel(PlanArgs A) {
   __shared__ PlanShared sh;
   const int64_t bid = blockIdx.x;
@@ -135,20 +157,24 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs A) {
   const int lb = (int)(t0 < kPlanLookback ? t0 : kPlanLookback);
   const int nwin = lb + own;
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-  const uint64_t below = (1ull << lane) - 1ull;
   const uint32_t Nu = (uint32_t)A.N;  // N < 2^31
   const int64_t T = A.T;
 
   for (int i = tid; i < kHashCap; i += 256) sh.hrow[i] = kEmpty;
+  for (int i = tid; i < (1 << kFiltBits) / 32; i += 256) sh.filt[i] = 0u;
   __syncthreads();
 
   // 1. every window step: rows, shards, list positions, hash inserts; for the
   //    workgroup's own steps also the list entries and the counts.  A wave
-  //    takes steps w, w + 4, ...; all of its loads are issued first, so it
+  //    takes window steps w, w + 4, ... (in both phases: the lookback is 0
+  //    or 8 steps, so a step's wave is the same in phase 2 and what phase 2
+  //    needs stays in registers); all of its loads are issued first, so it
   //    waits for memory once rather than once per step.
   constexpr int kPer = (kWin + 3) / 4;
   int32_t wrow_r[kPer], rrow_r[kPer];
   float wk_r[kPer], rw_r[kPer];
+  uint8_t wpos_r[kPer], rpos_r[kPer];
+  uint32_t cnt_r[kPer];  // lane s < S: write count | read count << 8 of shard s
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int ls = w + 4 * i;
@@ -167,14 +193,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs A) {
     const int32_t row = wrow_r[i];
     const bool ok = (uint32_t)row < Nu;
     const uint32_t sh_w = shard_of((uint32_t)row, A.sbits);
-    int pos = 0, cw = 0;
-    for (int s = 0; s < A.S; ++s) {
-      const uint64_t m = __ballot(ok && sh_w == (uint32_t)s);
-      if (sh_w == (uint32_t)s) pos = __popcll(m & below);
-      if (lane == s) cw = __popcll(m);
-    }
-    sh.wrow[ls][lane] = ok ? row : -1;
-    sh.wpos[ls][lane] = (uint8_t)pos;
+    int pos, cw;
+    shard_positions(ok, sh_w, A.sbits, lane, &pos, &cw);
+    wrow_r[i] = ok ? row : -1;
+    wpos_r[i] = (uint8_t)pos;
     if (ok) {
       const uint32_t inf = ((uint32_t)ls << 8) | (uint32_t)pos;
       for (uint32_t p = hash_slot((uint32_t)row);; p = (p + 1) & (kHashCap - 1)) {
@@ -183,9 +205,11 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs A) {
           break;
         }
       }
+      const uint32_t f = filt_bit((uint32_t)row);
+      atomicOr(&sh.filt[f >> 5], 1u << (f & 31u));
     }
+    cnt_r[i] = 0u;
     if (ls >= lb) {
-      const int lo = ls - lb;
       if (ok) {
         const int64_t e = (((int64_t)mem * A.S + sh_w) * T + ts) * 64 + pos;
         A.went[e] = make_uint2((uint32_t)row, __float_as_uint(wk_r[i]));
@@ -193,45 +217,46 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs A) {
       const int32_t rr = rrow_r[i];
       const bool rok = (uint32_t)rr < Nu;
       const uint32_t sh_r = shard_of((uint32_t)rr, A.sbits);
-      int rp = 0, cr = 0;
-      for (int s = 0; s < A.S; ++s) {
-        const uint64_t m = __ballot(rok && sh_r == (uint32_t)s);
-        if (sh_r == (uint32_t)s) rp = __popcll(m & below);
-        if (lane == s) cr = __popcll(m);
-      }
-      sh.rrow[lo][lane] = rok ? rr : -1;
-      sh.rpos[lo][lane] = (uint8_t)rp;
+      int rp, cr;
+      shard_positions(rok, sh_r, A.sbits, lane, &rp, &cr);
+      rrow_r[i] = rok ? rr : -1;
+      rpos_r[i] = (uint8_t)rp;
       if (rok) {
         const int64_t e = (((int64_t)mem * A.S + sh_r) * T + ts) * 64 + rp;
         A.rent[e] = make_uint2((uint32_t)rr, __float_as_uint(rw_r[i]));
       }
-      if (lane < A.S) sh.cnt[lo][lane] = (uint32_t)cw | ((uint32_t)cr << 8);
+      cnt_r[i] = (uint32_t)cw | ((uint32_t)cr << 8);
     }
   }
   __syncthreads();
 
   // 2. sources of every own step's rows, the flags and the headers
-  for (int lo = w; lo < own; lo += 4) {
-    const int ls = lo + lb;
-    const int64_t ts = t0 + lo;
-    const int32_t row = sh.wrow[ls][lane];
-    const int32_t rr = sh.rrow[lo][lane];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int ls = w + 4 * i;
+    if (ls >= nwin) break;
+    if (ls < lb) continue;
+    const int64_t ts = t0 - lb + ls;
+    const int32_t row = wrow_r[i];
+    const int32_t rr = rrow_r[i];
     const uint32_t sw = row >= 0 ? newest_writer(sh, (uint32_t)row, ls - kPlanLookback, ls - 1, ls) : 0u;
     const uint32_t sr = rr >= 0 ? newest_writer(sh, (uint32_t)rr, ls - kPlanLookback, ls, ls) : 0u;
-    const uint32_t sh_w = shard_of((uint32_t)row, A.sbits), sh_r = shard_of((uint32_t)rr, A.sbits);
     uint32_t fwd = 0;  // lane s < S: shard s has a forwarded row in this step
-    for (int s = 0; s < A.S; ++s) {
-      const bool mine_w = row >= 0 && sh_w == (uint32_t)s;
-      const bool mine_r = rr >= 0 && sh_r == (uint32_t)s;
-      const bool f = __ballot((mine_w && sw != 0u) || (mine_r && sr != 0u)) != 0ull;
-      if (lane == s) fwd = f ? 1u : 0u;
-      if (f) {
-        const int64_t base = (((int64_t)mem * A.S + s) * T + ts) * 64;
-        if (mine_w) A.srcw[base + sh.wpos[ls][lane]] = (uint16_t)sw;
-        if (mine_r) A.srcr[base + sh.rpos[lo][lane]] = (uint16_t)sr;
+    if (__ballot(sw != 0u || sr != 0u) != 0ull) {  // rare: some row has a writer in the window
+      const uint32_t sh_w = shard_of((uint32_t)row, A.sbits), sh_r = shard_of((uint32_t)rr, A.sbits);
+      for (int s = 0; s < A.S; ++s) {
+        const bool mine_w = row >= 0 && sh_w == (uint32_t)s;
+        const bool mine_r = rr >= 0 && sh_r == (uint32_t)s;
+        const bool f = __ballot((mine_w && sw != 0u) || (mine_r && sr != 0u)) != 0ull;
+        if (lane == s) fwd = f ? 1u : 0u;
+        if (f) {
+          const int64_t base = (((int64_t)mem * A.S + s) * T + ts) * 64;
+          if (mine_w) A.srcw[base + wpos_r[i]] = (uint16_t)sw;
+          if (mine_r) A.srcr[base + rpos_r[i]] = (uint16_t)sr;
+        }
       }
     }
-    if (lane < A.S) A.hdr[((int64_t)mem * A.S + lane) * T + ts] = sh.cnt[lo][lane] | (fwd << 16);
+    if (lane < A.S) A.hdr[((int64_t)mem * A.S + lane) * T + ts] = cnt_r[i] | (fwd << 16);
   }
 }
 

@@ -20,16 +20,19 @@
 //            and the list entries (row, weight).  Read-after-write hazards:
 //            every write row of the workgroup's steps and of the
 //            kPlanLookback steps before them goes into an LDS hash table
-//            (row -> step, position); a row of step u looks up the newest
-//            step in [u - kPlanLookback, u] (write rows: [.., u - 1]) that
-//            writes it, and the entry's source names that step's offset a
-//            and list position.  Flagged (memory, shard, step) entries get
-//            their source lists written; the rest do not.
+//            (row -> step, position) and sets a bit of an LDS filter; a
+//            row of step u looks up the newest step in [u - kPlanLookback,
+//            u] (write rows: [.., u - 1]) that writes it (the filter
+//            answers the rows no window step writes, nearly all of them,
+//            with one read), and the entry's source names that step's
+//            offset a and list position.  Flagged (memory, shard, step)
+//            entries get their source lists written; the rest do not.
 //   scan     (planned_kernel) one workgroup per (memory, 32-column tile,
-//            shard), two wavefronts.  A loader wavefront copies each chunk
-//            (8 or 16 steps) of the shard's lists into an LDS plan (byte offsets and
-//            weights laid out per row group, sources, v columns, gates) two
-//            chunks ahead, with the loads of the next chunk in flight.  The
+//            shard), two wavefronts, at most two workgroups per CU.  A
+//            loader wavefront copies each chunk (8 or 16 steps) of the
+//            shard's lists into an LDS plan (byte offsets and weights laid
+//            out per row group, sources, v columns, gates) two chunks
+//            ahead, with the loads of the next chunk in flight.  The
 //            consumer wavefront runs a chunk per loop iteration with every
 //            step index known at compile time, keeps the gathers of D steps
 //            in flight with NIC instructions per list (8 rows each), and
@@ -41,7 +44,7 @@
 //            takes a synchronous path (wait for every access, then gather,
 //            write, wait, read).  Row traffic is raw buffer instructions
 //            with out-of-range offsets for empty slots, as in the scan
-//            kernel.
+//            kernel, and non-temporal.
 //   combine  (combine_kernel) with S > 1 shards each shard's read sums go to
 //            its own partial output, and out = p_0 + p_1 + ... + p_{S-1},
 //            added in that fixed order, so results do not depend on timing.

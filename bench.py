@@ -45,6 +45,7 @@ PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_front_traffic.json")
 BF16_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_bf16_traffic.json")
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_mid_fp8_traffic.json")
 LONG_PLANNED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_long_planned_traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 _CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
 SCAN_SOURCES = [os.path.join(_CSRC, f)
                 for f in ("scan.hip", "scan_rows.h", "ranges.h", "device_common.h")]
@@ -52,6 +53,8 @@ BWD_SOURCES = [os.path.join(_CSRC, f) for f in ("backward.hip", "ranges.h", "dev
 PROJ_SOURCES = [os.path.join(_CSRC, f) for f in ("project.hip", "device_common.h", "internal.h")]
 PLANNED_SOURCES = [os.path.join(_CSRC, f) for f in
                    ("scan_planned.hip", "planned.h", "scan_rows.h", "ranges.h", "device_common.h")]
+DECODE_SOURCES = [os.path.join(_CSRC, f) for f in
+                  ("decode.hip", "select_wave.h", "device_common.h", "internal.h")]
 
 
 def _code_only(text: str) -> str:
@@ -523,6 +526,7 @@ def run_decode(cfg, args, torch, S, sdm):
     M = sdm.state_init(M0, B, sdt)
     del M0
     torch.cuda.empty_cache()
+    calibration_copy(args, torch, dev)
     out = torch.empty((B, H, d_v), dtype=f32, device=dev)
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -557,8 +561,11 @@ def run_decode(cfg, args, torch, S, sdm):
     gbps = call_bytes / (per_call_us * 1e-6) / 1e9
     workload = (f"{cfg.name}: B{B} H{H} n{n} (N={N}) d_v{d_v} {T} single-token calls "
                 f"W={W} R={R} {args.state} state")
+    # counted bytes per call, from the committed counter summary of the bf16 decode workload
+    traffic = (measured_traffic(call_bytes, DECODE_TRAFFIC_FILE, DECODE_SOURCES)
+               if es == 2 else None)
     roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": "decode_kernel<16,bf16>" if es == 2 else "decode_kernel<16,f32>",
                 "algorithmic_bytes_per_launch": call_bytes}
     extra = {"us_per_call": per_call_us, "wall_s": wall, "cpu_baseline": None}

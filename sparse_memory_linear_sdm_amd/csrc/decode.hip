@@ -82,19 +82,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   const float vreg = tid < d_v ? v[(int64_t)mem * d_v + tid] : 0.0f;
   const float a = alpha[mem], b = beta[mem];
 
-  // 1. selections: wave w runs stage 1 of half w into the LDS of its selection
+  // 1. selections: wave w runs stage 1 of half w into the LDS of its
+  // selection and sorts its survivors there (the four halves in parallel)
   uint32_t rc[pairtab::kSlots];
   if (w < 2) pair_slots(w == 0 ? W : R, rc);
   {
     const float* x = w == 0 ? s1 : w == 1 ? s2 : w == 2 ? q1 : q2;
     SelectLds& S = sl[w >> 1];
-    stage1_half<P, true>(x + (int64_t)mem * n, n, w < 2 ? W : R,
-                         (w & 1) ? S.sorted.b : S.sorted.a, S.trash, s_hist[w]);
+    uint64_t* const list = (w & 1) ? S.sorted.b : S.sorted.a;
+    const int K = w < 2 ? W : R;
+    stage1_half<P, true>(x + (int64_t)mem * n, n, K, list, S.trash, s_hist[w]);
+    sort_survivors(list, K);
   }
   if (tid < d_v) s_v[tid] = vreg;
   __syncthreads();
-  if (w == 0) select_finish<true>(n, W, sl[0], rc, s_widx, nullptr, s_wk);
-  else if (w == 1) select_finish<true>(n, R, sl[1], rc, s_ridx, nullptr, s_rw);
+  if (w == 0) select_finish<true, true>(n, W, sl[0], rc, s_widx, nullptr, s_wk);
+  else if (w == 1) select_finish<true, true>(n, R, sl[1], rc, s_ridx, nullptr, s_rw);
   __syncthreads();
   if (widx_out && tid < W) widx_out[(int64_t)mem * W + tid] = s_widx[tid];
   if (ridx_out && tid < R) ridx_out[(int64_t)mem * R + tid] = s_ridx[tid];

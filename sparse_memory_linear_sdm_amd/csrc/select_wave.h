@@ -314,10 +314,21 @@ __device__ __forceinline__ void stage1_half(const float* __restrict__ x, int n, 
   stage1<P, RADIX>(u, n, K, lane_id(), out, trash, hist);
 }
 
-// Everything after stage 1: both halves' survivors are in s.s1 (written by
-// this wave, or by others before a barrier).  Writes K outputs per unit
-// (lanes j < K write slot j).
-template <bool RADIX>
+// One half's K survivors (list[0 .. K)) sorted in place by (key desc, index
+// asc); entries K .. 63 become 0, below every survivor word.
+__device__ __forceinline__ void sort_survivors(uint64_t* list, int K) {
+  const int lane = lane_id();
+  uint64_t k = lane < K ? list[lane] : 0ull;
+  k = wave_sort_desc_u64(k);
+  wave_sync();
+  list[lane] = k;
+  wave_sync();
+}
+
+// Everything after stage 1: both halves' survivors are in s.sorted (written
+// by this wave, or by others before a barrier; SORTED: already sorted by
+// sort_survivors).  Writes K outputs per unit (lanes j < K write slot j).
+template <bool RADIX, bool SORTED = false>
 __device__ inline void select_finish(int n, int K, SelectLds& s, const uint32_t (&rc)[pairtab::kSlots],
                               int32_t* __restrict__ idx_out, float* __restrict__ score_out,
                               float* __restrict__ weight_out) {
@@ -325,12 +336,14 @@ __device__ inline void select_finish(int n, int K, SelectLds& s, const uint32_t 
   const int lane = lane_id();
 
   // ---- sort both survivor lists by (key desc, index asc)
-  uint64_t ka = lane < K ? s.sorted.a[lane] : 0ull, kb = lane < K ? s.sorted.b[lane] : 0ull;
-  wave_sort2_desc_u64(ka, kb);
-  wave_sync();
-  s.sorted.a[lane] = ka;
-  s.sorted.b[lane] = kb;
-  wave_sync();
+  if constexpr (!SORTED) {
+    uint64_t ka = lane < K ? s.sorted.a[lane] : 0ull, kb = lane < K ? s.sorted.b[lane] : 0ull;
+    wave_sort2_desc_u64(ka, kb);
+    wave_sync();
+    s.sorted.a[lane] = ka;
+    s.sorted.b[lane] = kb;
+    wave_sync();
+  }
 
   // ---- stage 2 over P+: slot keys and flat indices in registers
   uint32_t sk[S];

@@ -78,7 +78,8 @@ static __constant__ const pairtab::Table kPairTab = pairtab::make();
 
 struct SelectLds {
   // The survivors of each half as 64-bit words (key << 32) | ~index: stage 1
-  // writes them in no particular order, select_finish sorts them in place.
+  // writes them in no particular order; select_finish sorts them in place,
+  // or sort_survivors does, on the wave that wrote the half.
   struct {
     uint64_t a[64];
     uint64_t b[64];
